@@ -1,0 +1,176 @@
+/*
+ * mla_absorb.h - C ABI of an MI355X (gfx950) library for Multi-head Latent
+ * Attention decode in the weight-absorbed form over a paged latent KV cache.
+ *
+ * The method: each cached position stores only the compressed latent c (D_C
+ * wide) and one rotary key k_rope (D_R wide) shared by all heads ("DeepSeek's
+ * KV Cache: From 3.9 MB to 890 B per Token", Figure 3 and section "Calculating
+ * V2's KV cache").  A decode step never expands per-head keys or values:
+ *   1. mla_absorb_q    q_lat[h] = W_UK[h] q_nope[h]    (Figure 5, form (2))
+ *   2. mla_decode_attn score_j = scale*(q_lat[h].c_j + q_rope[h].k_rope_j),
+ *                      softmax over the visible positions, and the weighted
+ *                      latent U[h] = sum_j p_j c_j      (Figures 4, 5 (2), 6 (2))
+ *      optionally restricted to a picked subset of positions (Figure 10)
+ *   3. mla_combine     log-sum-exp merge of split partials (exact identity of
+ *                      softmax over a union of disjoint position sets)
+ *   4. mla_out_up      out[h] = W_UV[h] U[h]            (Figure 6, form (2))
+ *
+ * Conventions common to every call
+ *  - All pointers except *_host ones are device pointers.  The caller owns
+ *    every buffer; the library allocates nothing, keeps no state between
+ *    calls and never synchronises.  Kernels are enqueued on `stream` (a
+ *    hipStream_t; NULL = the default stream) and run asynchronously: buffers
+ *    must stay alive until the stream has passed them.
+ *  - Each call validates its host-visible arguments first.  On any error it
+ *    enqueues nothing and returns the error code.  MLA_ERR_LAUNCH reports a
+ *    failed kernel launch (hipGetLastError after the launch).
+ *  - Dense tensors are row-major with the shapes given below, element type
+ *    act_dtype (queries, weights, outputs) unless stated.  Pointers must be
+ *    16-byte aligned.
+ *  - Device-resident metadata (seq_lens, block tables, index lists) is not
+ *    read on the host.  Contract: 1 <= seq_lens[b]; block-table entries of the
+ *    pages a request uses are valid page ids; index lists are sorted,
+ *    distinct, within [0, seq_lens[b]) or -1 as padding.  Kernels never fault
+ *    on bad metadata: positions whose index is negative or >= seq_lens[b], and
+ *    positions whose page id is outside [0, num_pages), are skipped as if
+ *    masked.  mla_check_decode_inputs_host() checks the contract on host
+ *    copies and reports the first violation.
+ */
+#ifndef MLA_ABSORB_H
+#define MLA_ABSORB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+#define MLA_PAGE_TOKENS 64 /* positions per cache page */
+#define MLA_TILE_TOKENS 32 /* positions per attention tile; split granularity */
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null or misaligned pointer, bad size, too small workspace */
+  MLA_ERR_UNSUPPORTED = 2, /* a dims / dtype combination the library has no kernel for */
+  MLA_ERR_LAUNCH = 3       /* the HIP runtime refused a launch */
+} mla_status;
+
+typedef enum {
+  MLA_F32 = 0,
+  MLA_BF16 = 1,
+  MLA_FP8_E4M3 = 2 /* OCP E4M3: bias 7, max 448, no infinities (cache only) */
+} mla_dtype;
+
+/* Model dimensions and types.  Supported combinations:
+ *   cache F32,  act F32 : any dims with num_heads*d_latent <= 8192,
+ *                         d_latent, d_rope <= 512 (generic fp32 kernels)
+ *   cache BF16, act BF16: num_heads = 128, d_latent = 512, d_rope = 64
+ *                         (DeepSeek-V2 dims; MFMA kernels), d_nope and d_v
+ *                         multiples of 16
+ *   cache FP8,  act BF16: as BF16, latent stored as E4M3 with one float32
+ *                         scale per position, rotary key in BF16 */
+typedef struct {
+  int32_t num_heads;     /* H */
+  int32_t d_latent;      /* D_C, width of the cached latent c */
+  int32_t d_rope;        /* D_R, width of the shared rotary key */
+  int32_t d_nope;        /* D_N, per-head content query width */
+  int32_t d_v;           /* D_V, per-head value width */
+  int32_t block_size;    /* positions per page, must be MLA_PAGE_TOKENS */
+  float softmax_scale;   /* usually 1/sqrt(d_nope + d_rope) */
+  int32_t cache_dtype;   /* mla_dtype */
+  int32_t act_dtype;     /* mla_dtype, F32 or BF16 */
+} mla_config;
+
+/* Split plan for mla_decode_attn / mla_combine. */
+typedef struct {
+  int32_t num_workers;    /* work-groups that share the position tiles of all requests */
+  int32_t num_slots;      /* partial results the workers can emit: num_workers + batch - 1 */
+  size_t workspace_bytes; /* bytes mla_decode_attn needs for partials */
+} mla_plan;
+
+/* ABI version compiled into the library (MLA_ABI_VERSION). */
+int32_t mla_abi_version(void);
+
+/* Static text for a status code. */
+const char* mla_status_string(mla_status status);
+
+/* Byte layout of one cache page (structure of arrays, sections 16-byte
+ * aligned, positions in order inside each section):
+ *   F32 : c [64][D_C] f32,  k_rope [64][D_R] f32
+ *   BF16: c [64][D_C] bf16, k_rope [64][D_R] bf16
+ *   FP8 : c [64][D_C] e4m3, k_rope [64][D_R] bf16, scale [64] f32
+ * Outputs the page size and the offsets of the rope and scale sections.  Host
+ * only. */
+mla_status mla_page_layout(const mla_config* cfg, size_t* page_bytes, size_t* rope_offset,
+                           size_t* scale_offset);
+
+/* Choose the number of workers for a batch and size the partial workspace.
+ * seq_lens_host: host copy of the per-request lengths (used only to count
+ * tiles; may be NULL, then every request is assumed to be max_len long).
+ * topk: 0 for dense attention, else the index-list length per request.
+ * num_cus: compute units of the device (256 on MI355X).  Host only. */
+mla_status mla_decode_plan(const mla_config* cfg, int32_t batch, const int32_t* seq_lens_host,
+                           int32_t max_len, int32_t topk, int32_t num_cus, mla_plan* plan);
+
+/* Step 1 (Figure 5 (2)): absorb W_UK into the query.
+ *   q_nope [batch][H][D_N], w_uk [H][D_C][D_N] (k_nope_j = c_j W_UK[h], i.e.
+ *   W^UK_h as an [input, output] matrix), q_lat [batch][H][D_C]:
+ *   q_lat[b][h][c] = sum_n w_uk[h][c][n] * q_nope[b][h][n]  (fp32 accumulate) */
+mla_status mla_absorb_q(const mla_config* cfg, const void* q_nope, const void* w_uk, void* q_lat,
+                        int32_t batch, void* stream);
+
+/* Step 2: attention of every head over the latent cache.
+ *   q_lat [batch][H][D_C], q_rope [batch][H][D_R] (act_dtype)
+ *   kv_pool: num_pages pages laid out as mla_page_layout() describes
+ *   block_table [batch][block_table_stride] int32 page ids, logical page
+ *     i of request b holds positions 64i..64i+63
+ *   seq_lens [batch] int32 cached positions per request (all visible)
+ *   topk_idx: NULL for dense attention, else [batch][topk] int32 positions
+ *     (sorted, distinct, -1 = padding); only those positions are read and
+ *     the softmax runs over them alone (Figure 10)
+ * Two output modes:
+ *   o_lat != NULL: one work-group per request writes the final weighted latent
+ *     o_lat [batch][H][D_C] (act_dtype) and, if lse_out != NULL, lse_out
+ *     [batch][H] = log sum_j exp(score_j).  workspace is not used.
+ *   o_lat == NULL: plan->num_workers work-groups share all position tiles of
+ *     all requests evenly and write float32 partials (normalised weighted
+ *     latent and its log-sum-exp) into workspace; mla_combine() finishes.
+ * A request whose positions are all skipped yields zeros and lse = -inf. */
+mla_status mla_decode_attn(const mla_config* cfg, const void* q_lat, const void* q_rope,
+                           const void* kv_pool, int64_t num_pages, const int32_t* block_table,
+                           int32_t block_table_stride, const int32_t* seq_lens,
+                           const int32_t* topk_idx, int32_t topk, int32_t batch,
+                           const mla_plan* plan, void* workspace, size_t workspace_bytes,
+                           void* o_lat, float* lse_out, void* stream);
+
+/* Step 3: merge the partials of mla_decode_attn (o_lat == NULL mode):
+ *   o_lat[b][h] = sum_s exp(lse_s - LSE) o_s,  LSE = log sum_s exp(lse_s)
+ * over the partials that request b received.  seq_lens, topk, batch and plan
+ * must be those given to mla_decode_attn.  lse_out [batch][H] may be NULL. */
+mla_status mla_combine(const mla_config* cfg, const void* workspace, size_t workspace_bytes,
+                       const int32_t* seq_lens, int32_t topk, int32_t batch, const mla_plan* plan,
+                       void* o_lat, float* lse_out, void* stream);
+
+/* Step 4 (Figure 6 (2)): up-project the weighted latent.
+ *   o_lat [batch][H][D_C], w_uv [H][D_V][D_C] (v_j = W_UV[h] c_j),
+ *   out [batch][H][D_V]: out[b][h][v] = sum_c w_uv[h][v][c] * o_lat[b][h][c] */
+mla_status mla_out_up(const mla_config* cfg, const void* o_lat, const void* w_uv, void* out,
+                      int32_t batch, void* stream);
+
+/* Host-side check of the device-metadata contract on host copies: lengths
+ * >= 1, enough block-table columns, page ids in [0, num_pages) for every page
+ * a request uses, index lists sorted, distinct, in range, -1 only as trailing
+ * padding.  topk_idx may be NULL (dense).  Returns MLA_OK or
+ * MLA_ERR_INVALID_ARG and, if err_index != NULL, the request that failed. */
+mla_status mla_check_decode_inputs_host(const mla_config* cfg, int32_t batch,
+                                        const int32_t* seq_lens, const int32_t* block_table,
+                                        int32_t block_table_stride, int64_t num_pages,
+                                        const int32_t* topk_idx, int32_t topk,
+                                        int32_t* err_index);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_ABSORB_H */

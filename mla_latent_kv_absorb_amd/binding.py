@@ -1,0 +1,234 @@
+"""ctypes binding of libmla_absorb.so (C ABI in include/mla_absorb.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity (the C ABI receives plain pointers and cannot check sizes), then
+their pointers and the current HIP stream are passed to the library.  Every
+step of the decode path runs in the library's HIP kernels.  Importing this
+module loads the library and raises if it has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_LAUNCH = 0, 1, 2, 3
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+PAGE_TOKENS = 64
+TILE_TOKENS = 32
+
+EXPORTED = (
+    "mla_abi_version", "mla_status_string", "mla_page_layout", "mla_decode_plan",
+    "mla_absorb_q", "mla_decode_attn", "mla_combine", "mla_out_up",
+    "mla_check_decode_inputs_host",
+)
+
+
+class MlaConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32), ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+        ("d_nope", ctypes.c_int32), ("d_v", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("cache_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+    ]
+
+
+class MlaPlan(ctypes.Structure):
+    _fields_ = [("num_workers", ctypes.c_int32), ("num_slots", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m mla_latent_kv_absorb_amd.build_lib` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cfgp, planp = ctypes.POINTER(MlaConfig), ctypes.POINTER(MlaPlan)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "mla_abi_version": ([], I32),
+        "mla_status_string": ([I32], ctypes.c_char_p),
+        "mla_page_layout": ([cfgp, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
+        "mla_decode_plan": ([cfgp, I32, i32p, I32, I32, I32, planp], I32),
+        "mla_absorb_q": ([cfgp, P, P, P, I32, P], I32),
+        "mla_decode_attn": ([cfgp, P, P, P, I64, P, I32, P, P, I32, I32, planp, P, SZ, P, P, P], I32),
+        "mla_combine": ([cfgp, P, SZ, P, I32, I32, planp, P, P, P], I32),
+        "mla_out_up": ([cfgp, P, P, P, I32, P], I32),
+        "mla_check_decode_inputs_host": ([cfgp, I32, i32p, i32p, I32, I64, i32p, I32, i32p], I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(status: int) -> str:
+    return _lib.mla_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(_lib.mla_abi_version())
+
+
+def make_config(H, D_C, D_R, D_N, D_V, scale, cache_dtype, act_dtype) -> MlaConfig:
+    return MlaConfig(H, D_C, D_R, D_N, D_V, PAGE_TOKENS, float(scale), int(cache_dtype), int(act_dtype))
+
+
+def _check(fn: str, st: int):
+    if st != MLA_OK:
+        raise MlaError(fn, st)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _act(cfg: MlaConfig):
+    torch = _torch()
+    return torch.float32 if cfg.act_dtype == MLA_F32 else torch.bfloat16
+
+
+def page_layout(cfg: MlaConfig):
+    pb, ro, so = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check("mla_page_layout", _lib.mla_page_layout(ctypes.byref(cfg), ctypes.byref(pb), ctypes.byref(ro),
+                                                   ctypes.byref(so)))
+    return int(pb.value), int(ro.value), int(so.value)
+
+
+def mla_decode_plan(cfg: MlaConfig, batch: int, seq_lens_host=None, max_len: int = 0, topk: int = 0,
+                    num_cus: int = 256) -> MlaPlan:
+    plan = MlaPlan()
+    arr = None
+    if seq_lens_host is not None:
+        arr = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+        if arr.shape != (batch,):
+            raise ValueError("seq_lens_host must have one entry per request")
+    ptr = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if arr is not None else None
+    _check("mla_decode_plan", _lib.mla_decode_plan(ctypes.byref(cfg), batch, ptr, int(max_len), int(topk),
+                                                   int(num_cus), ctypes.byref(plan)))
+    return plan
+
+
+def mla_absorb_q(cfg: MlaConfig, q_nope, w_uk, q_lat, stream=None):
+    B = q_nope.shape[0]
+    dt = _act(cfg)
+    H, DC, DN = cfg.num_heads, cfg.d_latent, cfg.d_nope
+    st = _lib.mla_absorb_q(ctypes.byref(cfg), _dev(q_nope, "q_nope", dt, (B, H, DN)),
+                           _dev(w_uk, "w_uk", dt, (H, DC, DN)), _dev(q_lat, "q_lat", dt, (B, H, DC)),
+                           B, _stream(stream))
+    _check("mla_absorb_q", st)
+
+
+def mla_out_up(cfg: MlaConfig, o_lat, w_uv, out, stream=None):
+    B = o_lat.shape[0]
+    dt = _act(cfg)
+    H, DC, DV = cfg.num_heads, cfg.d_latent, cfg.d_v
+    st = _lib.mla_out_up(ctypes.byref(cfg), _dev(o_lat, "o_lat", dt, (B, H, DC)),
+                         _dev(w_uv, "w_uv", dt, (H, DV, DC)), _dev(out, "out", dt, (B, H, DV)),
+                         B, _stream(stream))
+    _check("mla_out_up", st)
+
+
+def mla_decode_attn(cfg: MlaConfig, q_lat, q_rope, kv_pool, block_table, seq_lens, topk_idx=None,
+                    plan: Optional[MlaPlan] = None, workspace=None, o_lat=None, lse_out=None, stream=None):
+    """Direct mode when o_lat is given (one work-group per request, final
+    output); split mode otherwise (plan + workspace, finish with mla_combine)."""
+    torch = _torch()
+    B = q_lat.shape[0]
+    dt = _act(cfg)
+    H, DC, DR = cfg.num_heads, cfg.d_latent, cfg.d_rope
+    page_bytes, _, _ = page_layout(cfg)
+    if kv_pool.dtype != torch.uint8 or kv_pool.dim() != 2 or kv_pool.shape[1] != page_bytes:
+        raise ValueError(f"kv_pool must be uint8 [num_pages, {page_bytes}]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [batch, stride]")
+    topk = 0
+    tp = None
+    if topk_idx is not None:
+        if topk_idx.dim() != 2 or topk_idx.shape[0] != B:
+            raise ValueError("topk_idx must be int32 [batch, k]")
+        topk = int(topk_idx.shape[1])
+        tp = _dev(topk_idx, "topk_idx", torch.int32)
+    ws, wsb = None, 0
+    if o_lat is None:
+        if plan is None or workspace is None:
+            raise ValueError("split mode needs a plan and a workspace")
+        ws = _dev(workspace, "workspace", torch.uint8)
+        wsb = workspace.numel()
+        ol = None
+    else:
+        ol = _dev(o_lat, "o_lat", dt, (B, H, DC))
+    lp = _dev(lse_out, "lse_out", torch.float32, (B, H)) if lse_out is not None else None
+    st = _lib.mla_decode_attn(
+        ctypes.byref(cfg), _dev(q_lat, "q_lat", dt, (B, H, DC)), _dev(q_rope, "q_rope", dt, (B, H, DR)),
+        _dev(kv_pool, "kv_pool"), int(kv_pool.shape[0]), _dev(block_table, "block_table", torch.int32),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, (B,)), tp, topk, B,
+        ctypes.byref(plan) if plan is not None else None, ws, wsb, ol, lp, _stream(stream))
+    _check("mla_decode_attn", st)
+
+
+def mla_combine(cfg: MlaConfig, workspace, seq_lens, plan: MlaPlan, o_lat, lse_out=None, topk: int = 0,
+                stream=None):
+    torch = _torch()
+    B = o_lat.shape[0]
+    dt = _act(cfg)
+    lp = _dev(lse_out, "lse_out", torch.float32, (B, cfg.num_heads)) if lse_out is not None else None
+    st = _lib.mla_combine(ctypes.byref(cfg), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                          _dev(seq_lens, "seq_lens", torch.int32, (B,)), int(topk), B, ctypes.byref(plan),
+                          _dev(o_lat, "o_lat", dt, (B, cfg.num_heads, cfg.d_latent)), lp, _stream(stream))
+    _check("mla_combine", st)
+
+
+def mla_check_decode_inputs_host(cfg: MlaConfig, seq_lens, block_table, num_pages: int, topk_idx=None):
+    """Host check of the metadata contract; returns (status, failing request)."""
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    tk = None if topk_idx is None else np.ascontiguousarray(topk_idx, dtype=np.int32)
+    err = ctypes.c_int32(-1)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    st = _lib.mla_check_decode_inputs_host(
+        ctypes.byref(cfg), int(sl.shape[0]), sl.ctypes.data_as(i32p), bt.ctypes.data_as(i32p), int(bt.shape[1]),
+        int(num_pages), tk.ctypes.data_as(i32p) if tk is not None else None,
+        int(tk.shape[1]) if tk is not None else 0, ctypes.byref(err))
+    return int(st), int(err.value)
+
+
+def raw_lib():
+    """The loaded ctypes library (for tests that call the C ABI directly)."""
+    return _lib

@@ -1,0 +1,564 @@
+// Weight-absorbed MLA decode attention over a paged latent cache, gfx950.
+//
+// Per work-group: 4 waves, each owning 32 of the 128 heads.  For every tile
+// of 32 cached positions the work-group streams the latent rows (512 wide)
+// and rotary-key rows (64 wide) from HBM straight into LDS and each wave
+//   * scores its heads against the tile with MFMA 32x32x16 (bf16 in, fp32
+//     accumulate): S^T[pos][head] = C[pos] . q_lat[head] + k_rope[pos] .
+//     q_rope[head] -- the absorbed score of "DeepSeek's KV Cache", Figure 5
+//     form (2), plus the unabsorbed rotary part (section "Why the positional
+//     part is kept separate");
+//   * runs an online softmax per head (each lane owns one head);
+//   * accumulates the weighted latent U^T[latent][head] += C^T P^T on MFMA
+//     (Figure 6 form (2), first step).  The S^T accumulator registers are the
+//     B operand of this product as they are; the positions inside the MFMA K
+//     dimension are permuted to match, and the C^T operand comes from
+//     transposing LDS reads (ds_read_b64_tr_b16).
+// Each latent row is read from HBM once and serves as both key and value
+// (same page, section "Looking at reads": one item counted once for both
+// roles).
+//
+// Loads use global_load_lds_dwordx4 (HBM -> LDS without registers) through a
+// 4-stage ring (6 for FP8) with explicit vmcnt waits; the rows are stored with
+// an XOR swizzle of their 16-byte chunks so the MFMA operand reads are free of
+// bank conflicts.  Page ids and index lists are read with scalar loads so
+// they never wait behind the LDS-bound vector loads.
+//
+// FP8 cache: the latent arrives as E4M3 with one float32 scale per position.
+// A conversion pass turns the tile into BF16 in LDS (exact); the scale
+// multiplies the content score before the rotary part is added, and multiplies
+// the probabilities fed to the weighted sum (the softmax normaliser uses the
+// unscaled probabilities).
+//
+// Sparse selection ("DeepSeek's KV Cache", Figure 10): with an index list the
+// tile rows are the listed positions, gathered one row per load; entries that
+// are -1, out of range or on an invalid page are masked.
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) short s16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+#define LDS __attribute__((address_space(3)))
+
+constexpr int kThreads = 256;
+constexpr int kCRow = kLatent * 2;  // bytes of one BF16 latent row (1024)
+constexpr int kRRow = kRope * 2;    // bytes of one BF16 rotary row (128)
+constexpr int kC8Row = kLatent;     // bytes of one FP8 latent row (512)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16-byte chunk swizzle: chunk c of row r lives at chunk c ^ swz(r % 8).
+// Makes 8 consecutive rows hit distinct bank groups for 16-byte row reads and
+// 4-row x 32-byte blocks distinct for the transposing 8-byte reads.
+__device__ __forceinline__ constexpr int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// HBM -> LDS without registers: lane l's bytes land at lds_addr + size * l.
+// lds_addr must be wave-uniform (it goes to M0).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ float wave_partner(float v) {
+  // value held by lane (l ^ 32)
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
+}
+
+// x * alpha for an accumulator value, kept in its accumulator register.  The
+// online-softmax rescale runs only when a head's running maximum grows by a
+// large step; writing it this way keeps the register allocator from moving
+// the whole accumulator file through ordinary registers around that branch.
+// The trailing s_nop covers the accumulator-write -> MFMA-read distance.
+__device__ __forceinline__ float scale_acc(float x, float alpha) {
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %1, %0\n\t"
+      "v_mul_f32 %1, %1, %2\n\t"
+      "v_accvgpr_write_b32 %0, %1\n\t"
+      "s_nop 2"
+      : "+a"(x), "=&v"(t)
+      : "v"(alpha));
+  return x;
+}
+
+// Uniform metadata reads go through the constant address space so they become
+// scalar loads (lgkmcnt), never vector loads that would queue behind the
+// in-flight LDS-bound loads on vmcnt.
+__device__ __forceinline__ int32_t sload(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
+}
+
+template <bool FP8>
+struct Cfg {
+  static constexpr int NS = FP8 ? 6 : 4;                       // ring stages
+  static constexpr int C_STAGE = FP8 ? kTile * kC8Row : kTile * kCRow;
+  static constexpr int R_STAGE = kTile * kRRow;
+  static constexpr int SC_STAGE = FP8 ? kTile * 4 : 0;
+  static constexpr int STAGE = C_STAGE + R_STAGE + SC_STAGE;
+  static constexpr int CONV_OFF = NS * STAGE;                  // BF16 copy of an FP8 tile
+  static constexpr int CONV = FP8 ? kTile * kCRow : 0;
+  static constexpr int MASK_OFF = CONV_OFF + CONV;
+  static constexpr int LDS_BYTES = MASK_OFF + NS * 4;
+  static constexpr int DMA_PER_WAVE = FP8 ? 6 : 9;             // loads per wave per tile
+};
+
+template <int NS, int DPW>
+__device__ __forceinline__ void wait_tiles(int64_t ahead) {
+  // wait until at most `ahead` newer tiles of this wave are still in flight
+  if (ahead >= NS - 2) { wait_vmcnt<DPW * (NS - 2)>(); return; }
+  if constexpr (NS - 2 > 4) { if (ahead == 4) { wait_vmcnt<DPW * 4>(); return; } }
+  if constexpr (NS - 2 > 3) { if (ahead == 3) { wait_vmcnt<DPW * 3>(); return; } }
+  if constexpr (NS - 2 > 2) { if (ahead == 2) { wait_vmcnt<DPW * 2>(); return; } }
+  if constexpr (NS - 2 > 1) { if (ahead == 1) { wait_vmcnt<DPW * 1>(); return; } }
+  wait_vmcnt<0>();
+}
+
+template <bool FP8, bool TOPK>
+struct Loader {
+  const DecodeArgs& a;
+  uint32_t smem_base;
+  int lane, w;
+
+  __device__ __forceinline__ int32_t ntiles(int32_t b) const {
+    if (TOPK) return tiles_of(a.topk);
+    int32_t T = sload(a.seq_lens + b);
+    return T > 0 ? tiles_of(T) : 0;
+  }
+
+  // Issue this wave's share of tile t of request b into ring stage st.
+  __device__ __forceinline__ void issue(int st, int32_t b, int32_t t, char* smem) const {
+    using C = Cfg<FP8>;
+    const uint32_t sb = smem_base + st * C::STAGE;
+    const int32_t T = sload(a.seq_lens + b);
+    const uint8_t* pool = a.pool;
+    uint32_t bits = 0;
+    if (!TOPK) {
+      const bool in_table = (t >> 1) < a.bt_stride;
+      const int32_t page = in_table ? sload(a.block_table + (int64_t)b * a.bt_stride + (t >> 1)) : -1;
+      const bool pv = page >= 0 && page < a.num_pages;
+      const uint8_t* pg = pool + (pv ? (int64_t)page * a.page_bytes : 0);
+      const int slot0 = (t & 1) * kTile + 8 * w;  // first row of this wave in the page
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int pos = t * kTile + 8 * w + k;
+        if (pv && pos < T) bits |= 1u << k;
+      }
+      if (FP8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dma16(pg + (int64_t)(slot0 + 2 * q) * kC8Row + 16 * lane, sb + (8 * w + 2 * q) * kC8Row);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          dma16(pg + (int64_t)(slot0 + k) * kCRow + 16 * (lane ^ swz(k)), sb + (8 * w + k) * kCRow);
+      }
+      const int rr = lane >> 3, rc = lane & 7;
+      dma16(pg + a.rope_off + (int64_t)(slot0 + rr) * kRRow + 16 * (rc ^ swz(rr)),
+            sb + C::C_STAGE + 8 * w * kRRow);
+      if (FP8) {
+        if (lane < 8) dma4(pg + a.scale_off + (int64_t)(slot0 + lane) * 4, sb + C::C_STAGE + C::R_STAGE + 32 * w);
+      }
+    } else {
+      // gathered rows: one index per row
+      const uint8_t* pgk[8];
+      int slk[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int lp = t * kTile + 8 * w + k;
+        int32_t idx = lp < a.topk ? sload(a.topk_idx + (int64_t)b * a.topk + lp) : -1;
+        bool v = idx >= 0 && idx < T && (idx >> 6) < a.bt_stride;
+        int32_t page = v ? sload(a.block_table + (int64_t)b * a.bt_stride + (idx >> 6)) : 0;
+        v = v && page >= 0 && page < a.num_pages;
+        pgk[k] = pool + (v ? (int64_t)page * a.page_bytes : 0);
+        slk[k] = v ? (idx & 63) : 0;
+        if (v) bits |= 1u << k;
+      }
+      constexpr int CR = FP8 ? kC8Row : kCRow;
+      if (FP8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint8_t* src = (lane < 32) ? pgk[2 * q] + slk[2 * q] * CR : pgk[2 * q + 1] + slk[2 * q + 1] * CR;
+          dma16(src + 16 * (lane & 31), sb + (8 * w + 2 * q) * kC8Row);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dma16(pgk[k] + slk[k] * CR + 16 * (lane ^ swz(k)), sb + (8 * w + k) * kCRow);
+      }
+      const int rr = lane >> 3, rc = lane & 7;
+      const uint8_t* rp = pgk[0];
+      int rs = slk[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) {
+        rp = (rr == k) ? pgk[k] : rp;
+        rs = (rr == k) ? slk[k] : rs;
+      }
+      dma16(rp + a.rope_off + rs * kRRow + 16 * (rc ^ swz(rr)), sb + C::C_STAGE + 8 * w * kRRow);
+      if (FP8) {
+        if (lane < 8) {
+          const uint8_t* sp = pgk[0];
+          int ss = slk[0];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) {
+            sp = (lane == k) ? pgk[k] : sp;
+            ss = (lane == k) ? slk[k] : ss;
+          }
+          dma4(sp + a.scale_off + ss * 4, sb + C::C_STAGE + C::R_STAGE + 32 * w);
+        }
+      }
+    }
+    if (lane == 0) smem[C::MASK_OFF + st * 4 + w] = (char)bits;
+  }
+};
+
+template <bool FP8, bool TOPK, bool DIRECT>
+__global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
+  using C = Cfg<FP8>;
+  constexpr int NS = C::NS;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  LDS char* L = (LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5;
+  const float scale_log2 = a.scale * kLog2e;
+
+  Loader<FP8, TOPK> ld{a, (uint32_t)(uintptr_t)smem, lane, w};
+
+  // ---- this work-group's tiles: [first request b0, tile t0], n tiles ----
+  int32_t b0, t0;
+  int64_t n;
+  int64_t worker = blockIdx.x;
+  if (DIRECT) {
+    b0 = blockIdx.x;
+    t0 = 0;
+    n = ld.ntiles(b0);
+  } else {
+    int64_t W = 0;
+    if (TOPK) {
+      W = (int64_t)a.batch * tiles_of(a.topk);
+    } else {
+      for (int32_t b = 0; b < a.batch; ++b) W += ld.ntiles(b);
+    }
+    const int64_t g0 = worker_lo(worker, W, a.num_workers);
+    const int64_t g1 = worker_lo(worker + 1, W, a.num_workers);
+    n = g1 - g0;
+    if (n <= 0) return;
+    if (TOPK) {
+      const int32_t nt = tiles_of(a.topk);
+      b0 = (int32_t)(g0 / nt);
+      t0 = (int32_t)(g0 % nt);
+    } else {
+      int64_t acc = 0;
+      int32_t b = 0;
+      while (acc + ld.ntiles(b) <= g0) { acc += ld.ntiles(b); ++b; }
+      b0 = b;
+      t0 = (int32_t)(g0 - acc);
+    }
+  }
+
+  // ---- per-lane LDS offsets (relative to a tile) ----
+  // The swizzle only touches the low 3 bits of a 16-byte chunk index, so the
+  // operand addresses are a few per-lane bases plus compile-time offsets.
+  const int row = lane & 31;
+  const int sw_row = swz(lane & 7);
+  int s_off[4];   // latent row operand of K-block kb = 4u+v: s_off[v] + 128u
+  int r_off[4];   // rotary row operand of K-block v
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int c = 16 * ((2 * v + hi) ^ sw_row);
+    s_off[v] = row * kCRow + c;
+    r_off[v] = row * kRRow + c;
+  }
+  int tr_off[2];  // transposed latent operand of column block mb = 2p+e: tr_off[e] + 128p
+  {
+    const int j16 = lane & 15, g16 = lane >> 4, hh = g16 >> 1, ch = g16 & 1;
+    const int tr_row = 4 * hh + (j16 >> 2);             // rows 16*kb2 + tr_row and +8
+    const int tr_sw = swz(tr_row & 7);
+    const int lo = (2 * ch + ((j16 & 3) >> 1)) ^ (tr_sw & 3);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      tr_off[e] = tr_row * kCRow + 64 * (e ^ (tr_sw >> 2)) + 16 * lo + (j16 & 1) * 8;
+  }
+  const int head = 32 * w + row;
+
+  // Weighted-latent accumulators: 32 heads x 512 latent columns per wave,
+  // 16 MFMA blocks (the whole accumulator register file).
+  f32x16 O[16];
+  bf16x8 q[32];
+  bf16x8 qr[4];
+
+  // ---- prologue ----
+  int32_t ib = b0, it = t0;      // issue cursor
+  int32_t cb = b0, ct = t0;      // compute cursor
+  auto advance = [&](int32_t& b, int32_t& t) {
+    ++t;
+    while (b < a.batch && t >= ld.ntiles(b)) { t = 0; ++b; }
+  };
+  int64_t issued = 0;
+  const int64_t pro = n < NS - 1 ? n : NS - 1;
+  for (; issued < pro; ++issued) {
+    ld.issue((int)(issued % NS), ib, it, smem);
+    advance(ib, it);
+  }
+
+  if (n == 0) {  // only in direct mode: a request with no position
+    if (DIRECT) {
+      __bf16* o = (__bf16*)a.o_lat + ((int64_t)b0 * kHeads + head) * kLatent + 4 * hi;
+      for (int d = 0; d < kLatent; d += 8) *(uint64_t*)(o + d) = 0;
+      if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)b0 * kHeads + head] = -INFINITY;
+    }
+    return;
+  }
+
+  int64_t i = 0;  // tiles of this work-group consumed so far
+  while (i < n) {
+    // ---- one segment: tiles [ct, ct + seg_len) of request cb ----
+    if (cb >= a.batch) break;  // unreachable when the tile accounting is consistent
+    const int32_t nt_cb = ld.ntiles(cb);
+    const int64_t left_in_req = nt_cb - ct;
+    const int64_t seg_len = left_in_req < n - i ? left_in_req : n - i;
+    if (seg_len <= 0) break;
+
+    // Drain (previous segment's output stores count on vmcnt too), then fetch
+    // this request's queries and make sure they have arrived before more
+    // tiles go in flight behind them.
+    wait_vmcnt<0>();
+    __syncthreads();
+    {
+      const __bf16* ql = (const __bf16*)a.q_lat + ((int64_t)cb * kHeads + head) * kLatent + 8 * hi;
+      const __bf16* qp = (const __bf16*)a.q_rope + ((int64_t)cb * kHeads + head) * kRope + 8 * hi;
+#pragma unroll
+      for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8*)(ql + 16 * kb);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) qr[kb] = *(const bf16x8*)(qp + 16 * kb);
+#pragma unroll
+      for (int kb = 0; kb < 32; ++kb) asm volatile("" ::"v"(q[kb]));
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) asm volatile("" ::"v"(qr[kb]));
+    }
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) O[mb] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int64_t j = 0; j < seg_len; ++j, ++i) {
+      const int st = (int)(i % NS);
+      if (j > 0) {
+        wait_tiles<NS, C::DMA_PER_WAVE>(n - 1 - i);
+        __syncthreads();
+      }
+      if (issued < n) {
+        ld.issue((int)(issued % NS), ib, it, smem);
+        advance(ib, it);
+        ++issued;
+      }
+      const uint32_t mask = *(const LDS uint32_t*)(L + C::MASK_OFF + st * 4);
+
+      LDS char* Ct;   // BF16 latent tile (swizzled)
+      LDS char* Rt = L + st * C::STAGE + C::C_STAGE;
+      if (FP8) {
+        // E4M3 -> BF16 into the conversion buffer; masked rows become zeros.
+        Ct = L + C::CONV_OFF;
+        const int r = tid >> 3, qq = tid & 7;
+        const LDS char* src = L + st * C::STAGE + r * kC8Row + 64 * qq;
+        LDS char* dst = Ct + r * kCRow;
+        const bool rv = (mask >> r) & 1;
+        const int rs = swz(r & 7);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          i32x4 raw = *(const LDS i32x4*)(src + 16 * v4);
+#pragma unroll
+          for (int hc = 0; hc < 2; ++hc) {
+            i32x4 outv;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int word = raw[2 * hc + e];
+              // exact: every E4M3 value is a BF16 value
+              const uint32_t u0 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 0)) >> 16;
+              const uint32_t u1 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 1)) >> 16;
+              const uint32_t u2 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 2)) >> 16;
+              const uint32_t u3 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 3)) >> 16;
+              outv[2 * e] = (int)(u0 | (u1 << 16));
+              outv[2 * e + 1] = (int)(u2 | (u3 << 16));
+            }
+            if (!rv) outv = i32x4{0, 0, 0, 0};
+            const int chunk = 8 * qq + 2 * v4 + hc;
+            *(LDS i32x4*)(dst + 16 * (chunk ^ rs)) = outv;
+          }
+        }
+        __syncthreads();
+      } else {
+        Ct = L + st * C::STAGE;
+        if (mask != 0xFFFFFFFFu) {
+          // masked rows may hold anything; zero them so 0-probability x row stays 0
+          const int r = tid >> 3, qq = tid & 7;
+          if (!((mask >> r) & 1)) {
+            LDS char* dst = Ct + r * kCRow + 128 * qq;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) *(LDS i32x4*)(dst + 16 * v) = i32x4{0, 0, 0, 0};
+          }
+          __syncthreads();
+        }
+      }
+
+      // ---- scores S^T[pos][head] ----
+      f32x16 sacc = f32x16{};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          bf16x8 av = *(const LDS bf16x8*)(Ct + s_off[v] + 128 * u);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, q[4 * u + v], sacc, 0, 0, 0);
+        }
+      }
+      float tsc[16];
+      if (FP8) {
+        const LDS float* sc = (const LDS float*)(L + st * C::STAGE + C::C_STAGE + C::R_STAGE);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v = *(const LDS f32x4*)(sc + 8 * g + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) tsc[4 * g + e] = v[e];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] *= tsc[r];
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        bf16x8 av = *(const LDS bf16x8*)(Rt + r_off[v]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qr[v], sacc, 0, 0, 0);
+      }
+
+      // ---- online softmax; lane owns head `head`, 16 of the 32 positions ----
+      // position of accumulator r: 8*(r/4) + 4*hi + r%4
+      const uint32_t mlane = mask >> (4 * hi);
+      float s[16];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool valid = (mlane >> (8 * (r >> 2) + (r & 3))) & 1u;
+        s[r] = valid ? sacc[r] * scale_log2 : -INFINITY;
+        mloc = fmaxf(mloc, s[r]);
+      }
+      mloc = fmaxf(mloc, wave_partner(mloc));
+      const float m_new = fmaxf(m_run, mloc);
+      // Rescale lazily: keep the old reference maximum unless the new one
+      // exceeds it by more than 8 (log2 units), so probabilities stay <= 256.
+      const bool need = m_new > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        m_run = need ? m_new : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
+      }
+      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      float lsum = 0.f;
+      bf16x8 P[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[r] - mref);
+        lsum += p;
+        const float pw = FP8 ? p * tsc[r] : p;
+        P[r >> 3][r & 7] = (__bf16)pw;
+      }
+      l_run += lsum;
+
+      // ---- weighted latent U^T[latent][head] += C^T P^T ----
+      typedef __attribute__((ext_vector_type(8))) short s16x8;
+      auto pv = [&](int mb, f32x16 acc) {
+        const int e = mb & 1, pp = mb >> 1;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const LDS char* p1 = Ct + tr_off[e] + 128 * pp + 16 * kCRow * kb2;
+          s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p1);
+          s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(p1 + 8 * kCRow));
+          s16x8 av8 = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av8), P[kb2], acc, 0, 0, 0);
+        }
+        return acc;
+      };
+#pragma unroll
+      for (int mb = 0; mb < 16; ++mb) O[mb] = pv(mb, O[mb]);
+    }
+
+    // ---- end of the segment: normalise and write ----
+    {
+      const float l_tot = l_run + wave_partner(l_run);
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      if (DIRECT) {
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+        __bf16* o = (__bf16*)a.o_lat + ((int64_t)cb * kHeads + head) * kLatent + 4 * hi;
+#pragma unroll
+        for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(O[mb][4 * g + e] * inv);
+            *(bf16x4*)(o + 32 * mb + 8 * g) = v;
+          }
+        if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
+      } else {
+        const int64_t slot = worker + cb;
+        float* o = a.part_o + (slot * kHeads + head) * kLatent + 4 * hi;
+#pragma unroll
+        for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = O[mb][4 * g + e] * inv;
+            *(f32x4*)(o + 32 * mb + 8 * g) = v;
+          }
+        if (hi == 0) a.part_lse[slot * kHeads + head] = lse;
+      }
+    }
+    // next request with tiles
+    ++cb;
+    ct = 0;
+    while (cb < a.batch && ld.ntiles(cb) == 0) ++cb;
+  }
+  wait_vmcnt<0>();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool fp8, hipStream_t s) {
+  const bool topk = a.topk_idx != nullptr;
+  const bool direct = a.num_workers == 0;
+  const dim3 grid(direct ? a.batch : a.num_workers);
+  const dim3 block(kThreads);
+#define MLA_LAUNCH(F, T, D) hipLaunchKernelGGL((decode_mfma_kernel<F, T, D>), grid, block, 0, s, a)
+  if (fp8) {
+    if (topk) { if (direct) MLA_LAUNCH(true, true, true); else MLA_LAUNCH(true, true, false); }
+    else { if (direct) MLA_LAUNCH(true, false, true); else MLA_LAUNCH(true, false, false); }
+  } else {
+    if (topk) { if (direct) MLA_LAUNCH(false, true, true); else MLA_LAUNCH(false, true, false); }
+    else { if (direct) MLA_LAUNCH(false, false, true); else MLA_LAUNCH(false, false, false); }
+  }
+#undef MLA_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,88 @@
+// Internal declarations shared by the host API and the kernel translation
+// units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kPageTokens = 64;
+constexpr int kTile = 32;  // positions per attention tile (split granularity)
+
+// V2 dimensions served by the MFMA kernels.
+constexpr int kHeads = 128;
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+
+struct DecodeArgs {
+  const void* q_lat;
+  const void* q_rope;
+  const uint8_t* pool;
+  int64_t num_pages;
+  int64_t page_bytes;
+  int64_t rope_off;
+  int64_t scale_off;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* topk_idx;  // nullptr = dense
+  int32_t topk;
+  int32_t batch;
+  int32_t num_workers;      // 0 = one work-group per request, final output
+  float* part_o;            // [slots][H][D_C]
+  float* part_lse;          // [slots][H]
+  void* o_lat;              // final output (direct mode)
+  float* lse_out;           // optional
+  int32_t H, D_C, D_R;
+  float scale;
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* seq_lens;
+  int32_t topk;
+  int32_t batch;
+  int32_t num_workers;
+  void* o_lat;
+  float* lse_out;
+  int32_t H, D_C;
+  int32_t out_bf16;
+};
+
+struct HeadGemmArgs {
+  // y[b][h][m] = sum_k w[h][m][k] * x[b][h][k]
+  const void* x;
+  const void* w;
+  void* y;
+  int32_t batch, H, M, K;
+};
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_head_gemm_bf16(const HeadGemmArgs& a, hipStream_t s);
+hipError_t launch_head_gemm_f32(const HeadGemmArgs& a, hipStream_t s);
+
+// LDS bytes the generic fp32 attention kernel needs for these dims.
+size_t decode_f32_lds_bytes(int H, int D_C, int D_R);
+
+}  // namespace mla
+
+// ---------------------------------------------------------------------------
+// Split partition shared by the attention kernels and the combine kernel:
+// all requests' tiles are concatenated in request order (W tiles in total)
+// and worker p takes tiles [lo(p), lo(p+1)) with lo(p) = floor(p*W/P).  A
+// worker that covers tiles of several requests emits one partial per request
+// into slot p + b, which is unique because p and b never both stay the same
+// from one piece to the next.
+// ---------------------------------------------------------------------------
+namespace mla {
+__host__ __device__ inline int64_t worker_lo(int64_t p, int64_t W, int64_t P) { return (p * W) / P; }
+// Worker whose tile range contains global tile x (0 <= x < W).
+__host__ __device__ inline int64_t worker_of(int64_t x, int64_t W, int64_t P) {
+  return ((x + 1) * P - 1) / W;
+}
+__host__ __device__ inline int32_t tiles_of(int32_t len) { return (len + kTile - 1) / kTile; }
+}  // namespace mla

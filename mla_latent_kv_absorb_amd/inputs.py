@@ -97,12 +97,17 @@ class DecodeInputs:
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest BF16 value (ties to even); returns
-    float32 holding exactly the BF16 values.  Inputs are finite."""
+    float32 holding exactly the BF16 values.  Inputs are finite.  Uses torch's
+    CPU conversion (same rounding, checked in the tests) when available."""
     x = np.ascontiguousarray(x, dtype=np.float32)
+    try:
+        import torch
+        return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    except ImportError:  # pragma: no cover
+        pass
     u = x.view(np.uint32)
     r = ((u >> 16) & 1) + np.uint32(0x7FFF)
-    out = ((u + r) & np.uint32(0xFFFF0000)).view(np.float32)
-    return out
+    return ((u + r) & np.uint32(0xFFFF0000)).view(np.float32)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -141,11 +146,26 @@ def encode_e4m3(x: np.ndarray) -> np.ndarray:
     return code | sign
 
 
-def quantize_fp8_per_token(c: np.ndarray):
-    """Per-token scale = max|c| / 448, codes = E4M3(c / scale)."""
-    amax = np.max(np.abs(c), axis=1).astype(np.float64)
-    scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
-    codes = encode_e4m3(c / scale.astype(np.float64)[:, None])
+def quantize_fp8_per_token(c: np.ndarray, chunk_rows: int = 1 << 18):
+    """Per-token scale = max|c| / 448, codes = E4M3(c / scale) rounded to the
+    nearest value (ties to even), quotients clamped to +-448.  The quotient is
+    formed in float32.  Uses torch's CPU float8 conversion when torch is
+    present (same rounding as encode_e4m3, checked in the tests)."""
+    amax = np.max(np.abs(c), axis=1).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    codes = np.empty(c.shape, dtype=np.uint8)
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        torch = None
+    for lo in range(0, c.shape[0], chunk_rows):
+        hi = min(lo + chunk_rows, c.shape[0])
+        if torch is not None:
+            x = torch.from_numpy(np.ascontiguousarray(c[lo:hi])) / torch.from_numpy(scale[lo:hi])[:, None]
+            codes[lo:hi] = x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        else:
+            x = np.clip(c[lo:hi] / scale[lo:hi, None], -448.0, 448.0)
+            codes[lo:hi] = encode_e4m3(x)
     return codes, scale
 
 

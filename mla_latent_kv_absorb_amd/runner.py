@@ -1,0 +1,114 @@
+"""Device-resident workload and the four-call decode step.
+
+Uploads one seeded workload (paged pool, block table, lengths, index lists,
+queries, weights) to GPU memory with torch, allocates the outputs and the
+split workspace, and runs absorb -> attention -> combine -> up-projection
+through the C ABI on the current stream.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as B
+from . import inputs as I
+
+
+def _dtype_code(name: str) -> int:
+    return {I.DTYPE_F32: B.MLA_F32, I.DTYPE_BF16: B.MLA_BF16, I.DTYPE_FP8: B.MLA_FP8_E4M3}[name]
+
+
+def to_device_act(x: np.ndarray, act: str, device):
+    import torch
+    if act == I.DTYPE_F32:
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+    bits = I.bf16_bits(x).view(np.int16)
+    return torch.from_numpy(bits).to(device).view(torch.bfloat16)
+
+
+def workspace_bytes(H: int, D_C: int, slots: int) -> int:
+    """Bytes of the split workspace: float32 partials [slots][H][D_C] then
+    float32 log-sum-exps [slots][H], each section 16-byte aligned (the layout
+    mla_decode_plan sizes)."""
+    al = lambda x: (x + 15) // 16 * 16
+    return al(slots * H * D_C * 4) + al(slots * H * 4)
+
+
+class DeviceWorkload:
+    def __init__(self, inp: I.DecodeInputs, device="cuda", split=True, num_workers=None, num_cus=256,
+                 pool=None, table=None):
+        import torch
+        self.inp = inp
+        self.device = device
+        self.cfg = B.make_config(inp.H, inp.D_C, inp.D_R, inp.D_N, inp.D_V, inp.scale,
+                                 _dtype_code(inp.cache_dtype), _dtype_code(inp.act_dtype))
+        if pool is None:
+            pool, table = I.build_paged_pool(inp)
+        self.pool = torch.from_numpy(pool).to(device)
+        self.table = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(device)
+        self.seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(device)
+        self.topk = 0
+        self.topk_idx = None
+        if inp.topk_idx is not None:
+            self.topk_idx = torch.from_numpy(inp.topk_idx.astype(np.int32)).to(device)
+            self.topk = int(inp.topk_idx.shape[1])
+        act = inp.act_dtype
+        self.q_nope = to_device_act(inp.q_nope, act, device)
+        self.q_rope = to_device_act(inp.q_rope, act, device)
+        self.w_uk = to_device_act(inp.w_uk, act, device)
+        self.w_uv = to_device_act(inp.w_uv, act, device)
+        dt = torch.float32 if act == I.DTYPE_F32 else torch.bfloat16
+        Bn, H = inp.B, inp.H
+        self.q_lat = torch.empty((Bn, H, inp.D_C), dtype=dt, device=device)
+        self.o_lat = torch.empty((Bn, H, inp.D_C), dtype=dt, device=device)
+        self.out = torch.empty((Bn, H, inp.D_V), dtype=dt, device=device)
+        self.lse = torch.empty((Bn, H), dtype=torch.float32, device=device)
+        self.split = split
+        self.plan = None
+        self.workspace = None
+        if split:
+            self.plan = B.mla_decode_plan(self.cfg, Bn, inp.seq_lens, 0, self.topk, num_cus)
+            if num_workers is not None:
+                self.plan.num_workers = int(num_workers)
+                self.plan.num_slots = int(num_workers) + Bn - 1
+                self.plan.workspace_bytes = workspace_bytes(H, inp.D_C, self.plan.num_slots)
+            self.workspace = torch.empty(self.plan.workspace_bytes, dtype=torch.uint8, device=device)
+
+    # the four calls ---------------------------------------------------------
+    def absorb(self, stream=None):
+        B.mla_absorb_q(self.cfg, self.q_nope, self.w_uk, self.q_lat, stream)
+
+    def attend(self, stream=None, q_lat=None):
+        ql = self.q_lat if q_lat is None else q_lat
+        if self.split:
+            B.mla_decode_attn(self.cfg, ql, self.q_rope, self.pool, self.table, self.seq_lens, self.topk_idx,
+                              plan=self.plan, workspace=self.workspace, stream=stream)
+        else:
+            B.mla_decode_attn(self.cfg, ql, self.q_rope, self.pool, self.table, self.seq_lens, self.topk_idx,
+                              o_lat=self.o_lat, lse_out=self.lse, stream=stream)
+
+    def combine(self, stream=None):
+        if self.split:
+            B.mla_combine(self.cfg, self.workspace, self.seq_lens, self.plan, self.o_lat, self.lse,
+                          topk=self.topk, stream=stream)
+
+    def up(self, stream=None):
+        B.mla_out_up(self.cfg, self.o_lat, self.w_uv, self.out, stream)
+
+    def step(self, stream=None):
+        self.absorb(stream)
+        self.attend(stream)
+        self.combine(stream)
+        self.up(stream)
+
+    def partials(self):
+        """(o_part [slots, H, D_C], lse_part [slots, H]) views of the workspace (split mode)."""
+        import torch
+        slots = self.plan.num_slots
+        H, DC = self.inp.H, self.inp.D_C
+        n_o = slots * H * DC
+        o_bytes = (n_o * 4 + 15) // 16 * 16
+        ws = self.workspace
+        o = ws[: n_o * 4].view(torch.float32).view(slots, H, DC)
+        l = ws[o_bytes: o_bytes + slots * H * 4].view(torch.float32).view(slots, H)
+        return o, l

@@ -1,0 +1,134 @@
+"""The C-ABI library on the host: it loads, exports every declared entry
+point, and its host-side logic (layout, plan, validation, status codes)
+behaves as the header states.  No GPU work is launched."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_absorb.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mla_latent_kv_absorb_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(B):
+    lib = B.raw_lib()
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_abi_version_and_status_strings(B):
+    assert B.abi_version() == 1
+    for s in (0, 1, 2, 3):
+        assert B.status_string(s) not in ("", "unknown status")
+    assert B.status_string(99) == "unknown status"
+
+
+def v2(B, cache=None):
+    return B.make_config(128, 512, 64, 128, 128, 1 / np.sqrt(192), B.MLA_BF16 if cache is None else cache, B.MLA_BF16)
+
+
+def test_page_layout(B):
+    assert B.page_layout(v2(B)) == (73728, 65536, 73728)
+    pb, ro, so = B.page_layout(v2(B, B.MLA_FP8_E4M3))
+    assert (pb, ro, so) == (32768 + 8192 + 256, 32768, 32768 + 8192)
+    # per-position bytes actually read: 512 + 128 + 4 = 644
+    assert (pb) // 64 == 644
+    tiny = B.make_config(4, 16, 8, 8, 8, 0.25, B.MLA_F32, B.MLA_F32)
+    assert B.page_layout(tiny) == (64 * 24 * 4, 64 * 16 * 4, 64 * 24 * 4)
+
+
+def test_plan_sizes_workspace(B):
+    cfg = v2(B)
+    lens = np.array([16384, 32768, 20000], dtype=np.int32)
+    plan = B.mla_decode_plan(cfg, 3, lens, 0, 0, 256)
+    tiles = int(np.sum((lens + 31) // 32))
+    assert plan.num_workers == min(256, -(-tiles // 16))
+    assert plan.num_slots == plan.num_workers + 2
+    assert plan.workspace_bytes == plan.num_slots * 128 * 512 * 4 + (plan.num_slots * 128 * 4 + 15) // 16 * 16
+    small = B.mla_decode_plan(cfg, 1, np.array([100], np.int32), 0, 0, 256)
+    assert small.num_workers == 1
+    topk = B.mla_decode_plan(cfg, 32, None, 0, 2048, 256)
+    assert topk.num_workers == 128
+
+
+def test_invalid_arguments_rejected_before_launch(B):
+    lib = B.raw_lib()
+    cfg = v2(B)
+    null = None
+    assert lib.mla_absorb_q(ctypes.byref(cfg), null, null, null, 1, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_out_up(ctypes.byref(cfg), null, null, null, 1, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(None, null, null, null, 1, null) == B.MLA_ERR_INVALID_ARG
+    # misaligned pointers
+    p = ctypes.c_void_p(0x1001)
+    assert lib.mla_absorb_q(ctypes.byref(cfg), p, p, p, 1, null) == B.MLA_ERR_INVALID_ARG
+    # unsupported dims for the MFMA path
+    bad = B.make_config(64, 512, 64, 128, 128, 0.1, B.MLA_BF16, B.MLA_BF16)
+    q = ctypes.c_void_p(0x1000)
+    assert lib.mla_absorb_q(ctypes.byref(bad), q, q, q, 1, null) == B.MLA_ERR_UNSUPPORTED
+    # bad block size / dtype
+    bs = v2(B)
+    bs.block_size = 32
+    assert lib.mla_absorb_q(ctypes.byref(bs), q, q, q, 1, null) == B.MLA_ERR_INVALID_ARG
+    mixed = B.make_config(4, 16, 8, 8, 8, 0.25, B.MLA_BF16, B.MLA_F32)
+    assert lib.mla_absorb_q(ctypes.byref(mixed), q, q, q, 1, null) == B.MLA_ERR_UNSUPPORTED
+    # attention: split mode without workspace, dense with topk > 0, batch < 1
+    plan = B.MlaPlan(4, 4, 1 << 20)
+    args = [ctypes.byref(cfg), q, q, q, 10, q, 4, q, None, 0, 1, ctypes.byref(plan), None, 0, None, None, None]
+    assert lib.mla_decode_attn(*args) == B.MLA_ERR_INVALID_ARG
+    args2 = list(args)
+    args2[9] = 5
+    assert lib.mla_decode_attn(*args2) == B.MLA_ERR_INVALID_ARG
+    args3 = list(args)
+    args3[10] = 0
+    assert lib.mla_decode_attn(*args3) == B.MLA_ERR_INVALID_ARG
+    # too small workspace
+    args4 = list(args)
+    args4[12] = q
+    args4[13] = 100
+    assert lib.mla_decode_attn(*args4) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine(ctypes.byref(cfg), q, 100, q, 0, 1, ctypes.byref(plan), q, None, None) == B.MLA_ERR_INVALID_ARG
+
+
+def test_host_metadata_check(B):
+    cfg = v2(B)
+    lens = np.array([100, 64], np.int32)
+    table = np.array([[0, 1], [2, -1]], np.int32)
+    assert B.mla_check_decode_inputs_host(cfg, lens, table, 3) == (0, -1)
+    assert B.mla_check_decode_inputs_host(cfg, lens, table, 2) == (1, 1)       # page 2 out of range
+    assert B.mla_check_decode_inputs_host(cfg, np.array([100, 0], np.int32), table, 3) == (1, 1)
+    assert B.mla_check_decode_inputs_host(cfg, np.array([200, 64], np.int32), table, 3) == (1, 0)  # table too short
+    good = np.array([[0, 5, 99, -1], [3, 4, 63, -1]], np.int32)
+    assert B.mla_check_decode_inputs_host(cfg, lens, table, 3, good) == (0, -1)
+    unsorted = np.array([[5, 0, 99, -1], [3, 4, 63, -1]], np.int32)
+    assert B.mla_check_decode_inputs_host(cfg, lens, table, 3, unsorted) == (1, 0)
+    dup = np.array([[0, 5, 99, -1], [3, 3, 63, -1]], np.int32)
+    assert B.mla_check_decode_inputs_host(cfg, lens, table, 3, dup) == (1, 1)
+    out_of_range = np.array([[0, 5, 100, -1], [3, 4, 63, -1]], np.int32)
+    assert B.mla_check_decode_inputs_host(cfg, lens, table, 3, out_of_range) == (1, 0)
+    pad_inside = np.array([[0, -1, 99, -1], [3, 4, 63, -1]], np.int32)
+    assert B.mla_check_decode_inputs_host(cfg, lens, table, 3, pad_inside) == (1, 0)
+
+
+def test_binding_rejects_bad_tensors(B):
+    torch = pytest.importorskip("torch")
+    cfg = v2(B)
+    with pytest.raises(ValueError):
+        B.mla_absorb_q(cfg, torch.zeros(1, 128, 128), torch.zeros(128, 512, 128), torch.zeros(1, 128, 512))

@@ -1,0 +1,370 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Tolerances: max |err| <= 2e-2 * max|ref| for BF16 / FP8 caches; max |err| <=
+1e-4 (absolute) for the float32 configuration; index handling bit-exact.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from mla_latent_kv_absorb_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 2e-2
+F32_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+@pytest.fixture(scope="module")
+def R(torch):
+    from mla_latent_kv_absorb_amd import runner
+    return runner
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def to_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def oracle_request(inp, b, heads=None):
+    lo, hi = inp.request(b)
+    if inp.cache_dtype == I.DTYPE_FP8:
+        c = oracle.dequant_fp8_latent(inp.c_codes[lo:hi], inp.c_scales[lo:hi])
+    else:
+        c = inp.c_kv[lo:hi]
+    picked = None if inp.topk_idx is None else inp.topk_idx[b]
+    return oracle.decode_unabsorbed(c, inp.k_rope[lo:hi], inp.q_nope[b], inp.q_rope[b], inp.w_uk, inp.w_uv,
+                                    inp.scale, picked=picked, heads=heads)
+
+
+def assert_close(got, ref, tol_rel=REL_TOL, abs_tol=None, what=""):
+    err = np.max(np.abs(got - ref))
+    if abs_tol is not None:
+        assert err <= abs_tol, f"{what}: max|err| {err:.3g} > {abs_tol}"
+    else:
+        bound = tol_rel * np.max(np.abs(ref))
+        assert err <= bound, f"{what}: max|err| {err:.3g} > {bound:.3g} (= {tol_rel} x max|ref|)"
+    return err
+
+
+def check_step(torch, R, inp, split=True, num_workers=None, requests=None, heads=None, f32=False):
+    w = R.DeviceWorkload(inp, split=split, num_workers=num_workers)
+    w.step()
+    torch.cuda.synchronize()
+    o_lat, out, lse = to_np(w.o_lat), to_np(w.out), to_np(w.lse)
+    reqs = range(inp.B) if requests is None else requests
+    hs = list(range(inp.H)) if heads is None else list(heads)
+    for b in reqs:
+        r_out, r_lse, r_olat = oracle_request(inp, b, heads=hs)
+        tag = f"b={b}"
+        if f32:
+            assert_close(out[b][hs], r_out, abs_tol=F32_TOL, what="out " + tag)
+            assert_close(o_lat[b][hs], r_olat, abs_tol=F32_TOL, what="o_lat " + tag)
+            assert_close(lse[b][hs], r_lse, abs_tol=F32_TOL, what="lse " + tag)
+        else:
+            assert_close(out[b][hs], r_out, what="out " + tag)
+            assert_close(o_lat[b][hs], r_olat, what="o_lat " + tag)
+            assert_close(lse[b][hs], r_lse, what="lse " + tag)
+    return w
+
+
+def custom_inputs(c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, seq_lens, cache, act, scale, topk_idx=None,
+                  codes=None, scales=None, perm_seed=0):
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    offsets = np.zeros(len(seq_lens) + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(seq_lens)
+    n_pages = int(np.sum(-(-seq_lens // 64)))
+    perm = np.random.default_rng(perm_seed).permutation(n_pages)
+    H, D_C = w_uk.shape[0], w_uk.shape[1]
+    return I.DecodeInputs(H=H, D_C=D_C, D_R=k_rope.shape[1], D_N=w_uk.shape[2], D_V=w_uv.shape[1],
+                          cache_dtype=cache, act_dtype=act, scale=float(scale), seq_lens=seq_lens,
+                          offsets=offsets, c_kv=np.ascontiguousarray(c_kv, dtype=np.float32),
+                          k_rope=np.ascontiguousarray(k_rope, dtype=np.float32),
+                          q_nope=np.ascontiguousarray(q_nope, dtype=np.float32),
+                          q_rope=np.ascontiguousarray(q_rope, dtype=np.float32),
+                          w_uk=np.ascontiguousarray(w_uk, dtype=np.float32),
+                          w_uv=np.ascontiguousarray(w_uv, dtype=np.float32), page_perm=perm,
+                          c_codes=codes, c_scales=scales, topk_idx=topk_idx)
+
+
+# ---------------------------------------------------------------------------
+# float32 configuration (tiny dims)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("split", [False, True])
+def test_tiny_fp32_full_step(torch, R, split):
+    _log(f"tiny_fp32 split={split}")
+    inp = I.make_inputs("tiny_fp32")
+    check_step(torch, R, inp, split=split, f32=True)
+
+
+def test_tiny_fp32_ragged_multi_request_splits(torch, R):
+    _log("tiny_fp32 ragged")
+    inp = I.make_inputs("tiny_fp32", seq_lens=[1, 33, 64, 100, 7])
+    for nw in (1, 2, 3, 9):
+        check_step(torch, R, inp, split=True, num_workers=nw, f32=True)
+
+
+def test_three_token_worked_example_on_gpu(torch, R):
+    """The page's worked example embedded in tiny MLA dims, run on the GPU
+    ("What attention stores, and what DeepSeek changed", first section)."""
+    _log("E1 on gpu")
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "e1_three_token.json")))
+    K = np.array([int(c) for c in g["K_digits"]], dtype=np.float64).reshape(3, 3).T
+    V = np.array([int(c) for c in g["V_digits"]], dtype=np.float64).reshape(3, 3).T
+    H, D_C, D_R, D_N, D_V = 4, 16, 8, 8, 8
+    c = np.zeros((3, D_C)); c[:, 0:3] = K; c[:, 8:11] = V; c[np.arange(3), 12 + np.arange(3)] = 1
+    w_uk = np.zeros((H, D_C, D_N)); w_uv = np.zeros((H, D_V, D_C))
+    for n in range(3):
+        w_uk[:, n, n] = 1
+        w_uv[:, n, 8 + n] = 1
+    q_nope = np.zeros((1, H, D_N)); q_nope[0, 0, 0:3] = g["q3"]
+    inp = custom_inputs(c, np.zeros((3, D_R)), q_nope, np.zeros((1, H, D_R)), w_uk, w_uv, [3],
+                        I.DTYPE_F32, I.DTYPE_F32, 1 / math.sqrt(g["d_h"]))
+    w = R.DeviceWorkload(inp, split=False)
+    w.step()
+    torch.cuda.synchronize()
+    out = to_np(w.out)[0, 0, :3]
+    weights = to_np(w.o_lat)[0, 0, 12:15]
+    tol = 0.5 * 10 ** -g["printed_decimals"] + 1e-6
+    np.testing.assert_allclose(out, g["printed_out"], atol=tol)
+    np.testing.assert_allclose(weights, g["printed_weights"], atol=tol)
+    scores = np.log(weights) + to_np(w.lse)[0, 0]
+    np.testing.assert_allclose(scores, g["printed_scores"], atol=tol)
+
+
+# ---------------------------------------------------------------------------
+# V2 dims, BF16 cache: several tiles, ragged tails, split counts
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def v2_ragged():
+    return I.make_inputs("v2_batched", seed=11, seq_lens=[200, 1000, 77])
+
+
+@pytest.mark.parametrize("mode", ["direct", 1, 2, 7, "auto"])
+def test_v2_bf16_ragged(torch, R, v2_ragged, mode):
+    _log(f"v2 ragged mode={mode}")
+    if mode == "direct":
+        check_step(torch, R, v2_ragged, split=False)
+    else:
+        check_step(torch, R, v2_ragged, split=True, num_workers=None if mode == "auto" else mode)
+
+
+def test_v2_page_order_is_bit_identical(torch, R, v2_ragged):
+    _log("page permutation")
+    import dataclasses
+    other = dataclasses.replace(v2_ragged, page_perm=np.random.default_rng(99).permutation(v2_ragged.page_perm.size))
+    outs = []
+    for inp in (v2_ragged, other):
+        w = R.DeviceWorkload(inp, split=True, num_workers=5)
+        w.step()
+        torch.cuda.synchronize()
+        outs.append((w.o_lat.clone(), w.out.clone(), w.lse.clone()))
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+def test_v2_repeat_runs_bit_identical(torch, R, v2_ragged):
+    _log("determinism")
+    w = R.DeviceWorkload(v2_ragged, split=True)
+    w.step()
+    a = (w.o_lat.clone(), w.out.clone())
+    for _ in range(3):
+        w.step()
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], w.o_lat) and torch.equal(a[1], w.out)
+
+
+def test_v2_absorb_and_up_projection_alone(torch, R, v2_ragged):
+    _log("absorb/out_up alone")
+    inp = v2_ragged
+    w = R.DeviceWorkload(inp, split=False)
+    w.absorb()
+    torch.cuda.synchronize()
+    ref = oracle.absorb_query(inp.q_nope, inp.w_uk)
+    assert_close(to_np(w.q_lat), ref, what="q_lat")
+    x = I.round_to_bf16(np.random.default_rng(3).standard_normal((inp.B, inp.H, inp.D_C)).astype(np.float32))
+    w.o_lat.copy_(R.to_device_act(x, I.DTYPE_BF16, "cuda"))
+    w.up()
+    torch.cuda.synchronize()
+    assert_close(to_np(w.out), oracle.up_project(x, inp.w_uv), what="out_up")
+
+
+def test_v2_topk_all_positions_equals_dense(torch, R):
+    _log("topk == dense")
+    dense = I.make_inputs("v2_batched", seed=12, seq_lens=[300, 129])
+    import dataclasses
+    idx = np.full((2, 300), -1, dtype=np.int32)
+    idx[0, :300] = np.arange(300)
+    idx[1, :129] = np.arange(129)
+    sparse = dataclasses.replace(dense, topk_idx=idx)
+    wd = R.DeviceWorkload(dense, split=False)
+    ws = R.DeviceWorkload(sparse, split=False)
+    wd.step(); ws.step()
+    torch.cuda.synchronize()
+    assert torch.equal(wd.o_lat, ws.o_lat)
+    assert torch.equal(wd.out, ws.out)
+
+
+def test_rescale_path_with_growing_scores(torch, R):
+    """Scores that grow along the context force the online-softmax rescale
+    several times."""
+    _log("rescale path")
+    rng = np.random.default_rng(5)
+    T, H, D_C, D_R = 2000, 128, 512, 64
+    c = rng.standard_normal((T, D_C)).astype(np.float32) * 0.1
+    c[:, 0] = np.arange(T) * 0.05
+    c = I.round_to_bf16(c)
+    kr = I.round_to_bf16(rng.standard_normal((T, D_R)).astype(np.float32) * 0.1)
+    q_lat = np.zeros((1, H, D_C), np.float32)
+    q_lat[0, :, 0] = np.linspace(0.5, 3.0, H)
+    q_lat = I.round_to_bf16(q_lat)
+    qr = I.round_to_bf16(rng.standard_normal((1, H, D_R)).astype(np.float32))
+    wz = np.zeros((H, D_C, 128), np.float32)
+    inp = custom_inputs(c, kr, np.zeros((1, H, 128), np.float32), qr, wz, np.zeros((H, 128, D_C), np.float32),
+                        [T], I.DTYPE_BF16, I.DTYPE_BF16, 1 / math.sqrt(192))
+    for split in (False, True):
+        w = R.DeviceWorkload(inp, split=split, num_workers=3)
+        w.attend(q_lat=R.to_device_act(q_lat, I.DTYPE_BF16, "cuda"))
+        w.combine()
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle.latent_decode(q_lat[0], qr[0], c, kr, inp.scale)
+        assert_close(to_np(w.o_lat)[0], ref_o, what=f"o_lat split={split}")
+        assert_close(to_np(w.lse)[0], ref_l, what=f"lse split={split}")
+
+
+# ---------------------------------------------------------------------------
+# FP8 latent + index lists
+# ---------------------------------------------------------------------------
+def test_fp8_every_code_converts_exactly(torch, R):
+    """Each finite E4M3 code, weighted by probability 1 (zero query, one
+    position), comes back as its exact value times the position's scale."""
+    _log("fp8 codes")
+    H, D_C, D_R = 128, 512, 64
+    codes = np.tile(np.arange(256, dtype=np.uint8), 2)[None, :]
+    codes[:, (codes[0] & 0x7F) == 0x7F] = 0  # NaN codes stay out of the arithmetic
+    codes = np.concatenate([codes, codes[:, ::-1]])            # two requests, one position each
+    scales = np.array([1.0, 0.375], dtype=np.float32)
+    inp = custom_inputs(np.zeros((2, D_C)), np.zeros((2, D_R)), np.zeros((2, H, 128)), np.zeros((2, H, D_R)),
+                        np.zeros((H, D_C, 128)), np.zeros((H, 128, D_C)), [1, 1], I.DTYPE_FP8, I.DTYPE_BF16,
+                        0.1, codes=codes, scales=scales)
+    w = R.DeviceWorkload(inp, split=False)
+    w.attend(q_lat=torch.zeros_like(w.q_lat))
+    torch.cuda.synchronize()
+    got = to_np(w.o_lat)
+    for b in range(2):
+        ref = oracle.e4m3_to_f64(codes[b]) * scales[b]
+        for h in (0, 63, 127):
+            assert np.array_equal(got[b, h], ref), f"request {b} head {h}"
+
+
+def _bit_pattern_case(cache, seed):
+    rng = np.random.default_rng(seed)
+    H, D_C, D_R, T, B = 128, 512, 64, 4096, 2
+    pos = np.arange(T)
+    c = np.zeros((B * T, D_C), np.float32)
+    for d in range(12):
+        c[:, d] = np.tile((pos >> d) & 1, B)
+    codes = scales = None
+    if cache == I.DTYPE_FP8:
+        codes = np.where(c > 0, 0x38, 0).astype(np.uint8)
+        scales = np.ones(B * T, np.float32)
+    idx = np.full((B, 160), -1, np.int32)
+    for b in range(B):
+        idx[b, :128] = np.sort(rng.choice(T, 128, replace=False))
+    inp = custom_inputs(c, np.zeros((B * T, D_R)), np.zeros((B, H, 128)), np.zeros((B, H, D_R)),
+                        np.zeros((H, D_C, 128)), np.zeros((H, 128, D_C)), [T] * B, cache, I.DTYPE_BF16, 0.1,
+                        topk_idx=idx, codes=codes, scales=scales, perm_seed=seed)
+    return inp, idx
+
+
+@pytest.mark.parametrize("cache", [I.DTYPE_BF16, I.DTYPE_FP8])
+def test_topk_index_handling_bit_exact(torch, R, cache):
+    """Zero queries give every picked position probability 1; latent dim d of
+    position p holds bit d of p.  With one worker the float32 partial is
+    exactly (number of picked positions with bit d set) / 128, so a wrong,
+    missing or repeated index changes its bits."""
+    _log(f"topk bit pattern {cache}")
+    inp, idx = _bit_pattern_case(cache, seed=7)
+    w = R.DeviceWorkload(inp, split=True, num_workers=1)
+    w.attend(q_lat=torch.zeros_like(w.q_lat))
+    torch.cuda.synchronize()
+    part_o, part_l = w.partials()
+    part_o = part_o.cpu().numpy()
+    for b in range(inp.B):
+        sel = idx[b][idx[b] >= 0]
+        expect = np.zeros(inp.D_C, np.float32)
+        for d in range(12):
+            expect[d] = np.float32(np.sum((sel >> d) & 1)) / np.float32(128)
+        got = part_o[0 + b]  # worker 0 covers every request: slot = 0 + b
+        assert np.array_equal(got, np.broadcast_to(expect, got.shape)), f"request {b}"
+        np.testing.assert_allclose(part_l[b].cpu().numpy(), math.log(128), rtol=1e-6)
+
+
+def test_fp8_topk_small(torch, R):
+    _log("fp8 topk small")
+    inp = I.make_inputs("v2_fp8_topk", seed=21, batch=2, ctx=(3000, 3000), topk=100)
+    inp.topk_idx[1, 96:] = -1  # padding entries
+    for split in (False, True):
+        check_step(torch, R, inp, split=split)
+
+
+def test_fp8_dense_small(torch, R):
+    _log("fp8 dense small")
+    import dataclasses
+    inp = dataclasses.replace(I.make_inputs("v2_fp8_topk", seed=22, batch=2, ctx=(500, 1500), topk=0))
+    check_step(torch, R, inp, split=True)
+
+
+def test_out_of_range_indices_are_skipped(torch, R):
+    _log("out of range indices")
+    inp = I.make_inputs("v2_fp8_topk", seed=23, batch=1, ctx=(1000, 1000), topk=40)
+    bad = inp.topk_idx.copy()
+    bad[0, 10] = 5000      # beyond the context: skipped
+    bad[0, 11] = -7        # negative: skipped
+    import dataclasses
+    w = R.DeviceWorkload(dataclasses.replace(inp, topk_idx=bad), split=False)
+    w.step()
+    torch.cuda.synchronize()
+    ref_out, _, _ = oracle_request(dataclasses.replace(inp, topk_idx=bad), 0)
+    assert_close(to_np(w.out)[0], ref_out, what="out")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads (sampled against the oracle)
+# ---------------------------------------------------------------------------
+def test_v2_single_full(torch, R):
+    _log("v2_single full")
+    check_step(torch, R, I.make_inputs("v2_single"), split=True)
+
+
+def test_v2_batched_full_size_sampled(torch, R):
+    _log("v2_batched full size")
+    inp = I.make_inputs("v2_batched")
+    check_step(torch, R, inp, split=True, requests=[0, 31, 63], heads=[0, 77, 127])
+
+
+def test_v2_long_layer_sampled(torch, R):
+    _log("v2_long one layer")
+    inp = I.make_inputs("v2_long", layer=29)
+    check_step(torch, R, inp, split=True, requests=[0], heads=[0, 64, 127])
+
+
+def test_fp8_topk_full_size_sampled(torch, R):
+    _log("v2_fp8_topk full size")
+    inp = I.make_inputs("v2_fp8_topk")
+    check_step(torch, R, inp, split=True, requests=[0, 31], heads=[0, 127])

@@ -294,12 +294,22 @@ def test_oracle_catches_planted_mistakes():
 # ----------------------------------------------------------------------------
 # The input generator (shared by both sides) against library conversions.
 # ----------------------------------------------------------------------------
-def test_generator_bf16_rounding_matches_torch():
-    torch = pytest.importorskip("torch")
-    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 3
+def test_generator_bf16_rounding_is_nearest_even():
+    """BF16 rounding of the generator against a brute-force nearest search
+    (ties to the even pattern) on values including exact ties."""
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(20000) * 3).astype(np.float32)
+    u = x.view(np.uint32)
+    ties = ((u & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)  # exactly halfway
+    x = np.concatenate([x, ties[:2000]])
     ours = inputs.round_to_bf16(x)
-    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
-    assert np.array_equal(ours, ref)
+    lo = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+    hi = ((x.view(np.uint32) & np.uint32(0xFFFF0000)) + np.uint32(0x10000)).view(np.float32).astype(np.float64)
+    xd = x.astype(np.float64)
+    dlo, dhi = np.abs(xd - lo), np.abs(hi - xd)
+    lo_even = ((lo.astype(np.float32).view(np.uint32) >> 16) & 1) == 0
+    expect = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo_even, lo, hi)))
+    assert np.array_equal(ours.astype(np.float64), expect)
 
 
 def test_generator_e4m3_encode_matches_torch():
