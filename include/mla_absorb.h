@@ -78,7 +78,7 @@ typedef struct {
   int32_t d_nope;        /* D_N, per-head content query width */
   int32_t d_v;           /* D_V, per-head value width */
   int32_t block_size;    /* positions per page, must be MLA_PAGE_TOKENS */
-  float softmax_scale;   /* usually 1/sqrt(d_nope + d_rope) */
+  float softmax_scale;   /* > 0, usually 1/sqrt(d_nope + d_rope) */
   int32_t cache_dtype;   /* mla_dtype */
   int32_t act_dtype;     /* mla_dtype, F32 or BF16 */
 } mla_config;

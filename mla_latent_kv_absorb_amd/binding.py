@@ -15,7 +15,8 @@ from typing import Optional
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
+LIB_PATH = os.environ.get("MLA_ABSORB_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libmla_absorb.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_LAUNCH = 0, 1, 2, 3
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2

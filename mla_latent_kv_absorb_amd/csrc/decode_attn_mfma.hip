@@ -54,10 +54,17 @@ constexpr int kC8Row = kLatent;     // bytes of one FP8 latent row (512)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// 16-byte chunk swizzle: chunk c of row r lives at chunk c ^ swz(r % 8).
-// Makes 8 consecutive rows hit distinct bank groups for 16-byte row reads and
-// 4-row x 32-byte blocks distinct for the transposing 8-byte reads.
-__device__ __forceinline__ constexpr int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// LDS row swizzles (16-byte chunks).  Chunk c of latent row r is stored at
+// chunk c ^ swz(r), of rotary row r at c ^ swz_r(r).  Chosen so that the three
+// operand read patterns -- 16-byte row reads for the scores (16 consecutive
+// rows per access phase), 8-byte transposing reads (4 rows x 64 bytes) and
+// the rotary row reads -- touch distinct banks on a 64-bank LDS and on a
+// 32-bank one.
+__device__ __forceinline__ constexpr int swz(int r) {
+  r &= 15;
+  return (((r & 3) << 2) | ((r >> 2) & 3)) ^ (r & 2);
+}
+__device__ __forceinline__ constexpr int swz_r(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
 // HBM -> LDS without registers: lane l's bytes land at lds_addr + size * l.
 // lds_addr must be wave-uniform (it goes to M0).
@@ -107,17 +114,25 @@ __device__ __forceinline__ int32_t sload(const int32_t* p) {
 
 template <bool FP8>
 struct Cfg {
-  static constexpr int NS = FP8 ? 6 : 4;                       // ring stages
+  static constexpr int NS = FP8 ? 5 : 4;                       // ring stages
   static constexpr int C_STAGE = FP8 ? kTile * kC8Row : kTile * kCRow;
   static constexpr int R_STAGE = kTile * kRRow;
   static constexpr int SC_STAGE = FP8 ? kTile * 4 : 0;
   static constexpr int STAGE = C_STAGE + R_STAGE + SC_STAGE;
   static constexpr int CONV_OFF = NS * STAGE;                  // BF16 copy of an FP8 tile
   static constexpr int CONV = FP8 ? kTile * kCRow : 0;
-  static constexpr int MASK_OFF = CONV_OFF + CONV;
+  static constexpr int LIST_OFF = CONV_OFF + CONV;             // page ids / row codes of a chunk
+  static constexpr int LIST = 2048;                            // entries (int32)
+  static constexpr int MASK_OFF = LIST_OFF + LIST * 4;
   static constexpr int LDS_BYTES = MASK_OFF + NS * 4;
   static constexpr int DMA_PER_WAVE = FP8 ? 6 : 9;             // loads per wave per tile
 };
+
+// Tiles of one request processed between two pipeline drains: bounded by the
+// LDS list (2048 page ids cover 4096 dense tiles; 2048 index entries cover 64
+// gathered tiles).
+template <bool TOPK>
+__device__ __forceinline__ constexpr int chunk_tiles() { return TOPK ? 2048 / kTile : 4000; }
 
 template <int NS, int DPW>
 __device__ __forceinline__ void wait_tiles(int64_t ahead) {
@@ -142,17 +157,43 @@ struct Loader {
     return T > 0 ? tiles_of(T) : 0;
   }
 
-  // Issue this wave's share of tile t of request b into ring stage st.
-  __device__ __forceinline__ void issue(int st, int32_t b, int32_t t, char* smem) const {
+  // Fill the LDS list for tiles [tc0, tc0 + len) of request b (all threads;
+  // the caller synchronises).  Dense: page id of each page the tiles touch,
+  // -1 when outside the table or the pool.  Gathered: per listed position the
+  // row code page * 64 + slot, -1 for padding, out-of-range or invalid pages.
+  __device__ __forceinline__ void fill_list(int32_t b, int32_t tc0, int32_t len, int32_t T, LDS int32_t* list,
+                                            int tid) const {
+    if (!TOPK) {
+      const int32_t p0 = tc0 >> 1;
+      const int32_t np = ((tc0 + len - 1) >> 1) - p0 + 1;
+      for (int k = tid; k < np; k += 256) {
+        const int32_t p = p0 + k;
+        int32_t page = p < a.bt_stride ? a.block_table[(int64_t)b * a.bt_stride + p] : -1;
+        list[k] = (page >= 0 && page < a.num_pages) ? page : -1;
+      }
+    } else {
+      const int32_t n = len * kTile;
+      for (int k = tid; k < n; k += 256) {
+        const int32_t lp = tc0 * kTile + k;
+        const int32_t idx = lp < a.topk ? a.topk_idx[(int64_t)b * a.topk + lp] : -1;
+        bool v = idx >= 0 && idx < T && (idx >> 6) < a.bt_stride;
+        const int32_t page = v ? a.block_table[(int64_t)b * a.bt_stride + (idx >> 6)] : -1;
+        v = v && page >= 0 && page < a.num_pages;
+        list[k] = v ? page * 64 + (idx & 63) : -1;
+      }
+    }
+  }
+
+  // Issue this wave's share of tile t (chunk starts at tc0) into stage st.
+  __device__ __forceinline__ void issue(int st, int32_t t, int32_t tc0, int32_t T, const LDS int32_t* list,
+                                        char* smem) const {
     using C = Cfg<FP8>;
     const uint32_t sb = smem_base + st * C::STAGE;
-    const int32_t T = sload(a.seq_lens + b);
     const uint8_t* pool = a.pool;
     uint32_t bits = 0;
     if (!TOPK) {
-      const bool in_table = (t >> 1) < a.bt_stride;
-      const int32_t page = in_table ? sload(a.block_table + (int64_t)b * a.bt_stride + (t >> 1)) : -1;
-      const bool pv = page >= 0 && page < a.num_pages;
+      const int32_t page = __builtin_amdgcn_readfirstlane(list[(t >> 1) - (tc0 >> 1)]);
+      const bool pv = page >= 0;
       const uint8_t* pg = pool + (pv ? (int64_t)page * a.page_bytes : 0);
       const int slot0 = (t & 1) * kTile + 8 * w;  // first row of this wave in the page
 #pragma unroll
@@ -167,27 +208,32 @@ struct Loader {
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          dma16(pg + (int64_t)(slot0 + k) * kCRow + 16 * (lane ^ swz(k)), sb + (8 * w + k) * kCRow);
+          dma16(pg + (int64_t)(slot0 + k) * kCRow + 16 * (lane ^ swz(8 * w + k)), sb + (8 * w + k) * kCRow);
       }
       const int rr = lane >> 3, rc = lane & 7;
-      dma16(pg + a.rope_off + (int64_t)(slot0 + rr) * kRRow + 16 * (rc ^ swz(rr)),
+      dma16(pg + a.rope_off + (int64_t)(slot0 + rr) * kRRow + 16 * (rc ^ swz_r(8 * w + rr)),
             sb + C::C_STAGE + 8 * w * kRRow);
       if (FP8) {
         if (lane < 8) dma4(pg + a.scale_off + (int64_t)(slot0 + lane) * 4, sb + C::C_STAGE + C::R_STAGE + 32 * w);
       }
     } else {
-      // gathered rows: one index per row
+      // gathered rows: this wave's 8 row codes
+      const LDS int32_t* lc = list + (t - tc0) * kTile + 8 * w;
+      const i32x4 c0 = *(const LDS i32x4*)lc;
+      const i32x4 c1 = *(const LDS i32x4*)(lc + 4);
+      int32_t code[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        code[k] = __builtin_amdgcn_readfirstlane(c0[k]);
+        code[k + 4] = __builtin_amdgcn_readfirstlane(c1[k]);
+      }
       const uint8_t* pgk[8];
       int slk[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int lp = t * kTile + 8 * w + k;
-        int32_t idx = lp < a.topk ? sload(a.topk_idx + (int64_t)b * a.topk + lp) : -1;
-        bool v = idx >= 0 && idx < T && (idx >> 6) < a.bt_stride;
-        int32_t page = v ? sload(a.block_table + (int64_t)b * a.bt_stride + (idx >> 6)) : 0;
-        v = v && page >= 0 && page < a.num_pages;
-        pgk[k] = pool + (v ? (int64_t)page * a.page_bytes : 0);
-        slk[k] = v ? (idx & 63) : 0;
+        const bool v = code[k] >= 0;
+        pgk[k] = pool + (v ? (int64_t)(code[k] >> 6) * a.page_bytes : 0);
+        slk[k] = v ? (code[k] & 63) : 0;
         if (v) bits |= 1u << k;
       }
       constexpr int CR = FP8 ? kC8Row : kCRow;
@@ -199,7 +245,8 @@ struct Loader {
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) dma16(pgk[k] + slk[k] * CR + 16 * (lane ^ swz(k)), sb + (8 * w + k) * kCRow);
+        for (int k = 0; k < 8; ++k)
+          dma16(pgk[k] + slk[k] * CR + 16 * (lane ^ swz(8 * w + k)), sb + (8 * w + k) * kCRow);
       }
       const int rr = lane >> 3, rc = lane & 7;
       const uint8_t* rp = pgk[0];
@@ -209,7 +256,7 @@ struct Loader {
         rp = (rr == k) ? pgk[k] : rp;
         rs = (rr == k) ? slk[k] : rs;
       }
-      dma16(rp + a.rope_off + rs * kRRow + 16 * (rc ^ swz(rr)), sb + C::C_STAGE + 8 * w * kRRow);
+      dma16(rp + a.rope_off + rs * kRRow + 16 * (rc ^ swz_r(8 * w + rr)), sb + C::C_STAGE + 8 * w * kRRow);
       if (FP8) {
         if (lane < 8) {
           const uint8_t* sp = pgk[0];
@@ -275,27 +322,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   }
 
   // ---- per-lane LDS offsets (relative to a tile) ----
-  // The swizzle only touches the low 3 bits of a 16-byte chunk index, so the
-  // operand addresses are a few per-lane bases plus compile-time offsets.
+  // The swizzles only touch the low 4 bits of a chunk index, so every operand
+  // address is one of a few per-lane bases plus a compile-time offset.
   const int row = lane & 31;
-  const int sw_row = swz(lane & 7);
-  int s_off[4];   // latent row operand of K-block kb = 4u+v: s_off[v] + 128u
-  int r_off[4];   // rotary row operand of K-block v
+  int s_off[8];   // latent operand of K-block k: s_off[k & 7] + 256 * (k >> 3)
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int c = 16 * ((2 * v + hi) ^ sw_row);
-    s_off[v] = row * kCRow + c;
-    r_off[v] = row * kRRow + c;
-  }
-  int tr_off[2];  // transposed latent operand of column block mb = 2p+e: tr_off[e] + 128p
+  for (int v = 0; v < 8; ++v) s_off[v] = row * kCRow + 16 * ((2 * v + hi) ^ swz(row));
+  int r_off[4];   // rotary operand of K-block v
+#pragma unroll
+  for (int v = 0; v < 4; ++v) r_off[v] = row * kRRow + 16 * ((2 * v + hi) ^ swz_r(row));
+  int tr_off[2][4];  // transposed latent operand, column block mb, rows t and t + 8:
+                     // tr_off[half][mb & 3] + 256 * (mb >> 2) + 16 KiB * kb2
   {
     const int j16 = lane & 15, g16 = lane >> 4, hh = g16 >> 1, ch = g16 & 1;
-    const int tr_row = 4 * hh + (j16 >> 2);             // rows 16*kb2 + tr_row and +8
-    const int tr_sw = swz(tr_row & 7);
-    const int lo = (2 * ch + ((j16 & 3) >> 1)) ^ (tr_sw & 3);
+    const int tr_row = 4 * hh + (j16 >> 2);             // 0..7
+    const int lo = 2 * ch + ((j16 & 3) >> 1);
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-      tr_off[e] = tr_row * kCRow + 64 * (e ^ (tr_sw >> 2)) + 16 * lo + (j16 & 1) * 8;
+    for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        tr_off[h8][e] = (tr_row + 8 * h8) * kCRow + 16 * ((4 * e + lo) ^ swz(tr_row + 8 * h8)) + (j16 & 1) * 8;
   }
   const int head = 32 * w + row;
 
@@ -305,19 +351,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   bf16x8 q[32];
   bf16x8 qr[4];
 
-  // ---- prologue ----
-  int32_t ib = b0, it = t0;      // issue cursor
-  int32_t cb = b0, ct = t0;      // compute cursor
-  auto advance = [&](int32_t& b, int32_t& t) {
-    ++t;
-    while (b < a.batch && t >= ld.ntiles(b)) { t = 0; ++b; }
-  };
-  int64_t issued = 0;
-  const int64_t pro = n < NS - 1 ? n : NS - 1;
-  for (; issued < pro; ++issued) {
-    ld.issue((int)(issued % NS), ib, it, smem);
-    advance(ib, it);
-  }
+  int32_t cb = b0, ct = t0;      // current request and tile
+  LDS int32_t* list = (LDS int32_t*)(L + C::LIST_OFF);
 
   if (n == 0) {  // only in direct mode: a request with no position
     if (DIRECT) {
@@ -334,172 +369,201 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     if (cb >= a.batch) break;  // unreachable when the tile accounting is consistent
     const int32_t nt_cb = ld.ntiles(cb);
     const int64_t left_in_req = nt_cb - ct;
-    const int64_t seg_len = left_in_req < n - i ? left_in_req : n - i;
+    const int32_t seg_len = (int32_t)(left_in_req < n - i ? left_in_req : n - i);
     if (seg_len <= 0) break;
+    const int32_t T = sload(a.seq_lens + cb);
 
-    // Drain (previous segment's output stores count on vmcnt too), then fetch
-    // this request's queries and make sure they have arrived before more
-    // tiles go in flight behind them.
-    wait_vmcnt<0>();
-    __syncthreads();
-    {
-      const __bf16* ql = (const __bf16*)a.q_lat + ((int64_t)cb * kHeads + head) * kLatent + 8 * hi;
-      const __bf16* qp = (const __bf16*)a.q_rope + ((int64_t)cb * kHeads + head) * kRope + 8 * hi;
-#pragma unroll
-      for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8*)(ql + 16 * kb);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) qr[kb] = *(const bf16x8*)(qp + 16 * kb);
-#pragma unroll
-      for (int kb = 0; kb < 32; ++kb) asm volatile("" ::"v"(q[kb]));
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) asm volatile("" ::"v"(qr[kb]));
-    }
 #pragma unroll
     for (int mb = 0; mb < 16; ++mb) O[mb] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int64_t j = 0; j < seg_len; ++j, ++i) {
-      const int st = (int)(i % NS);
-      if (j > 0) {
-        wait_tiles<NS, C::DMA_PER_WAVE>(n - 1 - i);
-        __syncthreads();
+    for (int32_t tc0 = ct; tc0 < ct + seg_len; tc0 += chunk_tiles<TOPK>()) {
+      const int32_t clen = min(chunk_tiles<TOPK>(), ct + seg_len - tc0);
+      // Drain (earlier output stores count on vmcnt too), then stage this
+      // chunk's page ids / row codes in LDS and, at a segment start, fetch the
+      // request's queries -- all before tiles go in flight again.
+      wait_vmcnt<0>();
+      __syncthreads();
+      ld.fill_list(cb, tc0, clen, T, list, tid);
+      if (tc0 == ct) {
+        const __bf16* ql = (const __bf16*)a.q_lat + ((int64_t)cb * kHeads + head) * kLatent + 8 * hi;
+        const __bf16* qp = (const __bf16*)a.q_rope + ((int64_t)cb * kHeads + head) * kRope + 8 * hi;
+#pragma unroll
+        for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8*)(ql + 16 * kb);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qr[kb] = *(const bf16x8*)(qp + 16 * kb);
+#pragma unroll
+        for (int kb = 0; kb < 32; ++kb) asm volatile("" ::"v"(q[kb]));
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) asm volatile("" ::"v"(qr[kb]));
       }
-      if (issued < n) {
-        ld.issue((int)(issued % NS), ib, it, smem);
-        advance(ib, it);
-        ++issued;
-      }
-      const uint32_t mask = *(const LDS uint32_t*)(L + C::MASK_OFF + st * 4);
+      wait_vmcnt<0>();
+      __syncthreads();
+      const int32_t pro = clen < NS - 1 ? clen : NS - 1;
+      for (int32_t k = 0; k < pro; ++k) ld.issue(k, tc0 + k, tc0, T, list, smem);
 
-      LDS char* Ct;   // BF16 latent tile (swizzled)
-      LDS char* Rt = L + st * C::STAGE + C::C_STAGE;
-      if (FP8) {
-        // E4M3 -> BF16 into the conversion buffer; masked rows become zeros.
-        Ct = L + C::CONV_OFF;
-        const int r = tid >> 3, qq = tid & 7;
-        const LDS char* src = L + st * C::STAGE + r * kC8Row + 64 * qq;
-        LDS char* dst = Ct + r * kCRow;
-        const bool rv = (mask >> r) & 1;
-        const int rs = swz(r & 7);
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          i32x4 raw = *(const LDS i32x4*)(src + 16 * v4);
-#pragma unroll
-          for (int hc = 0; hc < 2; ++hc) {
-            i32x4 outv;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int word = raw[2 * hc + e];
-              // exact: every E4M3 value is a BF16 value
-              const uint32_t u0 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 0)) >> 16;
-              const uint32_t u1 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 1)) >> 16;
-              const uint32_t u2 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 2)) >> 16;
-              const uint32_t u3 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 3)) >> 16;
-              outv[2 * e] = (int)(u0 | (u1 << 16));
-              outv[2 * e + 1] = (int)(u2 | (u3 << 16));
-            }
-            if (!rv) outv = i32x4{0, 0, 0, 0};
-            const int chunk = 8 * qq + 2 * v4 + hc;
-            *(LDS i32x4*)(dst + 16 * (chunk ^ rs)) = outv;
-          }
-        }
+      for (int32_t j = 0; j < clen; ++j) {
+        const int st = j % NS;
+        wait_tiles<NS, C::DMA_PER_WAVE>(clen - 1 - j);
         __syncthreads();
-      } else {
-        Ct = L + st * C::STAGE;
-        if (mask != 0xFFFFFFFFu) {
-          // masked rows may hold anything; zero them so 0-probability x row stays 0
+        if (j + NS - 1 < clen) ld.issue((j + NS - 1) % NS, tc0 + j + NS - 1, tc0, T, list, smem);
+        const uint32_t mask = *(const LDS uint32_t*)(L + C::MASK_OFF + st * 4);
+
+        LDS char* Ct;   // BF16 latent tile (swizzled)
+        LDS char* Rt = L + st * C::STAGE + C::C_STAGE;
+        if (FP8) {
+          // E4M3 -> BF16 into the conversion buffer; masked rows become zeros.
+          Ct = L + C::CONV_OFF;
           const int r = tid >> 3, qq = tid & 7;
-          if (!((mask >> r) & 1)) {
-            LDS char* dst = Ct + r * kCRow + 128 * qq;
+          const LDS char* src = L + st * C::STAGE + r * kC8Row + 64 * qq;
+          LDS char* dst = Ct + r * kCRow;
+          const bool rv = (mask >> r) & 1;
+          const int rs = swz(r);
 #pragma unroll
-            for (int v = 0; v < 8; ++v) *(LDS i32x4*)(dst + 16 * v) = i32x4{0, 0, 0, 0};
+          for (int v4 = 0; v4 < 4; ++v4) {
+            i32x4 raw = *(const LDS i32x4*)(src + 16 * v4);
+#pragma unroll
+            for (int hc = 0; hc < 2; ++hc) {
+              i32x4 outv;
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const int word = raw[2 * hc + e];
+                // exact: every E4M3 value is a BF16 value
+                const uint32_t u0 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 0)) >> 16;
+                const uint32_t u1 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 1)) >> 16;
+                const uint32_t u2 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 2)) >> 16;
+                const uint32_t u3 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 3)) >> 16;
+                outv[2 * e] = (int)(u0 | (u1 << 16));
+                outv[2 * e + 1] = (int)(u2 | (u3 << 16));
+              }
+              if (!rv) outv = i32x4{0, 0, 0, 0};
+              const int chunk = 8 * qq + 2 * v4 + hc;
+              *(LDS i32x4*)(dst + 16 * (chunk ^ rs)) = outv;
+            }
           }
           __syncthreads();
+        } else {
+          Ct = L + st * C::STAGE;
+          if (mask != 0xFFFFFFFFu) {
+            // masked rows may hold anything; zero them so 0-probability x row stays 0
+            const int r = tid >> 3, qq = tid & 7;
+            if (!((mask >> r) & 1)) {
+              LDS char* dst = Ct + r * kCRow + 128 * qq;
+#pragma unroll
+              for (int v = 0; v < 8; ++v) *(LDS i32x4*)(dst + 16 * v) = i32x4{0, 0, 0, 0};
+            }
+            __syncthreads();
+          }
         }
-      }
 
-      // ---- scores S^T[pos][head] ----
-      f32x16 sacc = f32x16{};
+        // ---- scores S^T[pos][head] ----
+        // 32 latent K-blocks then 4 rotary K-blocks, one accumulator chain.
+        // Operands are read SD blocks ahead into a register ring; scheduling
+        // fences keep the order "MFMA k, then the read for k + SD" so the LDS
+        // latency hides behind the MFMAs.
+        float tsc[16];
+        f32x16 sacc = f32x16{};
+        {
+          constexpr int SD = 4;
+          auto s_operand = [&](int k) -> bf16x8 {
+            if (k < 32) return *(const LDS bf16x8*)(Ct + s_off[k & 7] + 256 * (k >> 3));
+            return *(const LDS bf16x8*)(Rt + r_off[k - 32]);
+          };
+          bf16x8 ring[SD];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+          for (int k = 0; k < SD; ++k) ring[k] = s_operand(k);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          bf16x8 av = *(const LDS bf16x8*)(Ct + s_off[v] + 128 * u);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, q[4 * u + v], sacc, 0, 0, 0);
+          for (int k = 0; k < 36; ++k) {
+            if (FP8 && k == 32) {
+              // the per-position scale multiplies the content score only
+              const LDS float* sc = (const LDS float*)(L + st * C::STAGE + C::C_STAGE + C::R_STAGE);
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                f32x4 v = *(const LDS f32x4*)(sc + 8 * g + 4 * hi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tsc[4 * g + e] = v[e];
+              }
+#pragma unroll
+              for (int r = 0; r < 16; ++r) sacc[r] *= tsc[r];
+            }
+            const bf16x8 bq = k < 32 ? q[k] : qr[k - 32];
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[k % SD], bq, sacc, 0, 0, 0);
+            if (k + SD < 36) ring[k % SD] = s_operand(k + SD);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-      }
-      float tsc[16];
-      if (FP8) {
-        const LDS float* sc = (const LDS float*)(L + st * C::STAGE + C::C_STAGE + C::R_STAGE);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v = *(const LDS f32x4*)(sc + 8 * g + 4 * hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) tsc[4 * g + e] = v[e];
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] *= tsc[r];
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        bf16x8 av = *(const LDS bf16x8*)(Rt + r_off[v]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qr[v], sacc, 0, 0, 0);
-      }
 
-      // ---- online softmax; lane owns head `head`, 16 of the 32 positions ----
-      // position of accumulator r: 8*(r/4) + 4*hi + r%4
-      const uint32_t mlane = mask >> (4 * hi);
-      float s[16];
-      float mloc = -INFINITY;
+        // ---- online softmax; lane owns head `head`, 16 of the 32 positions ----
+        // Position of accumulator r: 8*(r/4) + 4*hi + r%4.  Work in log2
+        // units: exp2(score * scale * log2(e) - m).  The row maximum is taken
+        // on raw scores and scaled once (the scale is positive).
+        float s[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool valid = (mlane >> (8 * (r >> 2) + (r & 3))) & 1u;
-        s[r] = valid ? sacc[r] * scale_log2 : -INFINITY;
-        mloc = fmaxf(mloc, s[r]);
-      }
-      mloc = fmaxf(mloc, wave_partner(mloc));
-      const float m_new = fmaxf(m_run, mloc);
-      // Rescale lazily: keep the old reference maximum unless the new one
-      // exceeds it by more than 8 (log2 units), so probabilities stay <= 256.
-      const bool need = m_new > m_run + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        m_run = need ? m_new : m_run;
-        l_run *= alpha;
+        for (int r = 0; r < 16; ++r) s[r] = sacc[r];
+        if (mask != 0xFFFFFFFFu) {  // ragged or gathered tile: masked positions
+          const uint32_t mlane = mask >> (4 * hi);
 #pragma unroll
-        for (int mb = 0; mb < 16; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
-      }
-      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-      float lsum = 0.f;
-      bf16x8 P[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[r] - mref);
-        lsum += p;
-        const float pw = FP8 ? p * tsc[r] : p;
-        P[r >> 3][r & 7] = (__bf16)pw;
-      }
-      l_run += lsum;
-
-      // ---- weighted latent U^T[latent][head] += C^T P^T ----
-      typedef __attribute__((ext_vector_type(8))) short s16x8;
-      auto pv = [&](int mb, f32x16 acc) {
-        const int e = mb & 1, pp = mb >> 1;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const LDS char* p1 = Ct + tr_off[e] + 128 * pp + 16 * kCRow * kb2;
-          s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p1);
-          s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(p1 + 8 * kCRow));
-          s16x8 av8 = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av8), P[kb2], acc, 0, 0, 0);
+          for (int r = 0; r < 16; ++r)
+            s[r] = ((mlane >> (8 * (r >> 2) + (r & 3))) & 1u) ? s[r] : -INFINITY;
         }
-        return acc;
-      };
+        float mloc = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+        mloc = fmaxf(mloc, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
+                                 fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+        mloc = fmaxf(mloc, wave_partner(mloc)) * scale_log2;
+        const float m_new = fmaxf(m_run, mloc);
+        // Rescale lazily: keep the old reference maximum unless the new one
+        // exceeds it by more than 8 (log2 units), so probabilities stay <= 256.
+        const bool need = m_new > m_run + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+          m_run = need ? m_new : m_run;
+          l_run *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < 16; ++mb) O[mb] = pv(mb, O[mb]);
+          for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
+        }
+        const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+        float lsum = 0.f;
+        bf16x8 P[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, neg_m));
+          lsum += p;
+          const float pw = FP8 ? p * tsc[r] : p;
+          P[r >> 3][r & 7] = (__bf16)pw;
+        }
+        l_run += lsum;
+
+        // ---- weighted latent U^T[latent][head] += C^T P^T ----
+        // 16 column blocks x 2 position halves; each operand is two transposing
+        // LDS reads, prefetched PD operands ahead.
+        {
+          constexpr int PD = 3;
+          auto pv_operand = [&](int j) -> bf16x8 {
+            const int mb = j >> 1, kb2 = j & 1;
+            const LDS char* p1 = Ct + tr_off[0][mb & 3] + 256 * (mb >> 2) + 16 * kCRow * kb2;
+            const LDS char* p2 = Ct + tr_off[1][mb & 3] + 256 * (mb >> 2) + 16 * kCRow * kb2;
+            s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p1);
+            s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p2);
+            typedef __attribute__((ext_vector_type(8))) short s16x8;
+            return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
+          bf16x8 ring[PD];
+#pragma unroll
+          for (int j = 0; j < PD; ++j) ring[j] = pv_operand(j);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < 32; ++j) {
+            O[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[j % PD], P[j & 1], O[j >> 1], 0, 0, 0);
+            if (j + PD < 32) ring[j % PD] = pv_operand(j + PD);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
     }
+    i += seg_len;
 
     // ---- end of the segment: normalise and write ----
     {

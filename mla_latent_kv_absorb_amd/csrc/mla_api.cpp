@@ -22,7 +22,7 @@ mla_status check_config(const mla_config* c, Path* path) {
   if (c->num_heads < 1 || c->d_latent < 1 || c->d_rope < 0 || c->d_nope < 1 || c->d_v < 1)
     return MLA_ERR_INVALID_ARG;
   if (c->block_size != MLA_PAGE_TOKENS) return MLA_ERR_INVALID_ARG;
-  if (!isfinite(c->softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!isfinite(c->softmax_scale) || !(c->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   if (c->cache_dtype == MLA_F32 && c->act_dtype == MLA_F32) {
     if ((size_t)c->num_heads * c->d_latent > 8192 || c->d_latent > 512 || c->d_rope > 512)
       return MLA_ERR_UNSUPPORTED;
@@ -168,7 +168,7 @@ mla_status mla_decode_attn(const mla_config* cfg, const void* q_lat, const void*
   if (!aligned(q_lat, 16) || !aligned(q_rope, 16) || !aligned(kv_pool, 16) || !aligned(block_table, 4) ||
       !aligned(seq_lens, 4) || (topk_idx && !aligned(topk_idx, 4)))
     return MLA_ERR_INVALID_ARG;
-  if (path == Path::kF32 && num_pages >= (int64_t)1 << 24) return MLA_ERR_UNSUPPORTED;
+  if (num_pages >= (int64_t)1 << 24) return MLA_ERR_UNSUPPORTED;  // row codes page * 64 + slot fit int32
   size_t page, rope_off, scale_off;
   layout(cfg, &page, &rope_off, &scale_off);
   mla::DecodeArgs a{};
