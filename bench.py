@@ -11,8 +11,8 @@ Prints one JSON line.  `value` is the latent-KV read rate of the whole step:
 cache bytes read per step (each visible position's 1,152-byte item once) over
 the step time.  Also reported: decode tokens/s, the attention kernel's own
 rate against the HBM roofline (HIP events around every attention launch in
-the timed region), and the float64 CPU oracle timed on one request of the
-same workload on the host cores.
+the timed region), and the float64 CPU oracle timed on whole requests of
+the same workload on the host cores (about 15 s of work).
 """
 
 from __future__ import annotations
@@ -164,7 +164,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on one request")
+        log("timing the CPU oracle on whole requests (about 15 s)")
         cpu = cpu_baseline(inp)
 
     result = {
