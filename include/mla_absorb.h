@@ -85,7 +85,7 @@ typedef struct {
 
 /* Split plan for mla_decode_attn / mla_combine. */
 typedef struct {
-  int32_t num_workers;    /* work-groups that share the position tiles of all requests */
+  int32_t num_workers;    /* work-groups that share the position tiles of all requests, 1..65536 */
   int32_t num_slots;      /* partial results the workers can emit: num_workers + batch - 1 */
   size_t workspace_bytes; /* bytes mla_decode_attn needs for partials */
 } mla_plan;

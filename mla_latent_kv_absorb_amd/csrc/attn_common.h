@@ -1,0 +1,113 @@
+// Device helpers shared by the attention kernels (gfx950).  Included by
+// kernel translation units only.
+#pragma once
+
+#include "mla_internal.h"
+#include "tile_space.h"
+
+namespace mla {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) short s16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+#define LDS __attribute__((address_space(3)))
+
+constexpr int kThreads = 256;
+constexpr int kCRow = kLatent * 2;  // bytes of one BF16 latent row (1024)
+constexpr int kRRow = kRope * 2;    // bytes of one BF16 rotary row (128)
+constexpr int kC8Row = kLatent;     // bytes of one FP8 latent row (512)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// LDS row swizzles (16-byte chunks).  Chunk c of latent row r is stored at
+// chunk c ^ swz(r), of rotary row r at c ^ swz_r(r).  Chosen so that the three
+// operand read patterns -- 16-byte row reads for the scores (16 consecutive
+// rows per access phase), 8-byte transposing reads (4 rows x 64 bytes) and
+// the rotary row reads -- touch distinct banks on a 64-bank LDS and on a
+// 32-bank one.
+__device__ __forceinline__ constexpr int swz(int r) {
+  r &= 15;
+  return (((r & 3) << 2) | ((r >> 2) & 3)) ^ (r & 2);
+}
+__device__ __forceinline__ constexpr int swz_r(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// HBM -> LDS without registers: lane l's bytes land at lds_addr + size * l.
+// lds_addr must be wave-uniform (it goes to M0).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ float wave_partner(float v) {
+  // value held by lane (l ^ 32)
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
+}
+
+// x * alpha for an accumulator value, kept in its accumulator register.  The
+// online-softmax rescale runs only when a head's running maximum grows by a
+// large step; writing it this way keeps the register allocator from moving
+// the whole accumulator file through ordinary registers around that branch.
+// The trailing s_nop covers the accumulator-write -> MFMA-read distance.
+__device__ __forceinline__ float scale_acc(float x, float alpha) {
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %1, %0\n\t"
+      "v_mul_f32 %1, %1, %2\n\t"
+      "v_accvgpr_write_b32 %0, %1\n\t"
+      "s_nop 2"
+      : "+a"(x), "=&v"(t)
+      : "v"(alpha));
+  return x;
+}
+
+// Uniform metadata reads go through the constant address space so they become
+// scalar loads (lgkmcnt), never vector loads that would queue behind the
+// in-flight LDS-bound loads on vmcnt.
+__device__ __forceinline__ int32_t sload(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
+}
+
+// Per-lane LDS offsets of the MFMA operands inside one tile (relative to the
+// tile's latent or rotary section).  The swizzles only touch the low 4 bits
+// of a chunk index, so every operand address is one of a few per-lane bases
+// plus a compile-time offset.
+struct OperandOffsets {
+  int s_off[8];      // latent operand of score K-block k: s_off[k & 7] + 256 * (k >> 3)
+  int r_off[4];      // rotary operand of score K-block v
+  int tr_off[2][4];  // transposed latent operand of column block mb, position half h8:
+                     // tr_off[h8][mb & 3] + 256 * (mb >> 2) + 16 KiB * kb2
+
+  __device__ __forceinline__ explicit OperandOffsets(int lane) {
+    const int row = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) s_off[v] = row * kCRow + 16 * ((2 * v + hi) ^ swz(row));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) r_off[v] = row * kRRow + 16 * ((2 * v + hi) ^ swz_r(row));
+    const int j16 = lane & 15, g16 = lane >> 4, hh = g16 >> 1, ch = g16 & 1;
+    const int tr_row = 4 * hh + (j16 >> 2);  // 0..7
+    const int lo = 2 * ch + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        tr_off[h8][e] = (tr_row + 8 * h8) * kCRow + 16 * ((4 * e + lo) ^ swz(tr_row + 8 * h8)) + (j16 & 1) * 8;
+  }
+};
+
+}  // namespace
+}  // namespace mla

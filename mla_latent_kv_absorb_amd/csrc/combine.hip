@@ -6,33 +6,45 @@
 //   o = sum_s exp(lse_s - LSE) o_s,   LSE = log sum_s exp(lse_s),
 // an exact identity.  Which slots hold request b's partials follows from the
 // same tile partition the attention kernel used (worker p writes slot p + b).
-#include "mla_internal.h"
+//
+// One wave per (request, head): each lane owns 8 consecutive latent columns
+// (two 16-byte loads per partial), so a head row of 512 floats is one
+// coalesced 2 KiB read per partial, and the loads of 8 partials are in flight
+// together.  The merge weights are computed one partial per lane and read
+// back with readlane.
+#include "tile_space.h"
 
 namespace mla {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kHeadsPerBlock = 8;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 8;  // partials whose loads are in flight together
 
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int32_t b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int h = blockIdx.x * kHeadsPerBlock + tid / 32;
-  const int sub = tid & 31;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * kWaves + (threadIdx.x >> 6);
 
   // tile range of request b in the concatenated tile space
-  int64_t W = 0, start = 0;
-  int32_t nt_b = 0;
-  for (int32_t r = 0; r < a.batch; ++r) {
-    int32_t nt;
-    if (a.topk > 0) nt = tiles_of(a.topk);
-    else {
-      const int32_t T = a.seq_lens[r];
-      nt = T > 0 ? tiles_of(T) : 0;
-    }
-    if (r == b) { start = W; nt_b = nt; }
-    W += nt;
-  }
+  const int64_t W = tiles_below(a.seq_lens, a.batch, a.topk);
+  const int64_t start = tiles_below(a.seq_lens, b, a.topk);
+  const int32_t nt_b = a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[b]);
   if (h >= a.H) return;
   const int64_t P = a.num_workers;
   int64_t p_first = 0, p_last = -1;
@@ -40,52 +52,113 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     p_first = worker_of(start, W, P);
     p_last = worker_of(start + nt_b - 1, W, P);
   }
-  // weights
+  const int32_t np = (int32_t)(p_last - p_first + 1);  // candidate partials (some workers may be empty)
+  const float* lse_col = a.part_lse + (int64_t)b * a.H + h;  // slot s: lse_col[s * H]
+
+  // Merge weights.  Lane i looks after partial p_first + 64c + i of chunk c;
+  // an empty worker wrote nothing and counts as lse = -inf.
+  // Workers are empty only when there are fewer tiles than workers; then
+  // p * W < P * P and the test needs no 64-bit division.
+  const bool some_empty = W < P;
+  auto lane_lse = [&](int32_t c) -> float {
+    const int64_t p = p_first + 64 * c + lane;
+    if (p > p_last) return -INFINITY;
+    if (some_empty) {
+      const uint32_t pw = (uint32_t)p * (uint32_t)W, p32 = (uint32_t)P;
+      if (pw / p32 == (pw + (uint32_t)W) / p32) return -INFINITY;
+    }
+    return lse_col[p * a.H];
+  };
+  const int32_t nchunks = (np + 63) / 64;
   float mx = -INFINITY;
-  for (int64_t p = p_first; p <= p_last; ++p) {
-    if (worker_lo(p, W, P) == worker_lo(p + 1, W, P)) continue;  // empty worker
-    mx = fmaxf(mx, a.part_lse[(p + b) * a.H + h]);
-  }
+  for (int32_t c = 0; c < nchunks; ++c) mx = fmaxf(mx, lane_lse(c));
+  mx = wave_max(mx);
   const float mref = (mx == -INFINITY) ? 0.f : mx;
   float tot = 0.f;
-  for (int64_t p = p_first; p <= p_last; ++p) {
-    if (worker_lo(p, W, P) == worker_lo(p + 1, W, P)) continue;
-    tot += expf(a.part_lse[(p + b) * a.H + h] - mref);
+  for (int32_t c = 0; c < nchunks; ++c) {
+    const float l = lane_lse(c);
+    tot += (l == -INFINITY) ? 0.f : expf(l - mref);
   }
+  tot = wave_sum(tot);
   const float inv = tot > 0.f ? 1.0f / tot : 0.f;
-  for (int d0 = sub * 4; d0 < a.D_C; d0 += 128) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t p = p_first; p <= p_last; ++p) {
-      if (worker_lo(p, W, P) == worker_lo(p + 1, W, P)) continue;
-      const int64_t slot = p + b;
-      const float wgt = expf(a.part_lse[slot * a.H + h] - mref) * inv;
-      const float* src = a.part_o + (slot * a.H + h) * a.D_C + d0;
+  const int64_t dst = ((int64_t)b * a.H + h) * a.D_C;
+  const int64_t row_stride = (int64_t)a.H * a.D_C;  // floats between slots
+  const float* row0 = a.part_o + ((int64_t)b * a.H + h) * a.D_C;  // worker p's row (slot p + b): row0 + p * row_stride
+
+  // Every lane runs every iteration (the weights are read from other lanes
+  // with readlane, so no lane may sit out); lanes past the row end load a
+  // valid column and skip the store.
+  for (int dbase = 0; dbase < a.D_C; dbase += VEC ? 512 : 64) {
+    const int dl = dbase + (VEC ? lane * 8 : lane);
+    const bool act = dl < a.D_C;
+    const int d0 = act ? dl : 0;
+    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    float acc = 0.f;
+    for (int32_t c = 0; c < nchunks; ++c) {
+      const float l = lane_lse(c);
+      const float wl = (l == -INFINITY) ? 0.f : expf(l - mref) * inv;  // lane's weight
+      const int32_t n = np - 64 * c < 64 ? np - 64 * c : 64;
+      for (int32_t j = 0; j < n; j += kUnroll) {
+        // issue every load of the group first; slots past the end are
+        // clamped to a valid slot and get weight 0 (selected away, so
+        // whatever an empty worker's slot holds never reaches the sum)
+        f32x4 v0[kUnroll], v1[kUnroll];
+        float vs[kUnroll], wg[kUnroll];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (d0 + e < a.D_C) acc[e] = fmaf(wgt, src[e], acc[e]);
+        for (int u = 0; u < kUnroll; ++u) {
+          const int32_t jj = j + u < n ? j + u : n - 1;
+          wg[u] = j + u < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), jj)) : 0.f;
+          const int64_t p = p_first + 64 * c + jj;  // its slot is p + b
+          const float* src = row0 + p * row_stride + d0;
+          if (VEC) {
+            v0[u] = ((const f32x4*)src)[0];
+            v1[u] = ((const f32x4*)src)[1];
+          } else {
+            vs[u] = src[0];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const float w = wg[u];
+          if (VEC) {
+            acc0 += w == 0.f ? f32x4{0.f, 0.f, 0.f, 0.f} : w * v0[u];
+            acc1 += w == 0.f ? f32x4{0.f, 0.f, 0.f, 0.f} : w * v1[u];
+          } else {
+            acc += w == 0.f ? 0.f : w * vs[u];
+          }
+        }
+      }
     }
-    const int64_t dst = ((int64_t)b * a.H + h) * a.D_C + d0;
-    if (a.out_bf16) {
-      __bf16* o = (__bf16*)a.o_lat + dst;
+    if (!act) continue;
+    if (VEC) {
+      if (a.out_bf16) {
+        bf16x8 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (d0 + e < a.D_C) o[e] = (__bf16)acc[e];
+        for (int e = 0; e < 4; ++e) {
+          o[e] = (__bf16)acc0[e];
+          o[4 + e] = (__bf16)acc1[e];
+        }
+        *(bf16x8*)((__bf16*)a.o_lat + dst + d0) = o;
+      } else {
+        f32x4* o = (f32x4*)((float*)a.o_lat + dst + d0);
+        o[0] = acc0;
+        o[1] = acc1;
+      }
     } else {
-      float* o = (float*)a.o_lat + dst;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (d0 + e < a.D_C) o[e] = acc[e];
+      if (a.out_bf16) ((__bf16*)a.o_lat)[dst + d0] = (__bf16)acc;
+      else ((float*)a.o_lat)[dst + d0] = acc;
     }
   }
-  if (a.lse_out != nullptr && sub == 0)
+  if (a.lse_out != nullptr && lane == 0)
     a.lse_out[(int64_t)b * a.H + h] = tot > 0.f ? mref + logf(tot) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  const dim3 grid((a.H + kHeadsPerBlock - 1) / kHeadsPerBlock, a.batch);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, a);
+  const dim3 grid((a.H + kWaves - 1) / kWaves, a.batch);
+  if (a.D_C % 8 == 0) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

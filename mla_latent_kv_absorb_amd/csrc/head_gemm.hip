@@ -4,11 +4,11 @@
 // out-up:  x = o_lat,  w = W_UV ([H][D_V][D_C]), y = out    (M = D_V, K = D_C)
 // ("DeepSeek's KV Cache", Figure 5 form (2) and Figure 6 form (2)).
 //
-// BF16: one wave per (32 rows of w, head, 32 batch columns) computes
-// Y^T[m][b] on MFMA 32x32x16 with both operands loaded straight from HBM in
-// operand layout (the contraction dimension is contiguous in w and x, so
-// every lane loads 16 contiguous bytes).  At decode batch sizes the work is
-// bounded by reading the weights once.
+// BF16: each wave computes Y^T[m][b] for 32 rows of w and 64 batch columns on
+// MFMA 32x32x16 with both operands loaded straight from HBM in operand layout
+// (the contraction dimension is contiguous in w and x, so every lane loads 16
+// contiguous bytes).  At decode batch sizes the work is bounded by reading
+// the weights once.
 // F32: one thread per output element, fp32 FMA.
 #include "mla_internal.h"
 
@@ -19,42 +19,91 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
-__global__ __launch_bounds__(64) void head_gemm_bf16_kernel(HeadGemmArgs a) {
-  const int lane = threadIdx.x;
-  const int m0 = blockIdx.x * 32;
+// Work-group: 4 waves, 64 batch columns (two 32-column accumulators per
+// wave, so each weight row is read from HBM once per 64 requests).
+//   KS = 1: the 4 waves take 4 consecutive 32-row blocks of w, full K.
+//   KS = 4: the 4 waves take one 32-row block and a quarter of K each; the
+//           partial sums meet in LDS.  Used for long K (the up-projection,
+//           K = D_C) so the grid still has enough waves to cover the weights.
+template <int KS>
+__global__ __launch_bounds__(256) void head_gemm_bf16_kernel(HeadGemmArgs a) {
+  constexpr int kMBlocks = 4 / KS;
+  __shared__ float red[KS > 1 ? (KS - 1) * 32 * 64 : 1];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int m0 = (blockIdx.x * kMBlocks + (KS > 1 ? 0 : wv)) * 32;
+  const int kpart = KS > 1 ? wv : 0;
   const int h = blockIdx.y;
-  const int n0 = blockIdx.z * 32;
+  const int n0 = blockIdx.z * 64;
   const int kg = lane >> 5;
-  const int col = n0 + (lane & 31);
-  const bool colv = col < a.batch;
-  const __bf16* wp = (const __bf16*)a.w + ((int64_t)h * a.M + m0 + (lane & 31)) * a.K + 8 * kg;
-  const __bf16* xp = (const __bf16*)a.x + ((int64_t)(colv ? col : 0) * a.H + h) * a.K + 8 * kg;
-  f32x16 acc = f32x16{};
-  const int nk = a.K / 16;
+  const int klen = a.K / KS;
+  const int kbeg = kpart * klen;
+  const int colA = n0 + (lane & 31), colB = colA + 32;
+  const bool vA = colA < a.batch, vB = colB < a.batch;
+  if (KS == 1 && m0 >= a.M) return;
+  const __bf16* wp = (const __bf16*)a.w + ((int64_t)h * a.M + m0 + (lane & 31)) * a.K + kbeg + 8 * kg;
+  const __bf16* xa = (const __bf16*)a.x + ((int64_t)(vA ? colA : 0) * a.H + h) * a.K + kbeg + 8 * kg;
+  const __bf16* xb = (const __bf16*)a.x + ((int64_t)(vB ? colB : 0) * a.H + h) * a.K + kbeg + 8 * kg;
+  f32x16 accA = f32x16{}, accB = f32x16{};
+  const int nk = klen / 16;
   int kk = 0;
-  for (; kk + 4 <= nk; kk += 4) {
-    bf16x8 av[4], bv[4];
+  constexpr int U = 8;
+  for (; kk + U <= nk; kk += U) {
+    bf16x8 av[U], ba[U], bb[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       av[u] = *(const bf16x8*)(wp + 16 * (kk + u));
-      bv[u] = colv ? *(const bf16x8*)(xp + 16 * (kk + u)) : bf16x8{};
+      ba[u] = vA ? *(const bf16x8*)(xa + 16 * (kk + u)) : bf16x8{};
+      bb[u] = vB ? *(const bf16x8*)(xb + 16 * (kk + u)) : bf16x8{};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u], bv[u], acc, 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      accA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u], ba[u], accA, 0, 0, 0);
+      accB = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u], bb[u], accB, 0, 0, 0);
+    }
   }
   for (; kk < nk; ++kk) {
-    bf16x8 av = *(const bf16x8*)(wp + 16 * kk);
-    bf16x8 bv = colv ? *(const bf16x8*)(xp + 16 * kk) : bf16x8{};
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    const bf16x8 av = *(const bf16x8*)(wp + 16 * kk);
+    const bf16x8 ba = vA ? *(const bf16x8*)(xa + 16 * kk) : bf16x8{};
+    const bf16x8 bb = vB ? *(const bf16x8*)(xb + 16 * kk) : bf16x8{};
+    accA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ba, accA, 0, 0, 0);
+    accB = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bb, accB, 0, 0, 0);
   }
-  if (!colv) return;
-  __bf16* yp = (__bf16*)a.y + ((int64_t)col * a.H + h) * a.M + m0 + 4 * kg;
+  if (KS > 1) {
+    if (wv > 0) {
+      float* r = red + (wv - 1) * 32 * 64 + lane;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    bf16x4 v;
+      for (int i = 0; i < 16; ++i) {
+        r[i * 64] = accA[i];
+        r[(16 + i) * 64] = accB[i];
+      }
+    }
+    __syncthreads();
+    if (wv > 0) return;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * g + e];
-    *(bf16x4*)(yp + 8 * g) = v;
+    for (int w = 0; w < KS - 1; ++w) {
+      const float* r = red + w * 32 * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        accA[i] += r[i * 64];
+        accB[i] += r[(16 + i) * 64];
+      }
+    }
+  }
+  // lane holds rows m0 + 8g + 4 kg + e (e = 0..3) of its column
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int col = half ? colB : colA;
+    if (col >= a.batch) continue;
+    const f32x16& acc = half ? accB : accA;
+    __bf16* yp = (__bf16*)a.y + ((int64_t)col * a.H + h) * a.M + m0 + 4 * kg;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * g + e];
+      *(bf16x4*)(yp + 8 * g) = v;
+    }
   }
 }
 
@@ -75,8 +124,14 @@ __global__ __launch_bounds__(256) void head_gemm_f32_kernel(HeadGemmArgs a) {
 }  // namespace
 
 hipError_t launch_head_gemm_bf16(const HeadGemmArgs& a, hipStream_t s) {
-  const dim3 grid(a.M / 32, a.H, (a.batch + 31) / 32);
-  hipLaunchKernelGGL(head_gemm_bf16_kernel, grid, dim3(64), 0, s, a);
+  // requires M % 32 == 0 and K % 16 == 0 (checked by the caller)
+  if (a.K >= 256 && a.K % 64 == 0) {
+    const dim3 grid(a.M / 32, a.H, (a.batch + 63) / 64);
+    hipLaunchKernelGGL(head_gemm_bf16_kernel<4>, grid, dim3(256), 0, s, a);
+  } else {
+    const dim3 grid((a.M + 127) / 128, a.H, (a.batch + 63) / 64);
+    hipLaunchKernelGGL(head_gemm_bf16_kernel<1>, grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

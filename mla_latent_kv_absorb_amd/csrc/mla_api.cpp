@@ -44,6 +44,10 @@ mla_status check_config(const mla_config* c, Path* path) {
 
 size_t al16(size_t x) { return (x + 15) / 16 * 16; }
 
+// Upper bound on split workers (the combine kernel's empty-worker test works
+// in 32-bit products of worker index and tile count below this bound).
+constexpr int64_t kMaxWorkers = 65536;
+
 void layout(const mla_config* c, size_t* page, size_t* rope_off, size_t* scale_off) {
   size_t cb, rb, sb;
   if (c->cache_dtype == MLA_F32) {
@@ -116,6 +120,7 @@ mla_status mla_decode_plan(const mla_config* cfg, int32_t batch, const int32_t* 
   const int64_t kMinTilesPerWorker = 16;
   int64_t P = (W + kMinTilesPerWorker - 1) / kMinTilesPerWorker;
   if (P > num_cus) P = num_cus;
+  if (P > kMaxWorkers) P = kMaxWorkers;
   if (P < 1) P = 1;
   plan->num_workers = (int32_t)P;
   plan->num_slots = (int32_t)(P + batch - 1);
@@ -195,7 +200,8 @@ mla_status mla_decode_attn(const mla_config* cfg, const void* q_lat, const void*
     a.o_lat = o_lat;
     a.lse_out = lse_out;
   } else {
-    if (plan == nullptr || plan->num_workers < 1 || workspace == nullptr || !aligned(workspace, 16))
+    if (plan == nullptr || plan->num_workers < 1 || plan->num_workers > kMaxWorkers || workspace == nullptr ||
+        !aligned(workspace, 16))
       return MLA_ERR_INVALID_ARG;
     const int64_t slots = (int64_t)plan->num_workers + batch - 1;
     if (workspace_bytes < workspace_bytes_for(cfg, slots)) return MLA_ERR_INVALID_ARG;
@@ -205,6 +211,7 @@ mla_status mla_decode_attn(const mla_config* cfg, const void* q_lat, const void*
   }
   hipStream_t s = (hipStream_t)stream;
   if (path == Path::kF32) return launch_status(mla::launch_decode_f32(a, s));
+  if (path == Path::kMfmaBf16 && topk_idx == nullptr) return launch_status(mla::launch_decode_bf16(a, s));
   return launch_status(mla::launch_decode_mfma(a, path == Path::kMfmaFp8, s));
 }
 
@@ -215,7 +222,8 @@ mla_status mla_combine(const mla_config* cfg, const void* workspace, size_t work
   mla_status st = check_config(cfg, &path);
   if (st != MLA_OK) return st;
   if (workspace == nullptr || seq_lens == nullptr || plan == nullptr || o_lat == nullptr) return MLA_ERR_INVALID_ARG;
-  if (batch < 1 || batch > 65535 || topk < 0 || plan->num_workers < 1) return MLA_ERR_INVALID_ARG;
+  if (batch < 1 || batch > 65535 || topk < 0 || plan->num_workers < 1 || plan->num_workers > kMaxWorkers)
+    return MLA_ERR_INVALID_ARG;
   if (!aligned(workspace, 16) || !aligned(o_lat, 16) || (lse_out && !aligned(lse_out, 4))) return MLA_ERR_INVALID_ARG;
   const int64_t slots = (int64_t)plan->num_workers + batch - 1;
   if (workspace_bytes < workspace_bytes_for(cfg, slots)) return MLA_ERR_INVALID_ARG;

@@ -60,6 +60,7 @@ struct HeadGemmArgs {
 };
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);  // BF16 cache, dense
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_head_gemm_bf16(const HeadGemmArgs& a, hipStream_t s);

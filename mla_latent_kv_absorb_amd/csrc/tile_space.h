@@ -1,0 +1,76 @@
+// Device helpers over the concatenated tile space of all requests (the
+// split partition of mla_internal.h).  Included by kernel translation units
+// only.
+#pragma once
+
+#include "mla_internal.h"
+
+namespace mla {
+
+// ---- the concatenated tile space of all requests (see worker_lo) ----
+// Computed by the whole wave, 64 requests per load, so the per-request
+// lengths are read in parallel rather than one dependent scalar load after
+// another.  Every lane must be active; results are wave-uniform.
+__device__ inline int32_t tiles_dense(int32_t T) { return T > 0 ? tiles_of(T) : 0; }
+
+// Wave-uniform copy of a value every lane holds (keeps it in scalar registers).
+__device__ inline int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ inline int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return uniform_i64(v);
+}
+
+// Total tiles of requests [0, upto).
+__device__ inline int64_t tiles_below(const int32_t* seq_lens, int32_t upto, int32_t topk) {
+  if (topk > 0) return (int64_t)upto * tiles_of(topk);
+  const int lane = __lane_id();
+  int64_t sum = 0;
+  for (int32_t base = 0; base < upto; base += 64) {
+    const int32_t r = base + lane;
+    sum += r < upto ? tiles_dense(seq_lens[r]) : 0;
+  }
+  return wave_sum_i64(sum);
+}
+
+// Request holding global tile g (0 <= g < total) and the tile's index inside it.
+__device__ inline void locate_tile(const int32_t* seq_lens, int32_t batch, int32_t topk, int64_t g,
+                                            int32_t* b, int32_t* t) {
+  if (topk > 0) {
+    const int32_t nt = tiles_of(topk);
+    *b = (int32_t)(g / nt);
+    *t = (int32_t)(g % nt);
+    return;
+  }
+  const int lane = __lane_id();
+  int64_t off = 0;
+  for (int32_t base = 0; base < batch; base += 64) {
+    const int32_t r = base + lane;
+    const int64_t nt = r < batch ? tiles_dense(seq_lens[r]) : 0;
+    int64_t incl = nt;  // inclusive scan over the lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t up = __shfl_up(incl, d);
+      if (lane >= d) incl += up;
+    }
+    incl += off;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > g);
+    if (hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      const int64_t end = __shfl(incl, l), len = __shfl(nt, l);
+      *b = base + l;
+      *t = __builtin_amdgcn_readfirstlane((int32_t)(g - (end - len)));
+      return;
+    }
+    off = uniform_i64(__shfl(incl, 63));
+  }
+  *b = batch;  // g beyond the last tile
+  *t = 0;
+}
+
+}  // namespace mla
