@@ -16,9 +16,12 @@
 //
 // The softmax of tile j needs only the scores of tile j, and the weighted
 // latent of tile j - 1 needs only the probabilities of tile j - 1, so the two
-// are independent and the VALU work runs in the shadow of the MFMAs.  The
-// ring holds 4 tiles: j - 1 (being consumed), j (being scored), j + 1 and
-// j + 2 (in flight).
+// are independent and the VALU work runs in the shadow of the MFMAs.  The 68
+// MFMAs of an iteration read their LDS operands through one register ring
+// that runs three MFMAs ahead across the switch from scores to weighted
+// latent, and the rotary query blocks are fetched the same distance ahead, so
+// no MFMA waits on a fresh LDS read.  The stage ring holds 4 tiles: j - 1
+// (being consumed), j (being scored), j + 1 and j + 2 (in flight).
 //
 // Loads: each wave moves 8 latent rows (1 KiB each) and 8 rotary rows of a
 // tile with global_load_lds_dwordx4 in its scalar-base form: one 64-bit page
@@ -29,6 +32,8 @@
 // loaded from a valid page (so every wave always issues the same number of
 // loads and the vmcnt accounting holds), then zeroed in LDS and masked out
 // of the softmax.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace mla {
@@ -156,57 +161,66 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
   f32x16 O[16];
   bf16x8 q[32];
 
-  // ---- score MFMAs of the tile in stage st ----
-  auto scores = [&](int st, auto&& after) -> f32x16 {
-    const LDS char* Ct = L + st * kStage;
-    const LDS char* Rt = Ct + kCStage;
-    constexpr int SD = 3;
-    auto s_operand = [&](int k) -> bf16x8 {
-      if (k < 32) return *(const LDS bf16x8*)(Ct + off.s_off[k & 7] + 256 * (k >> 3));
-      return *(const LDS bf16x8*)(Rt + off.r_off[k - 32]);
-    };
+  // ---- the MFMA stream of one iteration ----
+  // Operand i < 36: score K-block i of the tile in stage `sst` (latent blocks,
+  // then rotary blocks); operand i >= 36: transposed latent block i - 36 of
+  // the tile in stage `pst` for the weighted latent.  One ring of loads runs
+  // three MFMAs ahead across both halves, so the matrix cores never wait for
+  // the first operand of a phase.
+  auto s_operand = [&](const LDS char* Ct, int k) -> bf16x8 {
+    if (k < 32) return *(const LDS bf16x8*)(Ct + off.s_off[k & 7] + 256 * (k >> 3));
+    return *(const LDS bf16x8*)(Ct + kCStage + off.r_off[k - 32]);
+  };
+  // step j: column block mb = j % 16, position half kb2 = j / 16, so that
+  // consecutive MFMAs accumulate into different blocks
+  auto pv_operand = [&](const LDS char* Ct, int j) -> bf16x8 {
+    const int mb = j & 15, kb2 = j >> 4;
+    const LDS char* p1 = Ct + off.tr_off[0][mb & 3] + 256 * (mb >> 2) + 16 * kCRow * kb2;
+    const LDS char* p2 = Ct + off.tr_off[1][mb & 3] + 256 * (mb >> 2) + 16 * kCRow * kb2;
+    s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p1);
+    s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p2);
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // rotary query block v of this lane's head (rows swizzled as the rotary keys)
+  auto rq_operand = [&](int v) -> bf16x8 {
+    return *(const LDS bf16x8*)(L + kQrOff + head * kRRow + 16 * ((2 * v + hi) ^ swz_r(head)));
+  };
+  // HAS_S: scores of the tile in sst (36 MFMAs) before the weighted latent of
+  // the tile in pst (32 MFMAs); without it only the weighted latent.
+  // after_s(k) runs after score MFMA k, piece(k) after weighted MFMA k + 1;
+  // the scores land in s before the first piece.
+  auto stream = [&](auto has_s, int sst, int pst, const bf16x8& P0, const bf16x8& P1, f32x16& s, auto&& after_s,
+                    auto&& piece) __attribute__((always_inline)) {
+    constexpr bool HAS_S = decltype(has_s)::value;
+    constexpr int I0 = HAS_S ? 0 : 36;
+    constexpr int D = 3;
+    const LDS char* Cs = L + sst * kStage;
+    const LDS char* Cp = L + pst * kStage;
+    auto operand = [&](int i) -> bf16x8 { return i < 36 ? s_operand(Cs, i) : pv_operand(Cp, i - 36); };
+    bf16x8 ring[D];
+    bf16x8 rq[D];
     f32x16 sacc = f32x16{};
-    bf16x8 ring[SD];
 #pragma unroll
-    for (int k = 0; k < SD; ++k) ring[k] = s_operand(k);
+    for (int i = I0; i < I0 + D; ++i) ring[i % D] = operand(i);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < 36; ++k) {
-      // rotary query block (k - 32) of this lane's head, from LDS (row swizzled as the rotary keys)
-      const bf16x8 bq =
-          k < 32 ? q[k] : *(const LDS bf16x8*)(L + kQrOff + head * kRRow + 16 * ((2 * (k - 32) + hi) ^ swz_r(head)));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[k % SD], bq, sacc, 0, 0, 0);
-      if (k + SD < 36) ring[k % SD] = s_operand(k + SD);
-      after(k);
+    for (int i = I0; i < 36; ++i) {
+      const bf16x8 bq = i < 32 ? q[i & 31] : rq[(i + 3 * D - 32) % D];
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % D], bq, sacc, 0, 0, 0);
+      ring[i % D] = operand(i + D);
+      // rotary query blocks, D MFMAs ahead of their use
+      if (i >= 32 - D && i < 36 - D) rq[(i + D - 32) % D] = rq_operand(i + D - 32);
+      after_s(i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    return sacc;
-  };
-
-  // ---- weighted latent of the tile in stage st, `piece(j)` after MFMA j ----
-  auto weighted = [&](int st, const bf16x8& P0, const bf16x8& P1, auto&& piece) {
-    const LDS char* Ct = L + st * kStage;
-    constexpr int PD = 3;
-    // step j: column block mb = j % 16, position half kb2 = j / 16, so that
-    // consecutive MFMAs accumulate into different blocks
-    auto pv_operand = [&](int j) -> bf16x8 {
-      const int mb = j & 15, kb2 = j >> 4;
-      const LDS char* p1 = Ct + off.tr_off[0][mb & 3] + 256 * (mb >> 2) + 16 * kCRow * kb2;
-      const LDS char* p2 = Ct + off.tr_off[1][mb & 3] + 256 * (mb >> 2) + 16 * kCRow * kb2;
-      s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p1);
-      s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p2);
-      typedef __attribute__((ext_vector_type(8))) short s16x8;
-      return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8 ring[PD];
+    if (HAS_S) s = sacc;
 #pragma unroll
-    for (int j = 0; j < PD; ++j) ring[j] = pv_operand(j);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      O[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[j % PD], (j >> 4) ? P1 : P0, O[j & 15], 0, 0, 0);
-      if (j + PD < 32) ring[j % PD] = pv_operand(j + PD);
-      piece(j);
+    for (int i = 36; i < 68; ++i) {
+      const int j = i - 36;
+      O[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % D], (j >> 4) ? P1 : P0, O[j & 15], 0, 0, 0);
+      if (i + D < 68) ring[i % D] = operand(i + D);
+      if (i > 36) piece(i - 37);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -277,62 +291,53 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
       Pp1[r] = (__bf16)0.f;
     }
 
-    for (int32_t j = 0; j <= seg; ++j) {
-      const bool has_cur = j < seg;
-      f32x16 s;  // scores, then probabilities, of tile j (unused after the last tile)
-      bool full = true;
-      if (has_cur) {
-        const int32_t t = ct + j;
-        // tile j landed (tile j + 1 may still be in flight)
-        wait_vmcnt<kDmaPerWave>();
+    for (int32_t j = 0; j < seg; ++j) {
+      const int32_t t = ct + j;
+      // tile j landed (tile j + 1 may still be in flight)
+      wait_vmcnt<kDmaPerWave>();
+      __syncthreads();
+      // stage (j + 2) % 4 held tile j - 2, consumed in the previous
+      // iteration; tile j + 2 is loaded into it during the scores below
+      const int32_t pg_next = ld.checked(pg_next_p, pg_next_raw);
+      const bool valid_j2 = pg_next >= 0;
+      const TileLoader::Tile next_tile = ld.tile((j + 2) & 3, t + 2, pg_next);
+      pg_next_p = j + 3 < seg ? (t + 3) >> 1 : INT32_MAX;
+      pg_next_raw = ld.raw(j + 3 < seg ? pg_next_p : 0);
+      // rows of tile j that are visible
+      const int32_t nvis = valid_j ? (T - t * kTile < kTile ? T - t * kTile : kTile) : 0;
+      const bool full = nvis == kTile;
+      if (!full) {
+        // zero the invisible rows (they hold page-0 or past-the-end data,
+        // which a zero probability must not turn into NaN)
+        LDS char* Ct = L + (j & 3) * kStage;
+        const int r = tid >> 3, qq = tid & 7;
+        if (r >= nvis) {
+          LDS char* dst = Ct + r * kCRow + 128 * qq;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) *(LDS i32x4*)(dst + 16 * v) = i32x4{0, 0, 0, 0};
+        }
         __syncthreads();
-        // stage (j + 2) % 4 held tile j - 2, consumed in the previous
-        // iteration; tile j + 2 is loaded into it during the scores below
-        const int32_t pg_next = ld.checked(pg_next_p, pg_next_raw);
-        const bool valid_j2 = pg_next >= 0;
-        const TileLoader::Tile next_tile = ld.tile((j + 2) & 3, t + 2, pg_next);
-        pg_next_p = j + 3 < seg ? (t + 3) >> 1 : INT32_MAX;
-        pg_next_raw = ld.raw(j + 3 < seg ? pg_next_p : 0);
-        // rows of tile j that are visible
-        const int32_t nvis = valid_j ? (T - t * kTile < kTile ? T - t * kTile : kTile) : 0;
-        full = nvis == kTile;
-        if (!full) {
-          // zero the invisible rows (they hold page-0 or past-the-end data,
-          // which a zero probability must not turn into NaN)
-          LDS char* Ct = L + (j & 3) * kStage;
-          const int r = tid >> 3, qq = tid & 7;
-          if (r >= nvis) {
-            LDS char* dst = Ct + r * kCRow + 128 * qq;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) *(LDS i32x4*)(dst + 16 * v) = i32x4{0, 0, 0, 0};
-          }
-          __syncthreads();
-        }
-        s = scores(j & 3, [&](int k) {
-          if ((k & 3) == 0 && (k >> 2) < kDmaPerWave) ld.issue_one(next_tile, k >> 2);
-        });
-        if (!full) {
-          // position of accumulator r: 8 * (r / 4) + 4 * hi + r % 4
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int pos = 8 * (r >> 2) + 4 * hi + (r & 3);
-            s[r] = pos < nvis ? s[r] : -INFINITY;
-          }
-        }
-        valid_j = valid_j1;
-        valid_j1 = valid_j2;
       }
+      valid_j = valid_j1;
+      valid_j1 = valid_j2;
 
       // ---- softmax of tile j, in pieces, inside the weighted latent of tile j - 1 ----
+      f32x16 s;  // scores, then probabilities, of tile j
       float mt = -INFINITY, m_use = m_run, neg_m = 0.f, lsum = 0.f;
       bool need = false;
       bf16x8 Pc0, Pc1;
-      // (runs unconditionally: after the last tile it works on zeros and its
-      // results are dropped, which keeps the MFMA block free of branches)
       auto piece = [&](int k) {
         // Each step ends with an empty asm that takes its result: code motion
         // cannot then sink the VALU work past the MFMAs that hide it.
         if (k == 0) {
+          if (!full) {
+            // position of accumulator r: 8 * (r / 4) + 4 * hi + r % 4
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int pos = 8 * (r >> 2) + 4 * hi + (r & 3);
+              s[r] = pos < nvis ? s[r] : -INFINITY;
+            }
+          }
           mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
           asm volatile("" : "+v"(mt));
         } else if (k == 1) {
@@ -370,23 +375,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
           if (k == 27) asm volatile("" : "+v"(Pc1));
         }
       };
-      weighted((j + 3) & 3, Pp0, Pp1, piece);
+      stream(std::true_type{}, j & 3, (j + 3) & 3, Pp0, Pp1, s,
+             [&](int k) {
+               if ((k & 3) == 0 && (k >> 2) < kDmaPerWave) ld.issue_one(next_tile, k >> 2);
+             },
+             piece);
 
-      if (has_cur) {
-        // rescale what the accumulator holds (tiles up to j - 1) to the new reference
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
-          l_run *= alpha;
+      // rescale what the accumulator holds (tiles up to j - 1) to the new reference
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
+        l_run *= alpha;
 #pragma unroll
-          for (int mb = 0; mb < 16; ++mb)
+        for (int mb = 0; mb < 16; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
-        }
-        m_run = m_use;
-        l_run += lsum;
-        Pp0 = Pc0;
-        Pp1 = Pc1;
+          for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
       }
+      m_run = m_use;
+      l_run += lsum;
+      Pp0 = Pc0;
+      Pp1 = Pc1;
+    }
+    {
+      // weighted latent of the last tile
+      f32x16 s_unused;
+      stream(std::false_type{}, 0, (seg + 3) & 3, Pp0, Pp1, s_unused, [](int) {}, [](int) {});
     }
     done += seg;
 
