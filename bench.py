@@ -31,7 +31,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_v2_batched_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_absorb_amd", "csrc", "decode_attn_mfma.hip")
+# Sources that define the timed attention kernel (decode_bf16_kernel): the
+# traffic counters are used only while they match.
+KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_absorb_amd", "csrc", f)
+               for f in ("decode_attn_bf16.hip", "attn_common.h", "tile_space.h", "mla_internal.h")]
 
 
 def log(msg):
@@ -39,8 +42,11 @@ def log(msg):
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile():
@@ -195,7 +201,7 @@ def main():
         "attn_us": round(attn_avg_ms * 1e3, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "mla_decode_attn (decode_mfma_kernel<bf16, dense, split>)",
+            "kernel": "mla_decode_attn (decode_bf16_kernel<split>)",
             "achieved": round(attn_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

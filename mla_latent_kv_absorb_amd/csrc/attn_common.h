@@ -58,6 +58,42 @@ __device__ __forceinline__ float wave_partner(float v) {
   return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
 }
 
+// Lane (l % 32, hi = l / 32) of a weighted-latent accumulator set O[16]
+// (U^T blocks of 32 columns, one head per lane) holds columns
+// 32 mb + 8 g + 4 hi + e of its head in O[mb][4 g + e].  Write the head's 512
+// columns, times inv, as BF16 to row[0..511] with 16-byte stores: the two
+// lanes of a head swap half of each pair of groups so that each lane owns 8
+// consecutive columns per store (32 stores per lane instead of 64).
+__device__ __forceinline__ void store_row_bf16(__bf16* row, const f32x16 (&O)[16], float inv) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const int hi = __lane_id() >> 5;
+#pragma unroll
+  for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int g0 = 2 * k, g1 = 2 * k + 1;
+      // hi = 0 keeps group g0 (columns 8 g0 + 0..3) and sends g1 (8 g1 + 0..3);
+      // hi = 1 keeps group g1 (8 g1 + 4..7) and sends g0 (8 g0 + 4..7).
+      uint32_t keep[2], send[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bf16x2 k0 = {(__bf16)(O[mb][4 * g0 + 2 * e] * inv), (__bf16)(O[mb][4 * g0 + 2 * e + 1] * inv)};
+        const bf16x2 k1 = {(__bf16)(O[mb][4 * g1 + 2 * e] * inv), (__bf16)(O[mb][4 * g1 + 2 * e + 1] * inv)};
+        const uint32_t u0 = __builtin_bit_cast(uint32_t, k0), u1 = __builtin_bit_cast(uint32_t, k1);
+        keep[e] = hi ? u1 : u0;
+        send[e] = hi ? u0 : u1;
+      }
+      uint32_t recv[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) recv[e] = __float_as_uint(wave_partner(__uint_as_float(send[e])));
+      // hi = 0: columns 8 g0 + [own 0..3 | partner's 4..7]
+      // hi = 1: columns 8 g1 + [partner's 0..3 | own 4..7]
+      const i32x4 v = hi ? i32x4{(int)recv[0], (int)recv[1], (int)keep[0], (int)keep[1]}
+                         : i32x4{(int)keep[0], (int)keep[1], (int)recv[0], (int)recv[1]};
+      *(i32x4*)(row + 32 * mb + 8 * (hi ? g1 : g0)) = v;
+    }
+}
+
 // x * alpha for an accumulator value, kept in its accumulator register.  The
 // online-softmax rescale runs only when a head's running maximum grows by a
 // large step; writing it this way keeps the register allocator from moving

@@ -8,10 +8,10 @@
 // same tile partition the attention kernel used (worker p writes slot p + b).
 //
 // One wave per (request, head): each lane owns 8 consecutive latent columns
-// (two 16-byte loads per partial), so a head row of 512 floats is one
-// coalesced 2 KiB read per partial, and the loads of 8 partials are in flight
-// together.  The merge weights are computed one partial per lane and read
-// back with readlane.
+// (one 16-byte load per partial for BF16 partials, two for FP32), so a head
+// row of 512 values is one coalesced read per partial, and the loads of 8
+// partials are in flight together.  The merge weights are computed one
+// partial per lane and read back with readlane.
 #include "tile_space.h"
 
 namespace mla {
@@ -35,15 +35,32 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <bool VEC>
+// 8 consecutive partial values starting at src, as FP32
+template <typename PT>
+__device__ __forceinline__ void load8(const PT* src, f32x4& lo, f32x4& hi) {
+  if constexpr (sizeof(PT) == 2) {
+    const bf16x8 v = *(const bf16x8*)src;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = (float)v[e];
+      hi[e] = (float)v[4 + e];
+    }
+  } else {
+    lo = ((const f32x4*)src)[0];
+    hi = ((const f32x4*)src)[1];
+  }
+}
+
+// PT: partial element type (__bf16 or float); VEC: 8 columns per lane.
+template <typename PT, bool VEC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int32_t b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.x * kWaves + (threadIdx.x >> 6);
 
-  // tile range of request b in the concatenated tile space
-  const int64_t W = tiles_below(a.seq_lens, a.batch, a.topk);
-  const int64_t start = tiles_below(a.seq_lens, b, a.topk);
+  // units of the split space (each request: its lead, then its tiles)
+  const int64_t W = spans_below(a.seq_lens, a.batch, a.topk);
+  const int64_t start = spans_below(a.seq_lens, b, a.topk) + kLeadTiles;  // first tile of request b
   const int32_t nt_b = a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[b]);
   if (h >= a.H) return;
   const int64_t P = a.num_workers;
@@ -82,8 +99,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   tot = wave_sum(tot);
   const float inv = tot > 0.f ? 1.0f / tot : 0.f;
   const int64_t dst = ((int64_t)b * a.H + h) * a.D_C;
-  const int64_t row_stride = (int64_t)a.H * a.D_C;  // floats between slots
-  const float* row0 = a.part_o + ((int64_t)b * a.H + h) * a.D_C;  // worker p's row (slot p + b): row0 + p * row_stride
+  const int64_t row_stride = (int64_t)a.H * a.D_C;  // elements between slots
+  const PT* row0 = (const PT*)a.part_o + ((int64_t)b * a.H + h) * a.D_C;  // worker p's row (slot p + b): row0 + p * row_stride
 
   // Every lane runs every iteration (the weights are read from other lanes
   // with readlane, so no lane may sit out); lanes past the row end load a
@@ -109,13 +126,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
           const int32_t jj = j + u < n ? j + u : n - 1;
           wg[u] = j + u < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), jj)) : 0.f;
           const int64_t p = p_first + 64 * c + jj;  // its slot is p + b
-          const float* src = row0 + p * row_stride + d0;
-          if (VEC) {
-            v0[u] = ((const f32x4*)src)[0];
-            v1[u] = ((const f32x4*)src)[1];
-          } else {
-            vs[u] = src[0];
-          }
+          const PT* src = row0 + p * row_stride + d0;
+          if (VEC) load8(src, v0[u], v1[u]);
+          else vs[u] = (float)src[0];
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -157,8 +170,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const dim3 grid((a.H + kWaves - 1) / kWaves, a.batch);
-  if (a.D_C % 8 == 0) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(kThreads), 0, s, a);
+  if (a.part_bf16) {
+    if (a.D_C % 8 == 0) hipLaunchKernelGGL((combine_kernel<__bf16, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<__bf16, false>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (a.D_C % 8 == 0) hipLaunchKernelGGL((combine_kernel<float, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<float, false>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

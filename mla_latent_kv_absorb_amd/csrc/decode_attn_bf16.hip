@@ -117,8 +117,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
   const int head = 32 * w + row;
   const float scale_log2 = a.scale * kLog2e;
 
-  // ---- this work-group's tiles: request b0 from tile t0, n tiles ----
-  int32_t b0, t0;
+  // ---- this work-group's share: n units of the split space from offset v0
+  // of request b0's span (a span is the request's lead, then its tiles) ----
+  int32_t b0, v0;
   int64_t n;
   const int64_t worker = blockIdx.x;
   auto ntiles = [&](int32_t b) -> int32_t {
@@ -127,15 +128,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
   };
   if (DIRECT) {
     b0 = blockIdx.x;
-    t0 = 0;
+    v0 = kLeadTiles;  // no lead: straight to tile 0
     n = ntiles(b0);
   } else {
-    const int64_t W = tiles_below(a.seq_lens, a.batch, 0);
+    const int64_t W = spans_below(a.seq_lens, a.batch, 0);
     const int64_t g0 = worker_lo(worker, W, a.num_workers);
     const int64_t g1 = worker_lo(worker + 1, W, a.num_workers);
     n = g1 - g0;
     if (n <= 0) return;
-    locate_tile(a.seq_lens, a.batch, 0, g0, &b0, &t0);
+    locate_span(a.seq_lens, a.batch, 0, g0, &b0, &v0);
   }
 
   if (n == 0) {  // direct mode, a request with no position
@@ -225,11 +226,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     }
   };
 
-  int32_t cb = b0, ct = t0;
-  int64_t done = 0;
+  int32_t cb = b0;
+  int64_t cv = v0;   // offset of the next unit inside request cb's span
+  int64_t done = 0;  // units consumed
   while (done < n) {
     // ---- one segment: tiles [ct, ct + seg) of request cb ----
     if (cb >= a.batch) break;  // unreachable when the tile accounting is consistent
+    if (cv < kLeadTiles) {  // the lead of request cb carries no work
+      const int64_t skip = kLeadTiles - cv < n - done ? kLeadTiles - cv : n - done;
+      done += skip;
+      cv += skip;
+      if (done >= n) break;
+    }
+    const int32_t ct = (int32_t)(cv - kLeadTiles);
     const int32_t nt_cb = ntiles(cb);
     const int64_t left = nt_cb - ct;
     const int32_t seg = (int32_t)(left < n - done ? left : n - done);
@@ -421,23 +430,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
           }
         if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
       } else {
+        // partials of the MFMA kernels are BF16
         const int64_t slot = worker + cb;
-        float* o = a.part_o + (slot * kHeads + head) * kLatent + 4 * hi;
-#pragma unroll
-        for (int mb = 0; mb < 16; ++mb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = O[mb][4 * g + e] * inv;
-            *(f32x4*)(o + 32 * mb + 8 * g) = v;
-          }
+        store_row_bf16((__bf16*)a.part_o + (slot * kHeads + head) * kLatent, O, inv);
         if (hi == 0) a.part_lse[slot * kHeads + head] = lse;
       }
     }
     // next request with tiles
     ++cb;
-    ct = 0;
+    cv = 0;
     while (cb < a.batch && ntiles(cb) == 0) ++cb;
   }
   wait_vmcnt<0>();

@@ -52,25 +52,27 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
     return T > 0 ? tiles_of(T) : 0;
   };
 
-  int32_t cb, ct;
-  int64_t n;
+  int32_t cb, ct = 0;
+  int64_t cv, n;
   const int64_t worker = blockIdx.x;
   if (DIRECT) {
     cb = blockIdx.x;
-    ct = 0;
+    cv = kLeadTiles;  // no lead: straight to tile 0
     n = ntiles(cb);
   } else {
+    // n units of the split space from offset cv of request cb's span (the
+    // request's lead, then its tiles)
     int64_t W = 0;
-    for (int32_t b = 0; b < a.batch; ++b) W += ntiles(b);
+    for (int32_t b = 0; b < a.batch; ++b) W += span_of(ntiles(b));
     const int64_t g0 = worker_lo(worker, W, a.num_workers);
     const int64_t g1 = worker_lo(worker + 1, W, a.num_workers);
     n = g1 - g0;
     if (n <= 0) return;
     int64_t acc = 0;
     int32_t b = 0;
-    while (acc + ntiles(b) <= g0) { acc += ntiles(b); ++b; }
+    while (acc + span_of(ntiles(b)) <= g0) { acc += span_of(ntiles(b)); ++b; }
     cb = b;
-    ct = (int32_t)(g0 - acc);
+    cv = g0 - acc;
   }
   if (n == 0) {
     if (DIRECT) {
@@ -87,6 +89,13 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
   int64_t i = 0;
   while (i < n) {
     if (cb >= a.batch) break;  // unreachable when the tile accounting is consistent
+    if (cv < kLeadTiles) {  // the lead of request cb carries no work
+      const int64_t skip = kLeadTiles - cv < n - i ? kLeadTiles - cv : n - i;
+      i += skip;
+      cv += skip;
+      if (i >= n) break;
+    }
+    ct = (int32_t)(cv - kLeadTiles);
     const int64_t left = ntiles(cb) - ct;
     const int64_t seg = left < n - i ? left : n - i;
     if (seg <= 0) break;
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
       const float l = sl[h];
       const float v = l > 0.f ? so[e] / l : 0.f;
       if (DIRECT) ((float*)a.o_lat)[(int64_t)b * H * DC + e] = v;
-      else a.part_o[((worker + b) * H) * DC + e] = v;
+      else ((float*)a.part_o)[((worker + b) * H) * DC + e] = v;
     }
     for (int h = tid; h < H; h += kThreads) {
       const float l = sl[h];
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
       else a.part_lse[(worker + b) * H + h] = lse;
     }
     ++cb;
-    ct = 0;
+    cv = 0;
     while (cb < a.batch && ntiles(cb) == 0) ++cb;
   }
 }

@@ -215,21 +215,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 
   Loader<FP8, TOPK> ld{a, (uint32_t)(uintptr_t)smem, lane, w};
 
-  // ---- this work-group's tiles: [first request b0, tile t0], n tiles ----
-  int32_t b0, t0;
+  // ---- this work-group's share: n units of the split space from offset v0
+  // of request b0's span (a span is the request's lead, then its tiles) ----
+  int32_t b0, v0;
   int64_t n;
   int64_t worker = blockIdx.x;
   if (DIRECT) {
     b0 = blockIdx.x;
-    t0 = 0;
+    v0 = kLeadTiles;  // no lead: straight to tile 0
     n = ld.ntiles(b0);
   } else {
-    const int64_t W = tiles_below(a.seq_lens, a.batch, TOPK ? a.topk : 0);
+    const int64_t W = spans_below(a.seq_lens, a.batch, TOPK ? a.topk : 0);
     const int64_t g0 = worker_lo(worker, W, a.num_workers);
     const int64_t g1 = worker_lo(worker + 1, W, a.num_workers);
     n = g1 - g0;
     if (n <= 0) return;
-    locate_tile(a.seq_lens, a.batch, TOPK ? a.topk : 0, g0, &b0, &t0);
+    locate_span(a.seq_lens, a.batch, TOPK ? a.topk : 0, g0, &b0, &v0);
   }
 
   // ---- per-lane LDS offsets (relative to a tile) ----
@@ -246,7 +247,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   bf16x8 q[32];
   bf16x8 qr[4];
 
-  int32_t cb = b0, ct = t0;      // current request and tile
+  int32_t cb = b0;      // current request
+  int64_t cv = v0;      // offset of the next unit inside request cb's span
   LDS int32_t* list = (LDS int32_t*)(L + C::LIST_OFF);
 
   if (n == 0) {  // only in direct mode: a request with no position
@@ -258,10 +260,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     return;
   }
 
-  int64_t i = 0;  // tiles of this work-group consumed so far
+  int64_t i = 0;  // units of this work-group consumed so far
   while (i < n) {
     // ---- one segment: tiles [ct, ct + seg_len) of request cb ----
     if (cb >= a.batch) break;  // unreachable when the tile accounting is consistent
+    if (cv < kLeadTiles) {  // the lead of request cb carries no work
+      const int64_t skip = kLeadTiles - cv < n - i ? kLeadTiles - cv : n - i;
+      i += skip;
+      cv += skip;
+      if (i >= n) break;
+    }
+    const int32_t ct = (int32_t)(cv - kLeadTiles);
     const int32_t nt_cb = ld.ntiles(cb);
     const int64_t left_in_req = nt_cb - ct;
     const int32_t seg_len = (int32_t)(left_in_req < n - i ? left_in_req : n - i);
@@ -479,23 +488,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
           }
         if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
       } else {
+        // partials of the MFMA kernels are BF16
         const int64_t slot = worker + cb;
-        float* o = a.part_o + (slot * kHeads + head) * kLatent + 4 * hi;
-#pragma unroll
-        for (int mb = 0; mb < 16; ++mb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = O[mb][4 * g + e] * inv;
-            *(f32x4*)(o + 32 * mb + 8 * g) = v;
-          }
+        store_row_bf16((__bf16*)a.part_o + (slot * kHeads + head) * kLatent, O, inv);
         if (hi == 0) a.part_lse[slot * kHeads + head] = lse;
       }
     }
     // next request with tiles
     ++cb;
-    ct = 0;
+    cv = 0;
     while (cb < a.batch && ld.ntiles(cb) == 0) ++cb;
   }
   wait_vmcnt<0>();

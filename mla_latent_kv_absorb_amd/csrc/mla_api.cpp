@@ -72,6 +72,13 @@ size_t workspace_bytes_for(const mla_config* c, int64_t slots) {
   return al16((size_t)slots * c->num_heads * c->d_latent * 4) + al16((size_t)slots * c->num_heads * 4);
 }
 
+// Split partials (normalised weighted latents) are kept in BF16 when the
+// activations are BF16: the combined output is rounded to BF16 anyway, so one
+// more BF16 rounding of each partial stays at the output's own precision,
+// and the partials cost half the bytes to write and to read back.  The FP32
+// path keeps FP32 partials.
+bool partials_bf16(Path p) { return p != Path::kF32; }
+
 mla_status launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
 
 }  // namespace
@@ -107,14 +114,14 @@ mla_status mla_decode_plan(const mla_config* cfg, int32_t batch, const int32_t* 
   if (st != MLA_OK) return st;
   if (plan == nullptr || batch < 1 || topk < 0 || num_cus < 1) return MLA_ERR_INVALID_ARG;
   if (seq_lens_host == nullptr && topk == 0 && max_len < 1) return MLA_ERR_INVALID_ARG;
-  int64_t W = 0;
+  int64_t W = 0;  // tiles of the batch
   for (int32_t b = 0; b < batch; ++b) {
     int32_t len = topk > 0 ? topk : (seq_lens_host ? seq_lens_host[b] : max_len);
     if (len < 0) return MLA_ERR_INVALID_ARG;
     W += mla::tiles_of(len);
   }
   if (W < 1) W = 1;
-  // Enough tiles per worker that a partial (H x D_C floats) stays small next
+  // Enough tiles per worker that a partial (H x D_C values) stays small next
   // to the cache bytes the worker reads, and no more workers than CUs: one
   // 4-wave work-group fills a CU.
   const int64_t kMinTilesPerWorker = 16;
@@ -206,8 +213,9 @@ mla_status mla_decode_attn(const mla_config* cfg, const void* q_lat, const void*
     const int64_t slots = (int64_t)plan->num_workers + batch - 1;
     if (workspace_bytes < workspace_bytes_for(cfg, slots)) return MLA_ERR_INVALID_ARG;
     a.num_workers = plan->num_workers;
-    a.part_o = (float*)workspace;
+    a.part_o = workspace;
     a.part_lse = (float*)((char*)workspace + al16((size_t)slots * cfg->num_heads * cfg->d_latent * 4));
+    a.part_bf16 = partials_bf16(path);
   }
   hipStream_t s = (hipStream_t)stream;
   if (path == Path::kF32) return launch_status(mla::launch_decode_f32(a, s));
@@ -229,8 +237,9 @@ mla_status mla_combine(const mla_config* cfg, const void* workspace, size_t work
   if (workspace_bytes < workspace_bytes_for(cfg, slots)) return MLA_ERR_INVALID_ARG;
   if (cfg->d_latent % 4 != 0) return MLA_ERR_UNSUPPORTED;
   mla::CombineArgs a{};
-  a.part_o = (const float*)workspace;
+  a.part_o = workspace;
   a.part_lse = (const float*)((const char*)workspace + al16((size_t)slots * cfg->num_heads * cfg->d_latent * 4));
+  a.part_bf16 = partials_bf16(path);
   a.seq_lens = seq_lens;
   a.topk = topk;
   a.batch = batch;

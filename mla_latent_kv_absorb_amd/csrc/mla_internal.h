@@ -30,8 +30,9 @@ struct DecodeArgs {
   int32_t topk;
   int32_t batch;
   int32_t num_workers;      // 0 = one work-group per request, final output
-  float* part_o;            // [slots][H][D_C]
+  void* part_o;             // [slots][H][D_C], BF16 if part_bf16 else FP32
   float* part_lse;          // [slots][H]
+  int32_t part_bf16;
   void* o_lat;              // final output (direct mode)
   float* lse_out;           // optional
   int32_t H, D_C, D_R;
@@ -39,8 +40,9 @@ struct DecodeArgs {
 };
 
 struct CombineArgs {
-  const float* part_o;
+  const void* part_o;       // [slots][H][D_C], BF16 if part_bf16 else FP32
   const float* part_lse;
+  int32_t part_bf16;
   const int32_t* seq_lens;
   int32_t topk;
   int32_t batch;
@@ -72,18 +74,26 @@ size_t decode_f32_lds_bytes(int H, int D_C, int D_R);
 }  // namespace mla
 
 // ---------------------------------------------------------------------------
-// Split partition shared by the attention kernels and the combine kernel:
-// all requests' tiles are concatenated in request order (W tiles in total)
-// and worker p takes tiles [lo(p), lo(p+1)) with lo(p) = floor(p*W/P).  A
-// worker that covers tiles of several requests emits one partial per request
-// into slot p + b, which is unique because p and b never both stay the same
-// from one piece to the next.
+// Split partition shared by the attention kernels and the combine kernel.
+// Every request with at least one tile occupies span_of(nt) = kLeadTiles + nt
+// units of a concatenated space (requests in order, W units in total): a
+// lead of kLeadTiles units that carry no work, then its nt tiles.  Worker p
+// takes units [lo(p), lo(p+1)) with lo(p) = floor(p*W/P) and processes the
+// tiles among them.  The lead stands for the fixed cost of starting a request
+// (query loads, pipeline fill, one more partial to write): a worker whose
+// range crosses into a new request gets that many fewer tiles, which evens
+// out the finishing times.  A worker that covers tiles of several requests
+// emits one partial per request into slot p + b, which is unique because p
+// and b never both stay the same from one piece to the next.
 // ---------------------------------------------------------------------------
 namespace mla {
+constexpr int32_t kLeadTiles = 16;
 __host__ __device__ inline int64_t worker_lo(int64_t p, int64_t W, int64_t P) { return (p * W) / P; }
-// Worker whose tile range contains global tile x (0 <= x < W).
+// Worker whose range contains unit x (0 <= x < W).
 __host__ __device__ inline int64_t worker_of(int64_t x, int64_t W, int64_t P) {
   return ((x + 1) * P - 1) / W;
 }
 __host__ __device__ inline int32_t tiles_of(int32_t len) { return (len + kTile - 1) / kTile; }
+// Units of the split space taken by a request with nt tiles.
+__host__ __device__ inline int64_t span_of(int32_t nt) { return nt > 0 ? (int64_t)nt + kLeadTiles : 0; }
 }  // namespace mla

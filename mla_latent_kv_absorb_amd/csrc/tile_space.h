@@ -26,33 +26,35 @@ __device__ inline int64_t wave_sum_i64(int64_t v) {
   return uniform_i64(v);
 }
 
-// Total tiles of requests [0, upto).
-__device__ inline int64_t tiles_below(const int32_t* seq_lens, int32_t upto, int32_t topk) {
-  if (topk > 0) return (int64_t)upto * tiles_of(topk);
+// Units of the split space (span_of) taken by requests [0, upto).
+__device__ inline int64_t spans_below(const int32_t* seq_lens, int32_t upto, int32_t topk) {
+  if (topk > 0) return (int64_t)upto * span_of(tiles_of(topk));
   const int lane = __lane_id();
   int64_t sum = 0;
   for (int32_t base = 0; base < upto; base += 64) {
     const int32_t r = base + lane;
-    sum += r < upto ? tiles_dense(seq_lens[r]) : 0;
+    sum += r < upto ? span_of(tiles_dense(seq_lens[r])) : 0;
   }
   return wave_sum_i64(sum);
 }
 
-// Request holding global tile g (0 <= g < total) and the tile's index inside it.
-__device__ inline void locate_tile(const int32_t* seq_lens, int32_t batch, int32_t topk, int64_t g,
-                                            int32_t* b, int32_t* t) {
+// Request whose span holds unit g of the split space (0 <= g < total) and
+// the unit's offset inside that span (below kLeadTiles: the lead; else tile
+// offset - kLeadTiles).
+__device__ inline void locate_span(const int32_t* seq_lens, int32_t batch, int32_t topk, int64_t g,
+                                   int32_t* b, int32_t* t) {
   if (topk > 0) {
-    const int32_t nt = tiles_of(topk);
-    *b = (int32_t)(g / nt);
-    *t = (int32_t)(g % nt);
+    const int64_t sp = span_of(tiles_of(topk));
+    *b = (int32_t)(g / sp);
+    *t = (int32_t)(g % sp);
     return;
   }
   const int lane = __lane_id();
   int64_t off = 0;
   for (int32_t base = 0; base < batch; base += 64) {
     const int32_t r = base + lane;
-    const int64_t nt = r < batch ? tiles_dense(seq_lens[r]) : 0;
-    int64_t incl = nt;  // inclusive scan over the lanes
+    const int64_t sp = r < batch ? span_of(tiles_dense(seq_lens[r])) : 0;
+    int64_t incl = sp;  // inclusive scan over the lanes
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int64_t up = __shfl_up(incl, d);
@@ -62,14 +64,14 @@ __device__ inline void locate_tile(const int32_t* seq_lens, int32_t batch, int32
     const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > g);
     if (hit != 0) {
       const int l = __builtin_ctzll(hit);
-      const int64_t end = __shfl(incl, l), len = __shfl(nt, l);
+      const int64_t end = __shfl(incl, l), len = __shfl(sp, l);
       *b = base + l;
       *t = __builtin_amdgcn_readfirstlane((int32_t)(g - (end - len)));
       return;
     }
     off = uniform_i64(__shfl(incl, 63));
   }
-  *b = batch;  // g beyond the last tile
+  *b = batch;  // g beyond the last span
   *t = 0;
 }
 

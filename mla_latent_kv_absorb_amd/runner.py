@@ -27,9 +27,10 @@ def to_device_act(x: np.ndarray, act: str, device):
 
 
 def workspace_bytes(H: int, D_C: int, slots: int) -> int:
-    """Bytes of the split workspace: float32 partials [slots][H][D_C] then
-    float32 log-sum-exps [slots][H], each section 16-byte aligned (the layout
-    mla_decode_plan sizes)."""
+    """Bytes of the split workspace: a partials section sized for float32
+    [slots][H][D_C] (the BF16-activation paths store BF16 partials in its first
+    half) then float32 log-sum-exps [slots][H], each section 16-byte aligned
+    (the layout mla_decode_plan sizes)."""
     al = lambda x: (x + 15) // 16 * 16
     return al(slots * H * D_C * 4) + al(slots * H * 4)
 
@@ -102,13 +103,18 @@ class DeviceWorkload:
         self.up(stream)
 
     def partials(self):
-        """(o_part [slots, H, D_C], lse_part [slots, H]) views of the workspace (split mode)."""
+        """(o_part [slots, H, D_C], lse_part [slots, H]) of the workspace (split
+        mode), both float32; the partials are stored as BF16 when the
+        activations are BF16 and widened here."""
         import torch
         slots = self.plan.num_slots
         H, DC = self.inp.H, self.inp.D_C
         n_o = slots * H * DC
         o_bytes = (n_o * 4 + 15) // 16 * 16
         ws = self.workspace
-        o = ws[: n_o * 4].view(torch.float32).view(slots, H, DC)
+        if self.inp.act_dtype == I.DTYPE_F32:
+            o = ws[: n_o * 4].view(torch.float32).view(slots, H, DC)
+        else:
+            o = ws[: n_o * 2].view(torch.bfloat16).view(slots, H, DC).float()
         l = ws[o_bytes: o_bytes + slots * H * 4].view(torch.float32).view(slots, H)
         return o, l

@@ -295,9 +295,10 @@ def _bit_pattern_case(cache, seed):
 @pytest.mark.parametrize("cache", [I.DTYPE_BF16, I.DTYPE_FP8])
 def test_topk_index_handling_bit_exact(torch, R, cache):
     """Zero queries give every picked position probability 1; latent dim d of
-    position p holds bit d of p.  With one worker the float32 partial is
-    exactly (number of picked positions with bit d set) / 128, so a wrong,
-    missing or repeated index changes its bits."""
+    position p holds bit d of p.  With one worker the partial is exactly
+    (number of picked positions with bit d set) / 128 (a multiple of 2^-7 with
+    at most 8 significant bits, so exact in the BF16 partials too), and a
+    wrong, missing or repeated index changes its bits."""
     _log(f"topk bit pattern {cache}")
     inp, idx = _bit_pattern_case(cache, seed=7)
     w = R.DeviceWorkload(inp, split=True, num_workers=1)
