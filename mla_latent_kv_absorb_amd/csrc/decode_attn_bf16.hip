@@ -50,6 +50,19 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
+// Score MFMA with its accumulator in ordinary registers (the softmax reads the
+// scores with VALU instructions, and the accumulator registers hold the
+// weighted latent).  Back-to-back MFMAs that accumulate into the same
+// registers need no wait states; the reader of the final value waits.
+__device__ __forceinline__ f32x16 mfma_sv0(const bf16x8& a, const bf16x8& b) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_sv(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
 struct TileLoader {
   const uint8_t* pool;
   int64_t page_bytes, rope_off, num_pages;
@@ -201,21 +214,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     auto operand = [&](int i) -> bf16x8 { return i < 36 ? s_operand(Cs, i) : pv_operand(Cp, i - 36); };
     bf16x8 ring[D];
     bf16x8 rq[D];
-    f32x16 sacc = f32x16{};
+    f32x16 sacc;
 #pragma unroll
     for (int i = I0; i < I0 + D; ++i) ring[i % D] = operand(i);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = I0; i < 36; ++i) {
       const bf16x8 bq = i < 32 ? q[i & 31] : rq[(i + 3 * D - 32) % D];
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % D], bq, sacc, 0, 0, 0);
+      if (i == 0) sacc = mfma_sv0(ring[i % D], bq);
+      else mfma_sv(sacc, ring[i % D], bq);
       ring[i % D] = operand(i + D);
       // rotary query blocks, D MFMAs ahead of their use
       if (i >= 32 - D && i < 36 - D) rq[(i + D - 32) % D] = rq_operand(i + D - 32);
       after_s(i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (HAS_S) s = sacc;
+    if (HAS_S) {
+      // the last score MFMA's result is read by VALU instructions: cover the
+      // MFMA-write -> VALU-read distance (at most 19 wait states)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(sacc));
+      s = sacc;
+    }
 #pragma unroll
     for (int i = 36; i < 68; ++i) {
       const int j = i - 36;
