@@ -4,15 +4,19 @@
 Workload: DeepSeek-V2 dims (128 heads, latent 512, rotary 64, head dim 128),
 BF16 latent cache in 64-token pages shuffled across one pool, batch 64 with
 per-request contexts uniform in [16,384, 32,768]; one decode step per request.
-A step is the whole path: absorb_q -> decode_attn -> combine -> out_up, on one
-stream, inputs resident in HBM before timing starts.
+A step is the whole path: absorb_q -> decode_attn -> combine + out_up (one
+launch, mla_combine_out_up), on one stream, inputs resident in HBM before
+timing starts.
 
 Prints one JSON line.  `value` is the latent-KV read rate of the whole step:
 cache bytes read per step (each visible position's 1,152-byte item once) over
 the step time.  Also reported: decode tokens/s, the attention kernel's own
 rate against the HBM roofline (HIP events around every attention launch in
-the timed region), and the float64 CPU oracle timed on whole requests of
-the same workload on the host cores (about 15 s of work).
+the timed region), the float64 CPU oracle timed on whole requests of the
+same workload on the host cores (about 15 s of work), each launch's time with
+the matrix-core utilisation of the attention and the weight rate of the two
+head GEMMs ("parts"), and a plain streaming read for reference.  --long adds
+one layer of the long-context workload (1 request x 131,072 positions).
 """
 
 from __future__ import annotations
@@ -30,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_FLOPS = 2.5e15  # dense MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_v2_batched_traffic.json")
 # Sources that define the timed attention kernel (decode_bf16_kernel): the
 # traffic counters are used only while they match.
@@ -98,6 +103,49 @@ def cpu_baseline(inp, budget_s=15.0):
     }
 
 
+def read_ceiling(torch, gib=2, reps=10):
+    """A plain streaming read for reference: torch's sum over a 2 GiB int32
+    buffer resident in HBM (bytes read / time, HIP events)."""
+    x = torch.ones((gib << 30) // 4, dtype=torch.int32, device="cuda")
+    x.sum()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        x.sum()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del x
+    return {"GBps": round((gib << 30) / (ms * 1e-3) / 1e9, 1), "kind": "torch.sum over 2 GiB int32"}
+
+
+def long_context_layer(torch, I, runner, num_cus, layers=4, reps=8):
+    """One decode step of the long-context workload (1 request, 131,072
+    positions) per layer: four independent layer draws are cycled so that
+    every launch reads its cache from HBM rather than from the last-level
+    cache.  Reports the average step time per layer and the per-token rate
+    over the workload's 60 layers."""
+    ws = []
+    for layer in range(layers):
+        inp = I.make_inputs("v2_long", layer=layer)
+        ws.append(runner.DeviceWorkload(inp, split=True, num_cus=num_cus))
+    cache_bytes = I.cache_bytes_read(inp)
+    for w in ws:
+        w.step_fused()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        for w in ws:
+            w.step_fused()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (reps * layers)
+    return {"us_per_layer": round(us, 2), "cache_GBps": round(cache_bytes / (us * 1e-6) / 1e9, 1),
+            "tokens_per_s_60_layers": round(1e6 / (60 * us), 1), "workers": ws[0].plan.num_workers}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +154,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--long", action="store_true",
+                    help="also time one layer of the long-context workload (1 request, 131,072 positions)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
@@ -137,36 +187,56 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        w.step()
+        w.step_fused()
     torch.cuda.synchronize()
     log("warmup done")
 
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # events between the three launches of every timed step, on the launch
+    # stream: absorb, attention, merge + up-projection (one launch)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for k in range(args.steps):
-        w.absorb()
         ev[k][0].record(stream)
-        w.attend()
+        w.absorb()
         ev[k][1].record(stream)
-        w.combine()
-        w.up()
+        w.attend()
+        ev[k][2].record(stream)
+        w.combine_up()
+        ev[k][3].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(stop)
-    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    part_ms = lambda i: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
+    absorb_ms, attn_avg_ms, tail_ms = part_ms(0), part_ms(1), part_ms(2)
     ms_per_step = total_ms / args.steps
-    attn_avg_ms = float(np.mean(attn_ms))
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s), "
         f"attention {attn_avg_ms * 1e3:.1f} us")
 
     gbps = cache_bytes / (ms_per_step * 1e-3) / 1e9
     attn_gbps = cache_bytes / (attn_avg_ms * 1e-3) / 1e9
     tokens_per_s = inp.B / (ms_per_step * 1e-3)
+
+    # matrix-core view of the same launches (dense BF16 peak), and the head
+    # GEMMs against their weight read
+    attn_flop = float(np.sum(inp.seq_lens.astype(np.int64))) * 2 * inp.H * (inp.D_C + inp.D_R + inp.D_C)
+    gemm_flop = 2.0 * inp.B * inp.H * inp.D_C * inp.D_N
+    w_bytes = inp.H * inp.D_C * inp.D_N * 2
+    gemm = lambda ms, act_bytes: {"us": round(ms * 1e3, 2), "weight_GBps": round(w_bytes / (ms * 1e-3) / 1e9, 1),
+                                  "bytes_GBps": round((w_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1),
+                                  "mfma_util": round(gemm_flop / (ms * 1e-3) / BF16_PEAK_FLOPS, 5)}
+    part_bytes = w.plan.num_slots * inp.H * (inp.D_C * 2 + 4)  # BF16 partials + lse
+    parts = {
+        "absorb": gemm(absorb_ms, inp.B * inp.H * (inp.D_N + inp.D_C) * 2),
+        "attention": {"us": round(attn_avg_ms * 1e3, 2), "mfma_util": round(attn_flop / (attn_avg_ms * 1e-3) / BF16_PEAK_FLOPS, 4)},
+        "combine_out_up": gemm(tail_ms, part_bytes + inp.B * inp.H * inp.D_V * 2),
+    }
+    ceiling = read_ceiling(torch)
+    long_layer = long_context_layer(torch, I, runner, num_cus) if args.long else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -209,7 +279,11 @@ def main():
             "traffic": traffic_from_profile(),
         },
         "cpu_baseline": cpu,
+        "parts": parts,
+        "read_ceiling": ceiling,
     }
+    if long_layer is not None:
+        result["v2_long_layer"] = long_layer
     print(json.dumps(result), flush=True)
 
 

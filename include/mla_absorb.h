@@ -14,6 +14,7 @@
  *   3. mla_combine     log-sum-exp merge of split partials (exact identity of
  *                      softmax over a union of disjoint position sets)
  *   4. mla_out_up      out[h] = W_UV[h] U[h]            (Figure 6, form (2))
+ *   3+4. mla_combine_out_up  both in one launch, without storing U
  *
  * Conventions common to every call
  *  - All pointers except *_host ones are device pointers.  The caller owns
@@ -135,8 +136,10 @@ mla_status mla_absorb_q(const mla_config* cfg, const void* q_nope, const void* w
  *     o_lat [batch][H][D_C] (act_dtype) and, if lse_out != NULL, lse_out
  *     [batch][H] = log sum_j exp(score_j).  workspace is not used.
  *   o_lat == NULL: plan->num_workers work-groups share all position tiles of
- *     all requests evenly and write float32 partials (normalised weighted
- *     latent and its log-sum-exp) into workspace; mla_combine() finishes.
+ *     all requests and write partials (the normalised weighted latent, BF16
+ *     when act_dtype is BF16 and float32 otherwise, and its float32
+ *     log-sum-exp) into workspace; mla_combine() or mla_combine_out_up()
+ *     finishes.
  * A request whose positions are all skipped yields zeros and lse = -inf. */
 mla_status mla_decode_attn(const mla_config* cfg, const void* q_lat, const void* q_rope,
                            const void* kv_pool, int64_t num_pages, const int32_t* block_table,
@@ -158,6 +161,17 @@ mla_status mla_combine(const mla_config* cfg, const void* workspace, size_t work
  *   out [batch][H][D_V]: out[b][h][v] = sum_c w_uv[h][v][c] * o_lat[b][h][c] */
 mla_status mla_out_up(const mla_config* cfg, const void* o_lat, const void* w_uv, void* out,
                       int32_t batch, void* stream);
+
+/* Steps 3 and 4 in one launch: out[b][h] = W_UV[h] o_lat[b][h] with o_lat[b][h]
+ * the merge mla_combine computes (rounded to BF16 as mla_combine stores it),
+ * never written to memory (Figure 6, form (2), after the exact log-sum-exp
+ * merge).  workspace, seq_lens, topk, batch and plan as for mla_combine;
+ * w_uv and out as for mla_out_up; lse_out [batch][H] may be NULL.  Served for
+ * act_dtype BF16 at H = 128, D_C = 512, D_V = 128; other configurations return
+ * MLA_ERR_UNSUPPORTED (use mla_combine, then mla_out_up). */
+mla_status mla_combine_out_up(const mla_config* cfg, const void* workspace, size_t workspace_bytes,
+                              const int32_t* seq_lens, int32_t topk, int32_t batch, const mla_plan* plan,
+                              const void* w_uv, void* out, float* lse_out, void* stream);
 
 /* Host-side check of the device-metadata contract on host copies: lengths
  * >= 1, enough block-table columns, page ids in [0, num_pages) for every page

@@ -25,7 +25,7 @@ TILE_TOKENS = 32
 
 EXPORTED = (
     "mla_abi_version", "mla_status_string", "mla_page_layout", "mla_decode_plan",
-    "mla_absorb_q", "mla_decode_attn", "mla_combine", "mla_out_up",
+    "mla_absorb_q", "mla_decode_attn", "mla_combine", "mla_out_up", "mla_combine_out_up",
     "mla_check_decode_inputs_host",
 )
 
@@ -67,6 +67,7 @@ def _load():
         "mla_decode_attn": ([cfgp, P, P, P, I64, P, I32, P, P, I32, I32, planp, P, SZ, P, P, P], I32),
         "mla_combine": ([cfgp, P, SZ, P, I32, I32, planp, P, P, P], I32),
         "mla_out_up": ([cfgp, P, P, P, I32, P], I32),
+        "mla_combine_out_up": ([cfgp, P, SZ, P, I32, I32, planp, P, P, P, P], I32),
         "mla_check_decode_inputs_host": ([cfgp, I32, i32p, i32p, I32, I64, i32p, I32, i32p], I32),
     }
     for name, (args, res) in sig.items():
@@ -214,6 +215,20 @@ def mla_combine(cfg: MlaConfig, workspace, seq_lens, plan: MlaPlan, o_lat, lse_o
                           _dev(seq_lens, "seq_lens", torch.int32, (B,)), int(topk), B, ctypes.byref(plan),
                           _dev(o_lat, "o_lat", dt, (B, cfg.num_heads, cfg.d_latent)), lp, _stream(stream))
     _check("mla_combine", st)
+
+
+def mla_combine_out_up(cfg: MlaConfig, workspace, seq_lens, plan: MlaPlan, w_uv, out, lse_out=None, topk: int = 0,
+                       stream=None):
+    torch = _torch()
+    B = out.shape[0]
+    dt = _act(cfg)
+    H, DC, DV = cfg.num_heads, cfg.d_latent, cfg.d_v
+    lp = _dev(lse_out, "lse_out", torch.float32, (B, H)) if lse_out is not None else None
+    st = _lib.mla_combine_out_up(ctypes.byref(cfg), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                                 _dev(seq_lens, "seq_lens", torch.int32, (B,)), int(topk), B, ctypes.byref(plan),
+                                 _dev(w_uv, "w_uv", dt, (H, DV, DC)), _dev(out, "out", dt, (B, H, DV)), lp,
+                                 _stream(stream))
+    _check("mla_combine_out_up", st)
 
 
 def mla_check_decode_inputs_host(cfg: MlaConfig, seq_lens, block_table, num_pages: int, topk_idx=None):

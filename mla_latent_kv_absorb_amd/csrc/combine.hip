@@ -51,97 +51,129 @@ __device__ __forceinline__ void load8(const PT* src, f32x4& lo, f32x4& hi) {
   }
 }
 
+// Merge plan of one (request b, head h): which workers hold partials of b and
+// the normalised merge weights, one candidate partial per lane (64 per chunk).
+struct MergePlan {
+  int64_t p_first, W, P;
+  int32_t np, nchunks;
+  float mref, inv, tot;
+  const float* lse_col;  // slot s: lse_col[s * H]
+  int H;
+  bool some_empty;
+
+  __device__ __forceinline__ void init(const CombineArgs& a, int32_t b, int h) {
+    // units of the split space (each request: its lead, then its tiles)
+    init(a, b, h, spans_below(a.seq_lens, a.batch, a.topk), spans_below(a.seq_lens, b, a.topk));
+  }
+  // the same, given W and the units below request b
+  __device__ __forceinline__ void init(const CombineArgs& a, int32_t b, int h, int64_t W_, int64_t below) {
+    W = W_;
+    const int64_t start = below + kLeadTiles;  // first tile of request b
+    const int32_t nt_b = a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[b]);
+    P = a.num_workers;
+    H = a.H;
+    p_first = 0;
+    int64_t p_last = -1;
+    if (nt_b > 0) {
+      p_first = worker_of(start, W, P);
+      p_last = worker_of(start + nt_b - 1, W, P);
+    }
+    np = (int32_t)(p_last - p_first + 1);  // candidate partials (some workers may be empty)
+    nchunks = (np + 63) / 64;
+    lse_col = a.part_lse + (int64_t)b * a.H + h;
+    // Workers are empty only when there are fewer units than workers; then
+    // p * W < P * P and the test needs no 64-bit division.
+    some_empty = W < P;
+    float mx = -INFINITY;
+    for (int32_t c = 0; c < nchunks; ++c) mx = fmaxf(mx, lane_lse(c));
+    mx = wave_max(mx);
+    mref = (mx == -INFINITY) ? 0.f : mx;
+    float t = 0.f;
+    for (int32_t c = 0; c < nchunks; ++c) {
+      const float l = lane_lse(c);
+      t += (l == -INFINITY) ? 0.f : expf(l - mref);
+    }
+    tot = wave_sum(t);
+    inv = tot > 0.f ? 1.0f / tot : 0.f;
+  }
+  // lse of partial p_first + 64c + lane; an empty worker wrote nothing and
+  // counts as lse = -inf
+  __device__ __forceinline__ float lane_lse(int32_t c) const {
+    const int64_t p = p_first + 64 * c + __lane_id();
+    if (p >= p_first + np) return -INFINITY;
+    if (some_empty) {
+      const uint32_t pw = (uint32_t)p * (uint32_t)W, p32 = (uint32_t)P;
+      if (pw / p32 == (pw + (uint32_t)W) / p32) return -INFINITY;
+    }
+    return lse_col[p * H];
+  }
+  __device__ __forceinline__ float lse() const { return tot > 0.f ? mref + logf(tot) : -INFINITY; }
+};
+
+// Weighted sum over the partials of columns d0 .. d0 + 7 (VEC) or column d0
+// of row0 + p * row_stride.  Every lane must take part (the weights are read
+// from other lanes with readlane).
+template <typename PT, bool VEC>
+__device__ __forceinline__ void merge_cols(const MergePlan& m, const PT* row0, int64_t row_stride, int d0,
+                                           f32x4& acc0, f32x4& acc1, float& acc) {
+  acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc1 = acc0;
+  acc = 0.f;
+  for (int32_t c = 0; c < m.nchunks; ++c) {
+    const float l = m.lane_lse(c);
+    const float wl = (l == -INFINITY) ? 0.f : expf(l - m.mref) * m.inv;  // lane's weight
+    const int32_t n = m.np - 64 * c < 64 ? m.np - 64 * c : 64;
+    for (int32_t j = 0; j < n; j += kUnroll) {
+      // issue every load of the group first; slots past the end are
+      // clamped to a valid slot and get weight 0 (selected away, so
+      // whatever an empty worker's slot holds never reaches the sum)
+      f32x4 v0[kUnroll], v1[kUnroll];
+      float vs[kUnroll], wg[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int32_t jj = j + u < n ? j + u : n - 1;
+        wg[u] = j + u < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), jj)) : 0.f;
+        const int64_t p = m.p_first + 64 * c + jj;
+        const PT* src = row0 + p * row_stride + d0;
+        if (VEC) load8(src, v0[u], v1[u]);
+        else vs[u] = (float)src[0];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float w = wg[u];
+        if (VEC) {
+          acc0 += w == 0.f ? f32x4{0.f, 0.f, 0.f, 0.f} : w * v0[u];
+          acc1 += w == 0.f ? f32x4{0.f, 0.f, 0.f, 0.f} : w * v1[u];
+        } else {
+          acc += w == 0.f ? 0.f : w * vs[u];
+        }
+      }
+    }
+  }
+}
+
 // PT: partial element type (__bf16 or float); VEC: 8 columns per lane.
 template <typename PT, bool VEC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int32_t b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.x * kWaves + (threadIdx.x >> 6);
-
-  // units of the split space (each request: its lead, then its tiles)
-  const int64_t W = spans_below(a.seq_lens, a.batch, a.topk);
-  const int64_t start = spans_below(a.seq_lens, b, a.topk) + kLeadTiles;  // first tile of request b
-  const int32_t nt_b = a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[b]);
   if (h >= a.H) return;
-  const int64_t P = a.num_workers;
-  int64_t p_first = 0, p_last = -1;
-  if (nt_b > 0) {
-    p_first = worker_of(start, W, P);
-    p_last = worker_of(start + nt_b - 1, W, P);
-  }
-  const int32_t np = (int32_t)(p_last - p_first + 1);  // candidate partials (some workers may be empty)
-  const float* lse_col = a.part_lse + (int64_t)b * a.H + h;  // slot s: lse_col[s * H]
-
-  // Merge weights.  Lane i looks after partial p_first + 64c + i of chunk c;
-  // an empty worker wrote nothing and counts as lse = -inf.
-  // Workers are empty only when there are fewer tiles than workers; then
-  // p * W < P * P and the test needs no 64-bit division.
-  const bool some_empty = W < P;
-  auto lane_lse = [&](int32_t c) -> float {
-    const int64_t p = p_first + 64 * c + lane;
-    if (p > p_last) return -INFINITY;
-    if (some_empty) {
-      const uint32_t pw = (uint32_t)p * (uint32_t)W, p32 = (uint32_t)P;
-      if (pw / p32 == (pw + (uint32_t)W) / p32) return -INFINITY;
-    }
-    return lse_col[p * a.H];
-  };
-  const int32_t nchunks = (np + 63) / 64;
-  float mx = -INFINITY;
-  for (int32_t c = 0; c < nchunks; ++c) mx = fmaxf(mx, lane_lse(c));
-  mx = wave_max(mx);
-  const float mref = (mx == -INFINITY) ? 0.f : mx;
-  float tot = 0.f;
-  for (int32_t c = 0; c < nchunks; ++c) {
-    const float l = lane_lse(c);
-    tot += (l == -INFINITY) ? 0.f : expf(l - mref);
-  }
-  tot = wave_sum(tot);
-  const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+  MergePlan m;
+  m.init(a, b, h);
   const int64_t dst = ((int64_t)b * a.H + h) * a.D_C;
   const int64_t row_stride = (int64_t)a.H * a.D_C;  // elements between slots
-  const PT* row0 = (const PT*)a.part_o + ((int64_t)b * a.H + h) * a.D_C;  // worker p's row (slot p + b): row0 + p * row_stride
+  // worker p's row (slot p + b): row0 + p * row_stride
+  const PT* row0 = (const PT*)a.part_o + ((int64_t)b * a.H + h) * a.D_C;
 
-  // Every lane runs every iteration (the weights are read from other lanes
-  // with readlane, so no lane may sit out); lanes past the row end load a
-  // valid column and skip the store.
+  // lanes past the row end load a valid column and skip the store
   for (int dbase = 0; dbase < a.D_C; dbase += VEC ? 512 : 64) {
     const int dl = dbase + (VEC ? lane * 8 : lane);
     const bool act = dl < a.D_C;
     const int d0 = act ? dl : 0;
-    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-    float acc = 0.f;
-    for (int32_t c = 0; c < nchunks; ++c) {
-      const float l = lane_lse(c);
-      const float wl = (l == -INFINITY) ? 0.f : expf(l - mref) * inv;  // lane's weight
-      const int32_t n = np - 64 * c < 64 ? np - 64 * c : 64;
-      for (int32_t j = 0; j < n; j += kUnroll) {
-        // issue every load of the group first; slots past the end are
-        // clamped to a valid slot and get weight 0 (selected away, so
-        // whatever an empty worker's slot holds never reaches the sum)
-        f32x4 v0[kUnroll], v1[kUnroll];
-        float vs[kUnroll], wg[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int32_t jj = j + u < n ? j + u : n - 1;
-          wg[u] = j + u < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), jj)) : 0.f;
-          const int64_t p = p_first + 64 * c + jj;  // its slot is p + b
-          const PT* src = row0 + p * row_stride + d0;
-          if (VEC) load8(src, v0[u], v1[u]);
-          else vs[u] = (float)src[0];
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const float w = wg[u];
-          if (VEC) {
-            acc0 += w == 0.f ? f32x4{0.f, 0.f, 0.f, 0.f} : w * v0[u];
-            acc1 += w == 0.f ? f32x4{0.f, 0.f, 0.f, 0.f} : w * v1[u];
-          } else {
-            acc += w == 0.f ? 0.f : w * vs[u];
-          }
-        }
-      }
-    }
+    f32x4 acc0, acc1;
+    float acc;
+    merge_cols<PT, VEC>(m, row0, row_stride, d0, acc0, acc1, acc);
     if (!act) continue;
     if (VEC) {
       if (a.out_bf16) {
@@ -162,8 +194,108 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
       else ((float*)a.o_lat)[dst + d0] = acc;
     }
   }
-  if (a.lse_out != nullptr && lane == 0)
-    a.lse_out[(int64_t)b * a.H + h] = tot > 0.f ? mref + logf(tot) : -INFINITY;
+  if (a.lse_out != nullptr && lane == 0) a.lse_out[(int64_t)b * a.H + h] = m.lse();
+}
+
+// ---- merge and value up-projection in one launch (V2 dims, BF16) ----
+// Work-group (head h, 32 requests), 16 waves: each wave merges two requests'
+// partials of head h into BF16 rows in LDS (the same arithmetic as
+// combine_kernel, rounded to BF16 as o_lat would be); then waves 0..3 each
+// multiply 32 rows of W_UV[h] (128 x 512) by the 32 rows on MFMA 32x32x16:
+// out^T[m][b] = sum_k W_UV[h][m][k] o[b][k] ("DeepSeek's KV Cache",
+// Figure 6, form (2)).  The merged latent never goes to HBM.
+constexpr int kCuThreads = 1024;
+constexpr int kCuWaves = kCuThreads / 64;
+constexpr int kCuReq = 32;                // requests per work-group (MFMA N)
+constexpr int kCuRow = kLatent * 2 + 16;  // LDS row pitch in bytes (padded against bank conflicts)
+constexpr int kDv = 128;
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+
+__global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u) {
+  __shared__ __attribute__((aligned(16))) char olds[kCuReq * kCuRow];
+  __shared__ int64_t below_s[kCuReq + 1];  // units below each request of the group; [kCuReq] = total
+  const CombineArgs& a = u.c;
+  const int h = blockIdx.x;
+  const int32_t b0 = blockIdx.y * kCuReq;
+  const int32_t nb = a.batch - b0 < kCuReq ? a.batch - b0 : kCuReq;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int64_t row_stride = (int64_t)kHeads * kLatent;
+
+  if (wv == 0) {
+    // exclusive prefix of the request spans, once for the whole group
+    int64_t off = 0;
+    for (int32_t base = 0; base < a.batch; base += 64) {
+      const int32_t r = base + lane;
+      const int64_t sp = r < a.batch ? span_of(a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[r])) : 0;
+      int64_t incl = sp;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int64_t up = __shfl_up(incl, d);
+        if (lane >= d) incl += up;
+      }
+      if (r >= b0 && r < b0 + kCuReq) below_s[r - b0] = off + incl - sp;
+      off += __shfl(incl, 63);
+    }
+    if (lane == 0) below_s[kCuReq] = off;
+  }
+  __syncthreads();
+
+  for (int bl = wv; bl < kCuReq; bl += kCuWaves) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)0.f;
+    if (bl < nb) {  // wave-uniform
+      const int32_t b = b0 + bl;
+      MergePlan m;
+      m.init(a, b, h, below_s[kCuReq], below_s[bl]);
+      const __bf16* row0 = (const __bf16*)a.part_o + ((int64_t)b * kHeads + h) * kLatent;
+      f32x4 acc0, acc1;
+      float acc;
+      merge_cols<__bf16, true>(m, row0, row_stride, 8 * lane, acc0, acc1, acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = (__bf16)acc0[e];
+        o[4 + e] = (__bf16)acc1[e];
+      }
+      if (a.lse_out != nullptr && lane == 0) a.lse_out[(int64_t)b * kHeads + h] = m.lse();
+    }
+    *(bf16x8*)(olds + bl * kCuRow + 16 * lane) = o;
+  }
+  __syncthreads();
+  if (wv >= kDv / 32) return;
+
+  // A: W_UV[h] rows 32 wv + (lane % 32), 8 columns per lane per K-block;
+  // B: merged row (lane % 32), the same 8 columns
+  const __bf16* wp = (const __bf16*)u.w_uv + ((int64_t)h * kDv + 32 * wv + (lane & 31)) * kLatent + 8 * (lane >> 5);
+  const char* op = olds + (lane & 31) * kCuRow + 16 * (lane >> 5);
+  f32x16 acc = f32x16{};
+  constexpr int U = 8;
+#pragma unroll
+  for (int kk = 0; kk < kLatent / 16; kk += U) {
+    bf16x8 av[U], bv[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      av[i] = *(const bf16x8*)(wp + 16 * (kk + i));
+      bv[i] = *(const bf16x8*)(op + 32 * (kk + i));
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[i], acc, 0, 0, 0);
+  }
+  // lane holds rows m = 32 wv + 8 g + 4 (lane / 32) + e of request lane % 32
+  const int bl = lane & 31;
+  if (bl < nb) {
+    __bf16* y = (__bf16*)u.out + ((int64_t)(b0 + bl) * kHeads + h) * kDv + 32 * wv + 4 * (lane >> 5);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * g + e];
+      *(bf16x4*)(y + 8 * g) = v;
+    }
+  }
 }
 
 }  // namespace
@@ -177,6 +309,13 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     if (a.D_C % 8 == 0) hipLaunchKernelGGL((combine_kernel<float, true>), grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((combine_kernel<float, false>), grid, dim3(kThreads), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_up(const CombineUpArgs& u, hipStream_t s) {
+  // V2 dims, BF16 partials and output (checked by the caller)
+  const dim3 grid(kHeads, (u.c.batch + kCuReq - 1) / kCuReq);
+  hipLaunchKernelGGL(combine_up_kernel, grid, dim3(kCuThreads), 0, s, u);
   return hipGetLastError();
 }
 

@@ -252,6 +252,39 @@ mla_status mla_combine(const mla_config* cfg, const void* workspace, size_t work
   return launch_status(mla::launch_combine(a, (hipStream_t)stream));
 }
 
+mla_status mla_combine_out_up(const mla_config* cfg, const void* workspace, size_t workspace_bytes,
+                              const int32_t* seq_lens, int32_t topk, int32_t batch, const mla_plan* plan,
+                              const void* w_uv, void* out, float* lse_out, void* stream) {
+  Path path;
+  mla_status st = check_config(cfg, &path);
+  if (st != MLA_OK) return st;
+  if (workspace == nullptr || seq_lens == nullptr || plan == nullptr || w_uv == nullptr || out == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  if (batch < 1 || batch > 65535 || topk < 0 || plan->num_workers < 1 || plan->num_workers > kMaxWorkers)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(workspace, 16) || !aligned(w_uv, 16) || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
+    return MLA_ERR_INVALID_ARG;
+  const int64_t slots = (int64_t)plan->num_workers + batch - 1;
+  if (workspace_bytes < workspace_bytes_for(cfg, slots)) return MLA_ERR_INVALID_ARG;
+  if (path == Path::kF32 || cfg->d_v != 128) return MLA_ERR_UNSUPPORTED;  // H, D_C fixed by the MFMA paths
+  mla::CombineUpArgs u{};
+  u.c.part_o = workspace;
+  u.c.part_lse = (const float*)((const char*)workspace + al16((size_t)slots * cfg->num_heads * cfg->d_latent * 4));
+  u.c.part_bf16 = partials_bf16(path);
+  u.c.seq_lens = seq_lens;
+  u.c.topk = topk;
+  u.c.batch = batch;
+  u.c.num_workers = plan->num_workers;
+  u.c.o_lat = nullptr;
+  u.c.lse_out = lse_out;
+  u.c.H = cfg->num_heads;
+  u.c.D_C = cfg->d_latent;
+  u.c.out_bf16 = 1;
+  u.w_uv = w_uv;
+  u.out = out;
+  return launch_status(mla::launch_combine_up(u, (hipStream_t)stream));
+}
+
 mla_status mla_check_decode_inputs_host(const mla_config* cfg, int32_t batch, const int32_t* seq_lens,
                                         const int32_t* block_table, int32_t block_table_stride,
                                         int64_t num_pages, const int32_t* topk_idx, int32_t topk,

@@ -53,6 +53,13 @@ struct CombineArgs {
   int32_t out_bf16;
 };
 
+// merge + value up-projection in one launch
+struct CombineUpArgs {
+  CombineArgs c;            // o_lat unused
+  const void* w_uv;         // [H][D_V][D_C] BF16
+  void* out;                // [batch][H][D_V] BF16
+};
+
 struct HeadGemmArgs {
   // y[b][h][m] = sum_k w[h][m][k] * x[b][h][k]
   const void* x;
@@ -65,6 +72,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);  // BF16 cache, dense
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_combine_up(const CombineUpArgs& u, hipStream_t s);  // V2 dims, BF16
 hipError_t launch_head_gemm_bf16(const HeadGemmArgs& a, hipStream_t s);
 hipError_t launch_head_gemm_f32(const HeadGemmArgs& a, hipStream_t s);
 

@@ -96,11 +96,23 @@ class DeviceWorkload:
     def up(self, stream=None):
         B.mla_out_up(self.cfg, self.o_lat, self.w_uv, self.out, stream)
 
+    def combine_up(self, stream=None):
+        """Merge and up-projection in one launch (split mode, BF16 V2 dims);
+        o_lat is not written."""
+        B.mla_combine_out_up(self.cfg, self.workspace, self.seq_lens, self.plan, self.w_uv, self.out,
+                             lse_out=self.lse, topk=self.topk, stream=stream)
+
     def step(self, stream=None):
         self.absorb(stream)
         self.attend(stream)
         self.combine(stream)
         self.up(stream)
+
+    def step_fused(self, stream=None):
+        """The same step with the merge and the up-projection in one launch."""
+        self.absorb(stream)
+        self.attend(stream)
+        self.combine_up(stream)
 
     def partials(self):
         """(o_part [slots, H, D_C], lse_part [slots, H]) of the workspace (split

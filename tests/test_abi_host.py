@@ -105,6 +105,15 @@ def test_invalid_arguments_rejected_before_launch(B):
     args4[13] = 100
     assert lib.mla_decode_attn(*args4) == B.MLA_ERR_INVALID_ARG
     assert lib.mla_combine(ctypes.byref(cfg), q, 100, q, 0, 1, ctypes.byref(plan), q, None, None) == B.MLA_ERR_INVALID_ARG
+    # fused merge + up-projection: null weights, too small workspace, float32 config
+    big = 1 << 30
+    assert lib.mla_combine_out_up(ctypes.byref(cfg), q, big, q, 0, 1, ctypes.byref(plan), None, q, None,
+                                  None) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine_out_up(ctypes.byref(cfg), q, 100, q, 0, 1, ctypes.byref(plan), q, q, None,
+                                  None) == B.MLA_ERR_INVALID_ARG
+    tiny = B.make_config(4, 16, 8, 8, 8, 0.25, B.MLA_F32, B.MLA_F32)
+    assert lib.mla_combine_out_up(ctypes.byref(tiny), q, big, q, 0, 1, ctypes.byref(plan), q, q, None,
+                                  None) == B.MLA_ERR_UNSUPPORTED
 
 
 def test_host_metadata_check(B):

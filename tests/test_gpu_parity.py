@@ -204,6 +204,32 @@ def test_v2_absorb_and_up_projection_alone(torch, R, v2_ragged):
     assert_close(to_np(w.out), oracle.up_project(x, inp.w_uv), what="out_up")
 
 
+@pytest.mark.parametrize("batch", [3, 37])
+def test_v2_fused_combine_up(torch, R, batch):
+    """mla_combine_out_up: against the oracle, and against mla_combine then
+    mla_out_up on the same partials.  The merge is the same code, so lse is
+    bit-identical; out may differ in the last BF16 bit (GEMM summation order).
+    37 requests span two request blocks of the fused kernel, the second one
+    partial."""
+    _log(f"fused merge + up-projection, batch {batch}")
+    inp = I.make_inputs("v2_batched", seed=31, batch=batch, ctx=(40, 900))
+    for nw in (None, 7):
+        w = R.DeviceWorkload(inp, split=True, num_workers=nw)
+        w.step()
+        torch.cuda.synchronize()
+        out_sep, lse_sep = w.out.clone(), w.lse.clone()
+        w.out.zero_()
+        w.lse.zero_()
+        w.combine_up()
+        torch.cuda.synchronize()
+        assert torch.equal(w.lse, lse_sep)
+        assert_close(to_np(w.out), to_np(out_sep), tol_rel=1e-2, what=f"fused vs separate, workers {nw}")
+        out = to_np(w.out)
+        for b in sorted({0, batch // 2, batch - 1}):
+            r_out, _, _ = oracle_request(inp, b)
+            assert_close(out[b], r_out, what=f"fused out b={b} workers {nw}")
+
+
 def test_v2_topk_all_positions_equals_dense(torch, R):
     _log("topk == dense")
     dense = I.make_inputs("v2_batched", seed=12, seq_lens=[300, 129])
