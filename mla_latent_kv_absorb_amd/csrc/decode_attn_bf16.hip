@@ -245,6 +245,46 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     }
   };
 
+  // Normalised accumulator (times inv) of this wave's 32 heads as BF16 rows
+  // [32][512] at dst.  Every stand-in load must have landed and every wave
+  // must have finished reading the stages before they are reused here; the
+  // next segment drains and synchronises again before loading into them.
+  auto store_rows_staged = [&](__bf16* dst, float inv) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    constexpr int kPitch = kCRow + 16;  // padded rows: the row-wise writes spread over the banks
+    LDS char* mine = L + w * 32 * kPitch;
+    LDS char* rowL = mine + row * kPitch;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    // lane (row, hi) holds columns 32 mb + 8 g + 4 hi + e; the two lanes of a
+    // row swap half of each group pair so each writes 16 contiguous bytes
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int g0 = 2 * k, g1 = 2 * k + 1;
+        uint32_t keep[2], send[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bf16x2 k0 = {(__bf16)(O[mb][4 * g0 + 2 * e] * inv), (__bf16)(O[mb][4 * g0 + 2 * e + 1] * inv)};
+          const bf16x2 k1 = {(__bf16)(O[mb][4 * g1 + 2 * e] * inv), (__bf16)(O[mb][4 * g1 + 2 * e + 1] * inv)};
+          const uint32_t u0 = __builtin_bit_cast(uint32_t, k0), u1 = __builtin_bit_cast(uint32_t, k1);
+          keep[e] = hi ? u1 : u0;
+          send[e] = hi ? u0 : u1;
+        }
+        uint32_t recv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) recv[e] = __float_as_uint(wave_partner(__uint_as_float(send[e])));
+        const i32x4 v = hi ? i32x4{(int)recv[0], (int)recv[1], (int)keep[0], (int)keep[1]}
+                           : i32x4{(int)keep[0], (int)keep[1], (int)recv[0], (int)recv[1]};
+        *(LDS i32x4*)(rowL + 2 * (32 * mb + 8 * (hi ? g1 : g0))) = v;
+      }
+    // each wave reads back only its own rows: no barrier needed
+#pragma unroll
+    for (int r = 0; r < 32; ++r)
+      *(i32x4*)(dst + r * kLatent + 8 * lane) = *(const LDS i32x4*)(mine + r * kPitch + 16 * lane);
+  };
+
   int32_t cb = b0;
   int64_t cv = v0;   // offset of the next unit inside request cb's span
   int64_t done = 0;  // units consumed
@@ -269,6 +309,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     // earlier stores and loads count on vmcnt too, so drain first.
     wait_vmcnt<0>();
     __syncthreads();
+    // Page ids are fetched one tile ahead of the load that needs them.  Every
+    // iteration loads one tile (past the segment end a stand-in from page 0
+    // that nothing reads), so each wait is the same vmcnt count.  The first
+    // two tiles are loaded before the queries, so the two latencies overlap.
+    int32_t pg_a = ld.page_of(ct >> 1);                                     // tile ct
+    int32_t pg_b = seg > 1 ? ld.page_of((ct + 1) >> 1) : -1;               // tile ct + 1
+    ld.issue(0, ct, pg_a);
+    ld.issue(1, ct + 1, pg_b);
+    // page of tile ct + 2: loaded now, checked when its load is issued
+    int32_t pg_next_p = seg > 2 ? (ct + 2) >> 1 : INT32_MAX;
+    int32_t pg_next_raw = ld.raw(seg > 2 ? pg_next_p : 0);
+    // validity of the tiles in flight, by stage: tile ct + j has stage j % 4
+    bool valid_j = pg_a >= 0, valid_j1 = pg_b >= 0;
     {
       const __bf16* ql = (const __bf16*)a.q_lat + ((int64_t)cb * kHeads + head) * kLatent + 8 * hi;
 #pragma unroll
@@ -293,20 +346,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
 #pragma unroll
       for (int v = 0; v < 8; ++v) *(LDS i32x4*)(dst + 16 * v) = i32x4{0, 0, 0, 0};
     }
-    wait_vmcnt<0>();
+    wait_vmcnt<0>();  // queries and the first two tiles
 
-    // page ids, fetched one tile ahead of the load that needs them
-    // Every iteration loads one tile (past the segment end a stand-in from
-    // page 0 that nothing reads), so each wait is the same vmcnt count.
-    int32_t pg_a = ld.page_of(ct >> 1);                                     // tile ct
-    int32_t pg_b = seg > 1 ? ld.page_of((ct + 1) >> 1) : -1;               // tile ct + 1
-    ld.issue(0, ct, pg_a);
-    ld.issue(1, ct + 1, pg_b);
-    // page of tile ct + 2: loaded now, checked when its load is issued
-    int32_t pg_next_p = seg > 2 ? (ct + 2) >> 1 : INT32_MAX;
-    int32_t pg_next_raw = ld.raw(seg > 2 ? pg_next_p : 0);
-    // validity of the tiles in flight, by stage: tile ct + j has stage j % 4
-    bool valid_j = pg_a >= 0, valid_j1 = pg_b >= 0;
 
 #pragma unroll
     for (int mb = 0; mb < 16; ++mb) O[mb] = f32x16{};
@@ -435,23 +476,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
       const float l_tot = l_run + wave_partner(l_run);
       const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
       const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      // BF16 rows of this wave's 32 heads (the final o_lat, or the partial:
+      // partials of the MFMA kernels are BF16), staged through LDS so that
+      // every global store writes one contiguous 1 KiB row
+      const int64_t slot = worker + cb;
+      __bf16* rows = DIRECT ? (__bf16*)a.o_lat + (int64_t)cb * kHeads * kLatent
+                            : (__bf16*)a.part_o + slot * kHeads * kLatent;
+      store_rows_staged(rows + (int64_t)32 * w * kLatent, inv);
       if (DIRECT) {
-        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-        __bf16* o = (__bf16*)a.o_lat + ((int64_t)cb * kHeads + head) * kLatent + 4 * hi;
-#pragma unroll
-        for (int mb = 0; mb < 16; ++mb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            bf16x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(O[mb][4 * g + e] * inv);
-            *(bf16x4*)(o + 32 * mb + 8 * g) = v;
-          }
         if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
       } else {
-        // partials of the MFMA kernels are BF16
-        const int64_t slot = worker + cb;
-        store_row_bf16((__bf16*)a.part_o + (slot * kHeads + head) * kLatent, O, inv);
         if (hi == 0) a.part_lse[slot * kHeads + head] = lse;
       }
     }
