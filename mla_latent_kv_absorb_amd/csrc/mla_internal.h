@@ -95,7 +95,7 @@ size_t decode_f32_lds_bytes(int H, int D_C, int D_R);
 // and b never both stay the same from one piece to the next.
 // ---------------------------------------------------------------------------
 namespace mla {
-constexpr int32_t kLeadTiles = 16;
+constexpr int32_t kLeadTiles = 12;
 __host__ __device__ inline int64_t worker_lo(int64_t p, int64_t W, int64_t P) { return (p * W) / P; }
 // Worker whose range contains unit x (0 <= x < W).
 __host__ __device__ inline int64_t worker_of(int64_t x, int64_t W, int64_t P) {
