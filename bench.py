@@ -16,7 +16,8 @@ the timed region), the float64 CPU oracle timed on whole requests of the
 same workload on the host cores (about 15 s of work), each launch's time with
 the matrix-core utilisation of the attention and the weight rate of the two
 head GEMMs ("parts"), and a plain streaming read for reference.  --long adds
-one layer of the long-context workload (1 request x 131,072 positions).
+one layer of the long-context workload (1 request x 131,072 positions);
+--fp8-topk adds the FP8-cache, top-2,048 workload.
 """
 
 from __future__ import annotations
@@ -147,6 +148,51 @@ def long_context_layer(torch, I, runner, num_cus, layers=4, reps=8):
             "tokens_per_s_60_layers": round(1e6 / (60 * us), 1), "workers": ws[0].plan.num_workers}
 
 
+def fp8_topk_step(torch, I, runner, num_cus, lists=8, reps=10):
+    """The FP8-cache workload with a top-2,048 index list per request.  One
+    step reads 42 MB out of a 1.35 GB pool, which would otherwise stay in the
+    last-level cache, so the steps cycle over `lists` independently drawn
+    index-list sets (338 MB of distinct rows).  Reports the step and attention
+    times, the cache rate and both roofline fractions (HBM, and BF16 matrix
+    cores: the FP8 latent is widened to BF16 for the MFMAs)."""
+    inp = I.make_inputs("v2_fp8_topk")
+    w = runner.DeviceWorkload(inp, split=True, num_cus=num_cus)
+    rng = np.random.default_rng(5005)
+    sets = []
+    for _ in range(lists):
+        idx = np.stack([np.sort(rng.choice(int(inp.seq_lens[b]), inp.topk_idx.shape[1], replace=False))
+                        for b in range(inp.B)]).astype(np.int32)
+        sets.append(torch.from_numpy(idx).to(w.topk_idx.device))
+    cache_bytes = I.cache_bytes_read(inp)
+    n_pos = int(np.sum(inp.topk_idx >= 0))
+    flop = float(n_pos) * 2 * inp.H * (inp.D_C + inp.D_R + inp.D_C)
+    for t in sets:
+        w.topk_idx = t
+        w.step_fused()
+    torch.cuda.synchronize()
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    att = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * lists)]
+    step_ev[0].record()
+    for r in range(reps):
+        for i, t in enumerate(sets):
+            w.topk_idx = t
+            w.absorb()
+            att[r * lists + i][0].record()
+            w.attend()
+            att[r * lists + i][1].record()
+            w.combine_up()
+    step_ev[1].record()
+    torch.cuda.synchronize()
+    step_us = step_ev[0].elapsed_time(step_ev[1]) * 1e3 / (reps * lists)
+    attn_us = float(np.mean([a.elapsed_time(b) for a, b in att])) * 1e3
+    return {"step_us": round(step_us, 2), "attn_us": round(attn_us, 2),
+            "cache_bytes_per_step": int(cache_bytes),
+            "attn_cache_GBps": round(cache_bytes / (attn_us * 1e-6) / 1e9, 1),
+            "attn_hbm_frac": round(cache_bytes / (attn_us * 1e-6) / (HBM_PEAK_GBPS * 1e9), 4),
+            "attn_mfma_util": round(flop / (attn_us * 1e-6) / BF16_PEAK_FLOPS, 4),
+            "tokens_per_s": round(inp.B / (step_us * 1e-6), 1), "workers": w.plan.num_workers}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +203,8 @@ def main():
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--long", action="store_true",
                     help="also time one layer of the long-context workload (1 request, 131,072 positions)")
+    ap.add_argument("--fp8-topk", action="store_true",
+                    help="also time the FP8-cache, top-2,048 workload (32 requests x 65,536 positions)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
@@ -238,6 +286,7 @@ def main():
     }
     ceiling = read_ceiling(torch)
     long_layer = long_context_layer(torch, I, runner, num_cus) if args.long else None
+    fp8 = fp8_topk_step(torch, I, runner, num_cus) if args.fp8_topk else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -285,6 +334,8 @@ def main():
     }
     if long_layer is not None:
         result["v2_long_layer"] = long_layer
+    if fp8 is not None:
+        result["fp8_topk_step"] = fp8
     print(json.dumps(result), flush=True)
 
 
