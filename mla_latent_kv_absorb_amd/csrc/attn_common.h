@@ -13,6 +13,8 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(2))) short s16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
 #define LDS __attribute__((address_space(3)))
@@ -65,7 +67,6 @@ __device__ __forceinline__ float wave_partner(float v) {
 // lanes of a head swap half of each pair of groups so that each lane owns 8
 // consecutive columns per store (32 stores per lane instead of 64).
 __device__ __forceinline__ void store_row_bf16(__bf16* row, const f32x16 (&O)[16], float inv) {
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const int hi = __lane_id() >> 5;
 #pragma unroll
   for (int mb = 0; mb < 16; ++mb)

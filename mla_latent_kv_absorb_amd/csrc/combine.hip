@@ -7,10 +7,11 @@
 // an exact identity.  Which slots hold request b's partials follows from the
 // same tile partition the attention kernel used (worker p writes slot p + b).
 //
-// One wave per (request, head): each lane owns 8 consecutive latent columns
-// (one 16-byte load per partial for BF16 partials, two for FP32), so a head
-// row of 512 values is one coalesced read per partial, and the loads of 8
-// partials are in flight together.  The merge weights are computed one
+// One wave per (request, head) -- or, for small batches, one work-group per
+// (request, head) with its partials split over the waves: each lane owns 8
+// consecutive latent columns (one 16-byte load per partial for BF16 partials,
+// two for FP32), so a head row of 512 values is one coalesced read per
+// partial, and the loads of 8 partials are in flight together.  The merge weights are computed one
 // partial per lane and read back with readlane.
 #include "tile_space.h"
 
@@ -113,17 +114,22 @@ struct MergePlan {
 // Weighted sum over the partials of columns d0 .. d0 + 7 (VEC) or column d0
 // of row0 + p * row_stride.  Every lane must take part (the weights are read
 // from other lanes with readlane).
+// Only candidate partials j_lo <= j < j_hi (indices from p_first) are summed;
+// the weights stay normalised over all of them, so sums over disjoint ranges
+// add up to the merge.
 template <typename PT, bool VEC>
 __device__ __forceinline__ void merge_cols(const MergePlan& m, const PT* row0, int64_t row_stride, int d0,
-                                           f32x4& acc0, f32x4& acc1, float& acc) {
+                                           f32x4& acc0, f32x4& acc1, float& acc, int32_t j_lo = 0,
+                                           int32_t j_hi = 0x7fffffff) {
   acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
   acc1 = acc0;
   acc = 0.f;
-  for (int32_t c = 0; c < m.nchunks; ++c) {
+  if (j_hi > m.np) j_hi = m.np;
+  for (int32_t c = j_lo >> 6; 64 * c < j_hi; ++c) {
     const float l = m.lane_lse(c);
     const float wl = (l == -INFINITY) ? 0.f : expf(l - m.mref) * m.inv;  // lane's weight
-    const int32_t n = m.np - 64 * c < 64 ? m.np - 64 * c : 64;
-    for (int32_t j = 0; j < n; j += kUnroll) {
+    const int32_t n = j_hi - 64 * c < 64 ? j_hi - 64 * c : 64;
+    for (int32_t j = j_lo - 64 * c > 0 ? j_lo - 64 * c : 0; j < n; j += kUnroll) {
       // issue every load of the group first; slots past the end are
       // clamped to a valid slot and get weight 0 (selected away, so
       // whatever an empty worker's slot holds never reaches the sum)
@@ -153,18 +159,27 @@ __device__ __forceinline__ void merge_cols(const MergePlan& m, const PT* row0, i
 }
 
 // PT: partial element type (__bf16 or float); VEC: 8 columns per lane.
-template <typename PT, bool VEC>
+// SPLIT: one (request, head) per work-group, its partials split into 4
+// contiguous ranges, one per wave, whose float32 sums are added in LDS (for
+// small batches, where one wave per (request, head) would leave most of the
+// chip idle and walk hundreds of partials serially).  Otherwise each wave
+// owns one head.
+template <typename PT, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+  __shared__ float red[SPLIT ? kWaves * 512 : 1];
   const int32_t b = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int h = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (h >= a.H) return;
+  const int wv = threadIdx.x >> 6;
+  const int h = SPLIT ? (int)blockIdx.x : (int)blockIdx.x * kWaves + wv;
+  if (!SPLIT && h >= a.H) return;
   MergePlan m;
   m.init(a, b, h);
   const int64_t dst = ((int64_t)b * a.H + h) * a.D_C;
   const int64_t row_stride = (int64_t)a.H * a.D_C;  // elements between slots
   // worker p's row (slot p + b): row0 + p * row_stride
   const PT* row0 = (const PT*)a.part_o + ((int64_t)b * a.H + h) * a.D_C;
+  const int32_t j_lo = SPLIT ? (int32_t)((int64_t)m.np * wv / kWaves) : 0;
+  const int32_t j_hi = SPLIT ? (int32_t)((int64_t)m.np * (wv + 1) / kWaves) : 0x7fffffff;
 
   // lanes past the row end load a valid column and skip the store
   for (int dbase = 0; dbase < a.D_C; dbase += VEC ? 512 : 64) {
@@ -173,7 +188,29 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     const int d0 = act ? dl : 0;
     f32x4 acc0, acc1;
     float acc;
-    merge_cols<PT, VEC>(m, row0, row_stride, d0, acc0, acc1, acc);
+    merge_cols<PT, VEC>(m, row0, row_stride, d0, acc0, acc1, acc, j_lo, j_hi);
+    if (SPLIT) {
+      // add the 4 waves' sums; wave 0 stores
+      if (VEC) {
+        *(f32x4*)(red + wv * 512 + 8 * lane) = acc0;
+        *(f32x4*)(red + wv * 512 + 8 * lane + 4) = acc1;
+      } else {
+        red[wv * 512 + lane] = acc;
+      }
+      __syncthreads();
+      if (wv == 0) {
+        for (int g = 1; g < kWaves; ++g) {
+          if (VEC) {
+            acc0 += *(const f32x4*)(red + g * 512 + 8 * lane);
+            acc1 += *(const f32x4*)(red + g * 512 + 8 * lane + 4);
+          } else {
+            acc += red[g * 512 + lane];
+          }
+        }
+      }
+      __syncthreads();  // red is reused by the next column block
+      if (wv != 0) continue;
+    }
     if (!act) continue;
     if (VEC) {
       if (a.out_bf16) {
@@ -194,13 +231,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
       else ((float*)a.o_lat)[dst + d0] = acc;
     }
   }
-  if (a.lse_out != nullptr && lane == 0) a.lse_out[(int64_t)b * a.H + h] = m.lse();
+  if (a.lse_out != nullptr && lane == 0 && (!SPLIT || wv == 0)) a.lse_out[(int64_t)b * a.H + h] = m.lse();
 }
 
 // ---- merge and value up-projection in one launch (V2 dims, BF16) ----
 // Work-group (head h, 32 requests), 16 waves: each wave merges two requests'
 // partials of head h into BF16 rows in LDS (the same arithmetic as
-// combine_kernel, rounded to BF16 as o_lat would be); then waves 0..3 each
+// combine_kernel, rounded to BF16 as o_lat would be).  With fewer than 16
+// requests in the group, the 16 / n waves of a request split its partials
+// into contiguous ranges and their float32 sums are added in LDS, so a lone
+// long request (hundreds of partials) is merged by all 16 waves.  Then waves
+// 0..3 each
 // multiply 32 rows of W_UV[h] (128 x 512) by the 32 rows on MFMA 32x32x16:
 // out^T[m][b] = sum_k W_UV[h][m][k] o[b][k] ("DeepSeek's KV Cache",
 // Figure 6, form (2)).  The merged latent never goes to HBM.
@@ -215,6 +256,7 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
 __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u) {
   __shared__ __attribute__((aligned(16))) char olds[kCuReq * kCuRow];
+  __shared__ __attribute__((aligned(16))) float red[kCuWaves * kLatent];  // per-wave sums (small groups)
   __shared__ int64_t below_s[kCuReq + 1];  // units below each request of the group; [kCuReq] = total
   const CombineArgs& a = u.c;
   const int h = blockIdx.x;
@@ -243,7 +285,42 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
   }
   __syncthreads();
 
-  for (int bl = wv; bl < kCuReq; bl += kCuWaves) {
+  const int G = nb >= kCuWaves ? 1 : kCuWaves / nb;  // waves per request
+  if (G > 1) {
+    // wave wv: request wv / G, partial range part wv % G of G
+    const int bl = wv / G, g = wv % G;
+    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    if (bl < nb) {  // wave-uniform
+      const int32_t b = b0 + bl;
+      MergePlan m;
+      m.init(a, b, h, below_s[kCuReq], below_s[bl]);
+      const __bf16* row0 = (const __bf16*)a.part_o + ((int64_t)b * kHeads + h) * kLatent;
+      const int32_t j_lo = (int32_t)((int64_t)m.np * g / G), j_hi = (int32_t)((int64_t)m.np * (g + 1) / G);
+      float acc;
+      merge_cols<__bf16, true>(m, row0, row_stride, 8 * lane, acc0, acc1, acc, j_lo, j_hi);
+      if (g == 0 && a.lse_out != nullptr && lane == 0) a.lse_out[(int64_t)b * kHeads + h] = m.lse();
+    }
+    *(f32x4*)(red + wv * kLatent + 8 * lane) = acc0;
+    *(f32x4*)(red + wv * kLatent + 8 * lane + 4) = acc1;
+    __syncthreads();
+    for (int r = wv; r < kCuReq; r += kCuWaves) {
+      f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+      if (r < nb) {
+        for (int gg = 0; gg < G; ++gg) {
+          s0 += *(const f32x4*)(red + (r * G + gg) * kLatent + 8 * lane);
+          s1 += *(const f32x4*)(red + (r * G + gg) * kLatent + 8 * lane + 4);
+        }
+      }
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = (__bf16)s0[e];
+        o[4 + e] = (__bf16)s1[e];
+      }
+      *(bf16x8*)(olds + r * kCuRow + 16 * lane) = o;
+    }
+  }
+  for (int bl = wv; G == 1 && bl < kCuReq; bl += kCuWaves) {
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (__bf16)0.f;
@@ -301,14 +378,22 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  const dim3 grid((a.H + kWaves - 1) / kWaves, a.batch);
+  // few (request, head) rows: split each one's partials over a work-group
+  const bool split = (int64_t)a.batch * a.H < 4096;
+  const dim3 grid(split ? a.H : (a.H + kWaves - 1) / kWaves, a.batch);
+#define MLA_COMBINE(PT, VEC)                                                                      \
+  do {                                                                                            \
+    if (split) hipLaunchKernelGGL((combine_kernel<PT, VEC, true>), grid, dim3(kThreads), 0, s, a); \
+    else hipLaunchKernelGGL((combine_kernel<PT, VEC, false>), grid, dim3(kThreads), 0, s, a);      \
+  } while (0)
   if (a.part_bf16) {
-    if (a.D_C % 8 == 0) hipLaunchKernelGGL((combine_kernel<__bf16, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<__bf16, false>), grid, dim3(kThreads), 0, s, a);
+    if (a.D_C % 8 == 0) MLA_COMBINE(__bf16, true);
+    else MLA_COMBINE(__bf16, false);
   } else {
-    if (a.D_C % 8 == 0) hipLaunchKernelGGL((combine_kernel<float, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<float, false>), grid, dim3(kThreads), 0, s, a);
+    if (a.D_C % 8 == 0) MLA_COMBINE(float, true);
+    else MLA_COMBINE(float, false);
   }
+#undef MLA_COMBINE
   return hipGetLastError();
 }
 

@@ -255,7 +255,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     constexpr int kPitch = kCRow + 16;  // padded rows: the row-wise writes spread over the banks
     LDS char* mine = L + w * 32 * kPitch;
     LDS char* rowL = mine + row * kPitch;
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     // lane (row, hi) holds columns 32 mb + 8 g + 4 hi + e; the two lanes of a
     // row swap half of each group pair so each writes 16 contiguous bytes
 #pragma unroll

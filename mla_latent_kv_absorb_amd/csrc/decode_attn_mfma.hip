@@ -316,34 +316,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         LDS char* Ct;   // BF16 latent tile (swizzled)
         LDS char* Rt = L + st * C::STAGE + C::C_STAGE;
         if (FP8) {
-          // E4M3 -> BF16 into the conversion buffer; masked rows become zeros.
+          // E4M3 -> BF16 into the conversion buffer (exact: every E4M3 value
+          // is a BF16 value); masked rows become zeros.  Each wave converts
+          // the 8 rows its own loads brought in: lane l takes bytes 8l .. 8l+7
+          // of a row (one 512-byte read across the wave) and writes their
+          // BF16 values as 16-byte chunk l of the swizzled row (one 1 KiB
+          // write), so neither side has bank conflicts.
           Ct = L + C::CONV_OFF;
-          const int r = tid >> 3, qq = tid & 7;
-          const LDS char* src = L + st * C::STAGE + r * kC8Row + 64 * qq;
-          LDS char* dst = Ct + r * kCRow;
-          const bool rv = (mask >> r) & 1;
-          const int rs = swz(r);
+          const LDS char* src = L + st * C::STAGE + 8 * w * kC8Row + 8 * lane;
+          const LDS float* scl = (const LDS float*)(L + st * C::STAGE + C::C_STAGE + C::R_STAGE);
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            i32x4 raw = *(const LDS i32x4*)(src + 16 * v4);
+          for (int k = 0; k < 8; ++k) {
+            const int r = 8 * w + k;
+            const i32x2 raw = *(const LDS i32x2*)(src + k * kC8Row);
+            const float sc = scl[r];
+            // E4M3 pairs -> exact float32 pairs, times the scale, one rounding to BF16
+            const f32x2 v[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(raw[0], false),
+                                __builtin_amdgcn_cvt_pk_f32_fp8(raw[0], true),
+                                __builtin_amdgcn_cvt_pk_f32_fp8(raw[1], false),
+                                __builtin_amdgcn_cvt_pk_f32_fp8(raw[1], true)};
+            i32x4 outv;
 #pragma unroll
-            for (int hc = 0; hc < 2; ++hc) {
-              i32x4 outv;
-#pragma unroll
-              for (int e = 0; e < 2; ++e) {
-                const int word = raw[2 * hc + e];
-                // exact: every E4M3 value is a BF16 value
-                const uint32_t u0 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 0)) >> 16;
-                const uint32_t u1 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 1)) >> 16;
-                const uint32_t u2 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 2)) >> 16;
-                const uint32_t u3 = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(word, 3)) >> 16;
-                outv[2 * e] = (int)(u0 | (u1 << 16));
-                outv[2 * e + 1] = (int)(u2 | (u3 << 16));
-              }
-              if (!rv) outv = i32x4{0, 0, 0, 0};
-              const int chunk = 8 * qq + 2 * v4 + hc;
-              *(LDS i32x4*)(dst + 16 * (chunk ^ rs)) = outv;
+            for (int e = 0; e < 4; ++e) {
+              const bf16x2 b = {(__bf16)(v[e][0] * sc), (__bf16)(v[e][1] * sc)};
+              outv[e] = __builtin_bit_cast(int, b);
             }
+            if (!((mask >> r) & 1)) outv = i32x4{0, 0, 0, 0};
+            *(LDS i32x4*)(Ct + r * kCRow + 16 * (lane ^ swz(r))) = outv;
           }
           __syncthreads();
         } else {
@@ -365,7 +364,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         // Operands are read SD blocks ahead into a register ring; scheduling
         // fences keep the order "MFMA k, then the read for k + SD" so the LDS
         // latency hides behind the MFMAs.
-        float tsc[16];
         f32x16 sacc = f32x16{};
         {
           constexpr int SD = 4;
@@ -379,18 +377,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int k = 0; k < 36; ++k) {
-            if (FP8 && k == 32) {
-              // the per-position scale multiplies the content score only
-              const LDS float* sc = (const LDS float*)(L + st * C::STAGE + C::C_STAGE + C::R_STAGE);
-#pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                f32x4 v = *(const LDS f32x4*)(sc + 8 * g + 4 * hi);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tsc[4 * g + e] = v[e];
-              }
-#pragma unroll
-              for (int r = 0; r < 16; ++r) sacc[r] *= tsc[r];
-            }
             const bf16x8 bq = k < 32 ? q[k] : qr[k - 32];
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[k % SD], bq, sacc, 0, 0, 0);
             if (k + SD < 36) ring[k % SD] = s_operand(k + SD);
@@ -435,8 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         for (int r = 0; r < 16; ++r) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, neg_m));
           lsum += p;
-          const float pw = FP8 ? p * tsc[r] : p;
-          P[r >> 3][r & 7] = (__bf16)pw;
+          P[r >> 3][r & 7] = (__bf16)p;
         }
         l_run += lsum;
 

@@ -121,10 +121,11 @@ mla_status mla_decode_plan(const mla_config* cfg, int32_t batch, const int32_t* 
     W += mla::tiles_of(len);
   }
   if (W < 1) W = 1;
-  // Enough tiles per worker that a partial (H x D_C values) stays small next
-  // to the cache bytes the worker reads, and no more workers than CUs: one
-  // 4-wave work-group fills a CU.
-  const int64_t kMinTilesPerWorker = 16;
+  // As many workers as CUs (one 4-wave work-group fills a CU), but at least
+  // two tiles each: a worker's fixed cost (queries, pipeline fill, partial
+  // write) is several tiles' worth, so short batches gain little from more,
+  // and each extra partial is read again by the merge.
+  const int64_t kMinTilesPerWorker = 2;
   int64_t P = (W + kMinTilesPerWorker - 1) / kMinTilesPerWorker;
   if (P > num_cus) P = num_cus;
   if (P > kMaxWorkers) P = kMaxWorkers;

@@ -60,13 +60,17 @@ def test_plan_sizes_workspace(B):
     lens = np.array([16384, 32768, 20000], dtype=np.int32)
     plan = B.mla_decode_plan(cfg, 3, lens, 0, 0, 256)
     tiles = int(np.sum((lens + 31) // 32))
-    assert plan.num_workers == min(256, -(-tiles // 16))
+    # one worker per CU, at least two tiles each
+    assert plan.num_workers == min(256, -(-tiles // 2))
     assert plan.num_slots == plan.num_workers + 2
     assert plan.workspace_bytes == plan.num_slots * 128 * 512 * 4 + (plan.num_slots * 128 * 4 + 15) // 16 * 16
     small = B.mla_decode_plan(cfg, 1, np.array([100], np.int32), 0, 0, 256)
-    assert small.num_workers == 1
+    assert small.num_workers == 2  # 4 tiles
+    single = B.mla_decode_plan(cfg, 1, np.array([4096], np.int32), 0, 0, 256)
+    assert single.num_workers == 64
     topk = B.mla_decode_plan(cfg, 32, None, 0, 2048, 256)
-    assert topk.num_workers == 128
+    assert topk.num_workers == 256
+    assert B.mla_decode_plan(cfg, 32, None, 0, 2048, 100).num_workers == 100
 
 
 def test_invalid_arguments_rejected_before_launch(B):

@@ -68,9 +68,19 @@ def check_step(torch, R, inp, split=True, num_workers=None, requests=None, heads
     o_lat, out, lse = to_np(w.o_lat), to_np(w.out), to_np(w.lse)
     reqs = range(inp.B) if requests is None else requests
     hs = list(range(inp.H)) if heads is None else list(heads)
+    # the merge and up-projection in one launch as well (the benchmarked
+    # step), on the same partials, where that call exists (BF16, V2 dims)
+    fused = None
+    if split and inp.act_dtype == I.DTYPE_BF16 and inp.D_V == 128 and inp.D_C == 512 and inp.H == 128:
+        w.out.zero_()
+        w.combine_up()
+        torch.cuda.synchronize()
+        fused = to_np(w.out)
     for b in reqs:
         r_out, r_lse, r_olat = oracle_request(inp, b, heads=hs)
         tag = f"b={b}"
+        if fused is not None:
+            assert_close(fused[b][hs], r_out, what="fused out " + tag)
         if f32:
             assert_close(out[b][hs], r_out, abs_tol=F32_TOL, what="out " + tag)
             assert_close(o_lat[b][hs], r_olat, abs_tol=F32_TOL, what="o_lat " + tag)
