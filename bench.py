@@ -17,7 +17,8 @@ same workload on the host cores (about 15 s of work), each launch's time with
 the matrix-core utilisation of the attention and the weight rate of the two
 head GEMMs ("parts"), and a plain streaming read for reference.  --long adds
 one layer of the long-context workload (1 request x 131,072 positions);
---fp8-topk adds the FP8-cache, top-2,048 workload.
+--fp8-topk adds the FP8-cache, top-2,048 workload, with one scale per token
+and, from the same draw, with one scale per 128 latent channels.
 """
 
 from __future__ import annotations
@@ -148,14 +149,13 @@ def long_context_layer(torch, I, runner, num_cus, layers=4, reps=8):
             "tokens_per_s_60_layers": round(1e6 / (60 * us), 1), "workers": ws[0].plan.num_workers}
 
 
-def fp8_topk_step(torch, I, runner, num_cus, lists=8, reps=10):
+def fp8_topk_step(torch, I, runner, num_cus, inp, lists=8, reps=10):
     """The FP8-cache workload with a top-2,048 index list per request.  One
     step reads 42 MB out of a 1.35 GB pool, which would otherwise stay in the
     last-level cache, so the steps cycle over `lists` independently drawn
     index-list sets (338 MB of distinct rows).  Reports the step and attention
     times, the cache rate and both roofline fractions (HBM, and BF16 matrix
-    cores: the FP8 latent is widened to BF16 for the MFMAs)."""
-    inp = I.make_inputs("v2_fp8_topk")
+    cores: the FP8 latent is dequantised to BF16 for the MFMAs)."""
     w = runner.DeviceWorkload(inp, split=True, num_cus=num_cus)
     rng = np.random.default_rng(5005)
     sets = []
@@ -286,7 +286,14 @@ def main():
     }
     ceiling = read_ceiling(torch)
     long_layer = long_context_layer(torch, I, runner, num_cus) if args.long else None
-    fp8 = fp8_topk_step(torch, I, runner, num_cus) if args.fp8_topk else None
+    fp8 = fp8g = None
+    if args.fp8_topk:
+        # one draw, both FP8 formats: one scale per token, and one per 128
+        # latent channels (the 656-byte item)
+        fp8_inp = I.make_inputs("v2_fp8_topk")
+        fp8 = fp8_topk_step(torch, I, runner, num_cus, fp8_inp)
+        fp8g = fp8_topk_step(torch, I, runner, num_cus, I.requantize(fp8_inp, I.DTYPE_FP8_G128))
+        del fp8_inp
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -336,6 +343,7 @@ def main():
         result["v2_long_layer"] = long_layer
     if fp8 is not None:
         result["fp8_topk_step"] = fp8
+        result["fp8_g128_topk_step"] = fp8g
     print(json.dumps(result), flush=True)
 
 

@@ -61,7 +61,12 @@ typedef enum {
 typedef enum {
   MLA_F32 = 0,
   MLA_BF16 = 1,
-  MLA_FP8_E4M3 = 2 /* OCP E4M3: bias 7, max 448, no infinities (cache only) */
+  MLA_FP8_E4M3 = 2,     /* OCP E4M3: bias 7, max 448, no infinities (cache only);
+                           one float32 scale per position */
+  MLA_FP8_E4M3_G128 = 3 /* the same codes with one float32 scale per 128
+                           consecutive latent channels of each position
+                           ("DeepSeek's KV Cache", section "Calculating V3.2's
+                           KV cache": the 656-byte main KV item; cache only) */
 } mla_dtype;
 
 /* Model dimensions and types.  Supported combinations:
@@ -71,7 +76,11 @@ typedef enum {
  *                         (DeepSeek-V2 dims; MFMA kernels), d_nope and d_v
  *                         multiples of 16
  *   cache FP8,  act BF16: as BF16, latent stored as E4M3 with one float32
- *                         scale per position, rotary key in BF16 */
+ *                         scale per position, rotary key in BF16
+ *   cache FP8_E4M3_G128, act BF16: as FP8, with D_C / 128 float32 scales per
+ *                         position; channel d of the latent uses scale d / 128
+ *   The FP8 latent is dequantised (code value times its scale) to BF16 inside
+ *   the kernel, one rounding per element, before the matrix products. */
 typedef struct {
   int32_t num_heads;     /* H */
   int32_t d_latent;      /* D_C, width of the cached latent c */
@@ -102,6 +111,8 @@ const char* mla_status_string(mla_status status);
  *   F32 : c [64][D_C] f32,  k_rope [64][D_R] f32
  *   BF16: c [64][D_C] bf16, k_rope [64][D_R] bf16
  *   FP8 : c [64][D_C] e4m3, k_rope [64][D_R] bf16, scale [64] f32
+ *   FP8_E4M3_G128: c [64][D_C] e4m3, k_rope [64][D_R] bf16,
+ *         scale [64][D_C / 128] f32
  * Outputs the page size and the offsets of the rope and scale sections.  Host
  * only. */
 mla_status mla_page_layout(const mla_config* cfg, size_t* page_bytes, size_t* rope_offset,

@@ -19,7 +19,7 @@ LIB_PATH = os.environ.get("MLA_ABSORB_LIB") or os.path.join(os.path.dirname(os.p
                                                            "libmla_absorb.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_LAUNCH = 0, 1, 2, 3
-MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_FP8_E4M3_G128 = 0, 1, 2, 3
 PAGE_TOKENS = 64
 TILE_TOKENS = 32
 

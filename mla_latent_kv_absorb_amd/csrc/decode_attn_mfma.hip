@@ -24,11 +24,11 @@
 // bank conflicts.  Page ids and index lists are read with scalar loads so
 // they never wait behind the LDS-bound vector loads.
 //
-// FP8 cache: the latent arrives as E4M3 with one float32 scale per position.
-// A conversion pass turns the tile into BF16 in LDS (exact); the scale
-// multiplies the content score before the rotary part is added, and multiplies
-// the probabilities fed to the weighted sum (the softmax normaliser uses the
-// unscaled probabilities).
+// FP8 cache: the latent arrives as E4M3 with one float32 scale per position,
+// or one per 128 latent channels of a position ("DeepSeek's KV Cache", section
+// "Calculating V3.2's KV cache").  A conversion pass dequantises the tile into
+// BF16 in LDS: the exact E4M3 value times its scale, rounded once to BF16.
+// The scores and the weighted latent then run exactly as for a BF16 cache.
 //
 // Sparse selection ("DeepSeek's KV Cache", Figure 10): with an index list the
 // tile rows are the listed positions, gathered one row per load; entries that
@@ -38,12 +38,15 @@
 namespace mla {
 namespace {
 
-template <bool FP8>
+// FP8: E4M3 latent; GS: with one scale per 128 latent channels of a position
+// (4 per position) instead of one per position.
+template <bool FP8, bool GS>
 struct Cfg {
   static constexpr int NS = FP8 ? 5 : 4;                       // ring stages
   static constexpr int C_STAGE = FP8 ? kTile * kC8Row : kTile * kCRow;
   static constexpr int R_STAGE = kTile * kRRow;
-  static constexpr int SC_STAGE = FP8 ? kTile * 4 : 0;
+  static constexpr int SCALES = GS ? kLatent / 128 : 1;        // scales per position
+  static constexpr int SC_STAGE = FP8 ? kTile * 4 * SCALES : 0;
   static constexpr int STAGE = C_STAGE + R_STAGE + SC_STAGE;
   static constexpr int CONV_OFF = NS * STAGE;                  // BF16 copy of an FP8 tile
   static constexpr int CONV = FP8 ? kTile * kCRow : 0;
@@ -71,7 +74,7 @@ __device__ __forceinline__ void wait_tiles(int64_t ahead) {
   wait_vmcnt<0>();
 }
 
-template <bool FP8, bool TOPK>
+template <bool FP8, bool GS, bool TOPK>
 struct Loader {
   const DecodeArgs& a;
   uint32_t smem_base;
@@ -113,7 +116,7 @@ struct Loader {
   // Issue this wave's share of tile t (chunk starts at tc0) into stage st.
   __device__ __forceinline__ void issue(int st, int32_t t, int32_t tc0, int32_t T, const LDS int32_t* list,
                                         char* smem) const {
-    using C = Cfg<FP8>;
+    using C = Cfg<FP8, GS>;
     const uint32_t sb = smem_base + st * C::STAGE;
     const uint8_t* pool = a.pool;
     uint32_t bits = 0;
@@ -140,7 +143,12 @@ struct Loader {
       dma16(pg + a.rope_off + (int64_t)(slot0 + rr) * kRRow + 16 * (rc ^ swz_r(8 * w + rr)),
             sb + C::C_STAGE + 8 * w * kRRow);
       if (FP8) {
-        if (lane < 8) dma4(pg + a.scale_off + (int64_t)(slot0 + lane) * 4, sb + C::C_STAGE + C::R_STAGE + 32 * w);
+        // this wave's 8 positions' scales: 32 B, or 128 B with group scales
+        if (GS) {
+          if (lane < 8) dma16(pg + a.scale_off + (int64_t)(slot0 + lane) * 16, sb + C::C_STAGE + C::R_STAGE + 128 * w);
+        } else {
+          if (lane < 8) dma4(pg + a.scale_off + (int64_t)(slot0 + lane) * 4, sb + C::C_STAGE + C::R_STAGE + 32 * w);
+        }
       }
     } else {
       // gathered rows: this wave's 8 row codes
@@ -192,7 +200,8 @@ struct Loader {
             sp = (lane == k) ? pgk[k] : sp;
             ss = (lane == k) ? slk[k] : ss;
           }
-          dma4(sp + a.scale_off + ss * 4, sb + C::C_STAGE + C::R_STAGE + 32 * w);
+          if (GS) dma16(sp + a.scale_off + ss * 16, sb + C::C_STAGE + C::R_STAGE + 128 * w);
+          else dma4(sp + a.scale_off + ss * 4, sb + C::C_STAGE + C::R_STAGE + 32 * w);
         }
       }
     }
@@ -200,9 +209,9 @@ struct Loader {
   }
 };
 
-template <bool FP8, bool TOPK, bool DIRECT>
+template <bool FP8, bool GS, bool TOPK, bool DIRECT>
 __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
-  using C = Cfg<FP8>;
+  using C = Cfg<FP8, GS>;
   constexpr int NS = C::NS;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   LDS char* L = (LDS char*)smem;
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const int hi = lane >> 5;
   const float scale_log2 = a.scale * kLog2e;
 
-  Loader<FP8, TOPK> ld{a, (uint32_t)(uintptr_t)smem, lane, w};
+  Loader<FP8, GS, TOPK> ld{a, (uint32_t)(uintptr_t)smem, lane, w};
 
   // ---- this work-group's share: n units of the split space from offset v0
   // of request b0's span (a span is the request's lead, then its tiles) ----
@@ -329,7 +338,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
           for (int k = 0; k < 8; ++k) {
             const int r = 8 * w + k;
             const i32x2 raw = *(const LDS i32x2*)(src + k * kC8Row);
-            const float sc = scl[r];
+            // lane l covers channels 8l .. 8l + 7: group l / 16 of 128 channels
+            const float sc = GS ? scl[C::SCALES * r + (lane >> 4)] : scl[r];
             // E4M3 pairs -> exact float32 pairs, times the scale, one rounding to BF16
             const f32x2 v[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(raw[0], false),
                                 __builtin_amdgcn_cvt_pk_f32_fp8(raw[0], true),
@@ -489,18 +499,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, bool fp8, hipStream_t s) {
+hipError_t launch_decode_mfma(const DecodeArgs& a, CacheKind kind, hipStream_t s) {
   const bool topk = a.topk_idx != nullptr;
   const bool direct = a.num_workers == 0;
   const dim3 grid(direct ? a.batch : a.num_workers);
   const dim3 block(kThreads);
-#define MLA_LAUNCH(F, T, D) hipLaunchKernelGGL((decode_mfma_kernel<F, T, D>), grid, block, 0, s, a)
-  if (fp8) {
-    if (topk) { if (direct) MLA_LAUNCH(true, true, true); else MLA_LAUNCH(true, true, false); }
-    else { if (direct) MLA_LAUNCH(true, false, true); else MLA_LAUNCH(true, false, false); }
-  } else {
-    if (topk) { if (direct) MLA_LAUNCH(false, true, true); else MLA_LAUNCH(false, true, false); }
-    else { if (direct) MLA_LAUNCH(false, false, true); else MLA_LAUNCH(false, false, false); }
+#define MLA_LAUNCH(F, G)                                                                                 \
+  do {                                                                                                   \
+    if (topk) {                                                                                          \
+      if (direct) hipLaunchKernelGGL((decode_mfma_kernel<F, G, true, true>), grid, block, 0, s, a);     \
+      else hipLaunchKernelGGL((decode_mfma_kernel<F, G, true, false>), grid, block, 0, s, a);           \
+    } else {                                                                                             \
+      if (direct) hipLaunchKernelGGL((decode_mfma_kernel<F, G, false, true>), grid, block, 0, s, a);    \
+      else hipLaunchKernelGGL((decode_mfma_kernel<F, G, false, false>), grid, block, 0, s, a);          \
+    }                                                                                                    \
+  } while (0)
+  switch (kind) {
+    case CacheKind::kFp8Token: MLA_LAUNCH(true, false); break;
+    case CacheKind::kFp8Group128: MLA_LAUNCH(true, true); break;
+    default: MLA_LAUNCH(false, false); break;
   }
 #undef MLA_LAUNCH
   return hipGetLastError();

@@ -13,7 +13,7 @@ using mla::kHeads;
 using mla::kLatent;
 using mla::kRope;
 
-enum class Path { kF32, kMfmaBf16, kMfmaFp8 };
+enum class Path { kF32, kMfmaBf16, kMfmaFp8, kMfmaFp8G128 };
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -30,13 +30,16 @@ mla_status check_config(const mla_config* c, Path* path) {
     *path = Path::kF32;
     return MLA_OK;
   }
-  if ((c->cache_dtype == MLA_BF16 || c->cache_dtype == MLA_FP8_E4M3) && c->act_dtype == MLA_BF16) {
+  if ((c->cache_dtype == MLA_BF16 || c->cache_dtype == MLA_FP8_E4M3 || c->cache_dtype == MLA_FP8_E4M3_G128) &&
+      c->act_dtype == MLA_BF16) {
     if (c->num_heads != kHeads || c->d_latent != kLatent || c->d_rope != kRope) return MLA_ERR_UNSUPPORTED;
     if (c->d_nope % 16 != 0 || c->d_v % 32 != 0) return MLA_ERR_UNSUPPORTED;
-    *path = c->cache_dtype == MLA_BF16 ? Path::kMfmaBf16 : Path::kMfmaFp8;
+    *path = c->cache_dtype == MLA_BF16       ? Path::kMfmaBf16
+            : c->cache_dtype == MLA_FP8_E4M3 ? Path::kMfmaFp8
+                                             : Path::kMfmaFp8G128;
     return MLA_OK;
   }
-  if (c->cache_dtype < MLA_F32 || c->cache_dtype > MLA_FP8_E4M3 || c->act_dtype < MLA_F32 ||
+  if (c->cache_dtype < MLA_F32 || c->cache_dtype > MLA_FP8_E4M3_G128 || c->act_dtype < MLA_F32 ||
       c->act_dtype > MLA_BF16)
     return MLA_ERR_INVALID_ARG;
   return MLA_ERR_UNSUPPORTED;
@@ -59,9 +62,11 @@ void layout(const mla_config* c, size_t* page, size_t* rope_off, size_t* scale_o
     rb = (size_t)MLA_PAGE_TOKENS * c->d_rope * 2;
     sb = 0;
   } else {
+    // FP8: one float32 scale per position, or one per 128 latent channels
     cb = (size_t)MLA_PAGE_TOKENS * c->d_latent;
     rb = (size_t)MLA_PAGE_TOKENS * c->d_rope * 2;
-    sb = (size_t)MLA_PAGE_TOKENS * 4;
+    const size_t groups = c->cache_dtype == MLA_FP8_E4M3_G128 ? (size_t)(c->d_latent + 127) / 128 : 1;
+    sb = (size_t)MLA_PAGE_TOKENS * groups * 4;
   }
   *rope_off = al16(cb);
   *scale_off = al16(*rope_off + rb);
@@ -221,7 +226,10 @@ mla_status mla_decode_attn(const mla_config* cfg, const void* q_lat, const void*
   hipStream_t s = (hipStream_t)stream;
   if (path == Path::kF32) return launch_status(mla::launch_decode_f32(a, s));
   if (path == Path::kMfmaBf16 && topk_idx == nullptr) return launch_status(mla::launch_decode_bf16(a, s));
-  return launch_status(mla::launch_decode_mfma(a, path == Path::kMfmaFp8, s));
+  const mla::CacheKind kind = path == Path::kMfmaFp8       ? mla::CacheKind::kFp8Token
+                              : path == Path::kMfmaFp8G128 ? mla::CacheKind::kFp8Group128
+                                                           : mla::CacheKind::kBf16;
+  return launch_status(mla::launch_decode_mfma(a, kind, s));
 }
 
 mla_status mla_combine(const mla_config* cfg, const void* workspace, size_t workspace_bytes,

@@ -68,7 +68,10 @@ struct HeadGemmArgs {
   int32_t batch, H, M, K;
 };
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, bool fp8, hipStream_t s);
+// latent storage of the MFMA attention kernels
+enum class CacheKind { kBf16, kFp8Token, kFp8Group128 };
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, CacheKind kind, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);  // BF16 cache, dense
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

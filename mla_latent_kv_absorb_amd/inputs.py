@@ -17,6 +17,8 @@ Workloads (sizes follow DeepSeek-V2's MLA: 128 heads, latent 512, rotary key
   v2_fp8_topk   32 requests x 65,536 tokens, latent stored as FP8 E4M3 with
                 one float32 scale per token, rotary key in BF16, each request
                 reads a sorted list of 2,048 distinct positions
+  v2_fp8g_topk  the same draw (same seed), the latent stored as FP8 E4M3 with
+                one float32 scale per 128 latent channels of each token
 
 Values: latents, rotary keys and queries ~ N(0, 1); W_UK and W_UV ~ N(0, 1/D_C)
 (variance 1/D_C).  BF16 configs round every drawn value to BF16 with
@@ -27,7 +29,8 @@ lengths, page permutation, c_kv, k_rope, q_nope, q_rope, W_UK, W_UV, top-k
 lists.
 
 FP8 encoding of the latent (a data-preparation step, not part of decode):
-per token the scale is max|c|/448 and each element is rounded to the nearest
+per token (or per group of 128 consecutive channels of a token) the scale is
+max|c|/448 over the token (group), and each element is rounded to the nearest
 E4M3 value (ties to the even code), saturating at +-448.
 """
 
@@ -43,6 +46,9 @@ PAGE_TOKENS = 64
 DTYPE_F32 = "f32"
 DTYPE_BF16 = "bf16"
 DTYPE_FP8 = "fp8_e4m3"
+DTYPE_FP8_G128 = "fp8_e4m3_g128"
+FP8_GROUP = 128
+FP8_DTYPES = (DTYPE_FP8, DTYPE_FP8_G128)
 
 WORKLOADS = {
     "tiny_fp32": dict(H=4, D_C=16, D_R=8, D_N=8, D_V=8, B=1, ctx=(64, 64),
@@ -55,6 +61,8 @@ WORKLOADS = {
                     cache=DTYPE_BF16, act=DTYPE_BF16, seed=4000, topk=0, layers=60),
     "v2_fp8_topk": dict(H=128, D_C=512, D_R=64, D_N=128, D_V=128, B=32, ctx=(65536, 65536),
                         cache=DTYPE_FP8, act=DTYPE_BF16, seed=5, topk=2048),
+    "v2_fp8g_topk": dict(H=128, D_C=512, D_R=64, D_N=128, D_V=128, B=32, ctx=(65536, 65536),
+                         cache=DTYPE_FP8_G128, act=DTYPE_BF16, seed=5, topk=2048),
 }
 
 
@@ -79,7 +87,7 @@ class DecodeInputs:
     w_uv: np.ndarray              # float32 [H, D_V, D_C]
     page_perm: np.ndarray         # int64 [total pages]: logical page -> physical page
     c_codes: Optional[np.ndarray] = None   # uint8 [sum T, D_C] (FP8 cache)
-    c_scales: Optional[np.ndarray] = None  # float32 [sum T] (FP8 cache)
+    c_scales: Optional[np.ndarray] = None  # float32 [sum T], or [sum T, D_C / 128] with group scales
     topk_idx: Optional[np.ndarray] = None  # int32 [B, k] sorted, -1 padded
 
     @property
@@ -153,6 +161,22 @@ def quantize_fp8_per_token(c: np.ndarray, chunk_rows: int = 1 << 18):
     present (same rounding as encode_e4m3, checked in the tests)."""
     amax = np.max(np.abs(c), axis=1).astype(np.float32)
     scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return _encode_scaled(c, scale[:, None], chunk_rows), scale
+
+
+def quantize_fp8_per_group(c: np.ndarray, group: int = FP8_GROUP, chunk_rows: int = 1 << 18):
+    """As quantize_fp8_per_token, with one scale per group of ``group``
+    consecutive channels of a token: scales [T, D_C / group]."""
+    T, D = c.shape
+    assert D % group == 0
+    amax = np.max(np.abs(c.reshape(T, D // group, group)), axis=2).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return _encode_scaled(c, np.repeat(scale, group, axis=1), chunk_rows), scale
+
+
+def _encode_scaled(c: np.ndarray, scale: np.ndarray, chunk_rows: int):
+    """E4M3 codes of c / scale (scale broadcast over rows [T, 1] or given per
+    element [T, D]), quotient in float32, clamped to +-448."""
     codes = np.empty(c.shape, dtype=np.uint8)
     try:
         import torch
@@ -161,12 +185,12 @@ def quantize_fp8_per_token(c: np.ndarray, chunk_rows: int = 1 << 18):
     for lo in range(0, c.shape[0], chunk_rows):
         hi = min(lo + chunk_rows, c.shape[0])
         if torch is not None:
-            x = torch.from_numpy(np.ascontiguousarray(c[lo:hi])) / torch.from_numpy(scale[lo:hi])[:, None]
+            x = torch.from_numpy(np.ascontiguousarray(c[lo:hi])) / torch.from_numpy(np.ascontiguousarray(scale[lo:hi]))
             codes[lo:hi] = x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         else:
-            x = np.clip(c[lo:hi] / scale[lo:hi, None], -448.0, 448.0)
+            x = np.clip(c[lo:hi] / scale[lo:hi], -448.0, 448.0)
             codes[lo:hi] = encode_e4m3(x)
-    return codes, scale
+    return codes
 
 
 def make_inputs(name: str, seed: Optional[int] = None, *, batch: Optional[int] = None,
@@ -219,17 +243,30 @@ def make_inputs(name: str, seed: Optional[int] = None, *, batch: Optional[int] =
             idx[b, :n] = pick
     if cache == DTYPE_BF16:
         c = round_to_bf16(c)
-    if cache in (DTYPE_BF16, DTYPE_FP8):
+    if cache in (DTYPE_BF16,) + FP8_DTYPES:
         kr = round_to_bf16(kr)
     if act == DTYPE_BF16:
         qn, qr, wuk, wuv = (round_to_bf16(a) for a in (qn, qr, wuk, wuv))
     codes = scales = None
     if cache == DTYPE_FP8:
         codes, scales = quantize_fp8_per_token(c)
+    elif cache == DTYPE_FP8_G128:
+        codes, scales = quantize_fp8_per_group(c)
     return DecodeInputs(H=H, D_C=D_C, D_R=D_R, D_N=D_N, D_V=D_V, cache_dtype=cache, act_dtype=act,
                         scale=float(1.0 / np.sqrt(D_N + D_R)), seq_lens=T.astype(np.int32),
                         offsets=offsets, c_kv=c, k_rope=kr, q_nope=qn, q_rope=qr, w_uk=wuk, w_uv=wuv,
                         page_perm=page_perm, c_codes=codes, c_scales=scales, topk_idx=idx)
+
+
+def requantize(inp: DecodeInputs, cache_dtype: str) -> DecodeInputs:
+    """The same draw with the latent stored in the other FP8 format (from the
+    pre-quantisation values the FP8 workloads keep)."""
+    assert inp.cache_dtype in FP8_DTYPES and cache_dtype in FP8_DTYPES
+    if cache_dtype == DTYPE_FP8:
+        codes, scales = quantize_fp8_per_token(inp.c_kv)
+    else:
+        codes, scales = quantize_fp8_per_group(inp.c_kv)
+    return dataclasses.replace(inp, cache_dtype=cache_dtype, c_codes=codes, c_scales=scales)
 
 
 # ---------------------------------------------------------------------------
@@ -238,6 +275,7 @@ def make_inputs(name: str, seed: Optional[int] = None, *, batch: Optional[int] =
 #   F32 : c_kv [64][D_C] f32, k_rope [64][D_R] f32
 #   BF16: c_kv [64][D_C] bf16, k_rope [64][D_R] bf16
 #   FP8 : c_kv [64][D_C] e4m3, k_rope [64][D_R] bf16, scale [64] f32
+#   FP8 with group scales: the same, scale [64][D_C / 128] f32
 # Rows past a request's length in its last page are zero.
 # ---------------------------------------------------------------------------
 def page_layout(cache_dtype: str, D_C: int, D_R: int):
@@ -250,6 +288,8 @@ def page_layout(cache_dtype: str, D_C: int, D_R: int):
         c_bytes, r_bytes, s_bytes = PAGE_TOKENS * D_C * 2, PAGE_TOKENS * D_R * 2, 0
     elif cache_dtype == DTYPE_FP8:
         c_bytes, r_bytes, s_bytes = PAGE_TOKENS * D_C, PAGE_TOKENS * D_R * 2, PAGE_TOKENS * 4
+    elif cache_dtype == DTYPE_FP8_G128:
+        c_bytes, r_bytes, s_bytes = PAGE_TOKENS * D_C, PAGE_TOKENS * D_R * 2, PAGE_TOKENS * (D_C // FP8_GROUP) * 4
     else:
         raise ValueError(cache_dtype)
     r_off = al16(c_bytes)
@@ -307,8 +347,10 @@ def cache_bytes_read(inp: DecodeInputs) -> int:
         item = (inp.D_C + inp.D_R) * 4
     elif inp.cache_dtype == DTYPE_BF16:
         item = (inp.D_C + inp.D_R) * 2
-    else:
+    elif inp.cache_dtype == DTYPE_FP8:
         item = inp.D_C + inp.D_R * 2 + 4
+    else:
+        item = inp.D_C + inp.D_R * 2 + 4 * (inp.D_C // FP8_GROUP)
     if inp.topk_idx is not None:
         n = int(np.sum(inp.topk_idx >= 0))
     else:

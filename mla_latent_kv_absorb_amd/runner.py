@@ -15,7 +15,8 @@ from . import inputs as I
 
 
 def _dtype_code(name: str) -> int:
-    return {I.DTYPE_F32: B.MLA_F32, I.DTYPE_BF16: B.MLA_BF16, I.DTYPE_FP8: B.MLA_FP8_E4M3}[name]
+    return {I.DTYPE_F32: B.MLA_F32, I.DTYPE_BF16: B.MLA_BF16, I.DTYPE_FP8: B.MLA_FP8_E4M3,
+            I.DTYPE_FP8_G128: B.MLA_FP8_E4M3_G128}[name]
 
 
 def to_device_act(x: np.ndarray, act: str, device):

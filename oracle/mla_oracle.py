@@ -76,13 +76,28 @@ def e4m3_to_f64(codes) -> np.ndarray:
 
 
 def dequant_fp8_latent(codes, scales) -> np.ndarray:
-    """Latent stored as E4M3 codes [T, D_C] with one float32 scale per token [T].
+    """Latent stored as E4M3 codes [T, D_C] with float32 scales: one per token
+    ([T]), or one per group of consecutive channels of a token ([T, G], group
+    g covering channels g * D_C / G .. (g + 1) * D_C / G - 1).
 
     The stored value times its scale gives the latent ("DeepSeek's KV Cache",
     section "Calculating V3.2's KV cache": the scale brings low-precision values
-    back to their original size).  Exact in float64.
+    back to their original size; the main KV item keeps one float32 scale per
+    128 of the 512 latent dimensions).  Exact in float64.
     """
-    return e4m3_to_f64(codes) * np.asarray(scales, dtype=np.float64)[:, None]
+    vals = e4m3_to_f64(codes)
+    s = np.asarray(scales, dtype=np.float64)
+    if s.ndim == 1:
+        return vals * s[:, None]
+    T, D = vals.shape
+    G = s.shape[1]
+    if D % G:
+        raise ValueError("latent width must be a multiple of the number of groups")
+    out = np.empty_like(vals)
+    w = D // G
+    for g in range(G):
+        out[:, g * w:(g + 1) * w] = vals[:, g * w:(g + 1) * w] * s[:, g:g + 1]
+    return out
 
 
 # ---------------------------------------------------------------------------

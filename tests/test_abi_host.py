@@ -51,6 +51,10 @@ def test_page_layout(B):
     assert (pb, ro, so) == (32768 + 8192 + 256, 32768, 32768 + 8192)
     # per-position bytes actually read: 512 + 128 + 4 = 644
     assert (pb) // 64 == 644
+    # one float32 scale per 128 latent channels: the 656-byte item
+    pb, ro, so = B.page_layout(v2(B, B.MLA_FP8_E4M3_G128))
+    assert (pb, ro, so) == (32768 + 8192 + 1024, 32768, 32768 + 8192)
+    assert pb // 64 == 656
     tiny = B.make_config(4, 16, 8, 8, 8, 0.25, B.MLA_F32, B.MLA_F32)
     assert B.page_layout(tiny) == (64 * 24 * 4, 64 * 16 * 4, 64 * 24 * 4)
 

@@ -42,7 +42,7 @@ def to_np(t):
 
 def oracle_request(inp, b, heads=None):
     lo, hi = inp.request(b)
-    if inp.cache_dtype == I.DTYPE_FP8:
+    if inp.cache_dtype in I.FP8_DTYPES:
         c = oracle.dequant_fp8_latent(inp.c_codes[lo:hi], inp.c_scales[lo:hi])
     else:
         c = inp.c_kv[lo:hi]
@@ -286,24 +286,32 @@ def test_rescale_path_with_growing_scores(torch, R):
 # ---------------------------------------------------------------------------
 # FP8 latent + index lists
 # ---------------------------------------------------------------------------
-def test_fp8_every_code_converts_exactly(torch, R):
+@pytest.mark.parametrize("cache", [I.DTYPE_FP8, I.DTYPE_FP8_G128])
+def test_fp8_every_code_converts_exactly(torch, R, cache):
     """Each finite E4M3 code, weighted by probability 1 (zero query, one
-    position), comes back as its exact value times the position's scale."""
-    _log("fp8 codes")
+    position), comes back as its exact value times its scale.  With group
+    scales the two copies of the 256 codes meet four different scales; every
+    product has at most 7 significant bits, so BF16 holds it exactly."""
+    _log(f"fp8 codes {cache}")
     H, D_C, D_R = 128, 512, 64
     codes = np.tile(np.arange(256, dtype=np.uint8), 2)[None, :]
     codes[:, (codes[0] & 0x7F) == 0x7F] = 0  # NaN codes stay out of the arithmetic
     codes = np.concatenate([codes, codes[:, ::-1]])            # two requests, one position each
-    scales = np.array([1.0, 0.375], dtype=np.float32)
+    if cache == I.DTYPE_FP8:
+        scales = np.array([1.0, 0.375], dtype=np.float32)
+        full = np.repeat(scales[:, None], D_C, axis=1)
+    else:
+        scales = np.array([[1.0, 0.375, 2.0, 0.15625], [0.15625, 4.0, 0.375, 1.0]], dtype=np.float32)
+        full = np.repeat(scales, 128, axis=1)
     inp = custom_inputs(np.zeros((2, D_C)), np.zeros((2, D_R)), np.zeros((2, H, 128)), np.zeros((2, H, D_R)),
-                        np.zeros((H, D_C, 128)), np.zeros((H, 128, D_C)), [1, 1], I.DTYPE_FP8, I.DTYPE_BF16,
+                        np.zeros((H, D_C, 128)), np.zeros((H, 128, D_C)), [1, 1], cache, I.DTYPE_BF16,
                         0.1, codes=codes, scales=scales)
     w = R.DeviceWorkload(inp, split=False)
     w.attend(q_lat=torch.zeros_like(w.q_lat))
     torch.cuda.synchronize()
     got = to_np(w.o_lat)
     for b in range(2):
-        ref = oracle.e4m3_to_f64(codes[b]) * scales[b]
+        ref = oracle.e4m3_to_f64(codes[b]) * full[b]
         for h in (0, 63, 127):
             assert np.array_equal(got[b, h], ref), f"request {b} head {h}"
 
@@ -316,9 +324,9 @@ def _bit_pattern_case(cache, seed):
     for d in range(12):
         c[:, d] = np.tile((pos >> d) & 1, B)
     codes = scales = None
-    if cache == I.DTYPE_FP8:
+    if cache in I.FP8_DTYPES:
         codes = np.where(c > 0, 0x38, 0).astype(np.uint8)
-        scales = np.ones(B * T, np.float32)
+        scales = np.ones(B * T, np.float32) if cache == I.DTYPE_FP8 else np.ones((B * T, D_C // 128), np.float32)
     idx = np.full((B, 160), -1, np.int32)
     for b in range(B):
         idx[b, :128] = np.sort(rng.choice(T, 128, replace=False))
@@ -328,7 +336,7 @@ def _bit_pattern_case(cache, seed):
     return inp, idx
 
 
-@pytest.mark.parametrize("cache", [I.DTYPE_BF16, I.DTYPE_FP8])
+@pytest.mark.parametrize("cache", [I.DTYPE_BF16, I.DTYPE_FP8, I.DTYPE_FP8_G128])
 def test_topk_index_handling_bit_exact(torch, R, cache):
     """Zero queries give every picked position probability 1; latent dim d of
     position p holds bit d of p.  With one worker the partial is exactly
@@ -352,18 +360,35 @@ def test_topk_index_handling_bit_exact(torch, R, cache):
         np.testing.assert_allclose(part_l[b].cpu().numpy(), math.log(128), rtol=1e-6)
 
 
-def test_fp8_topk_small(torch, R):
-    _log("fp8 topk small")
-    inp = I.make_inputs("v2_fp8_topk", seed=21, batch=2, ctx=(3000, 3000), topk=100)
+@pytest.mark.parametrize("name", ["v2_fp8_topk", "v2_fp8g_topk"])
+def test_fp8_topk_small(torch, R, name):
+    _log(f"{name} small")
+    inp = I.make_inputs(name, seed=21, batch=2, ctx=(3000, 3000), topk=100)
     inp.topk_idx[1, 96:] = -1  # padding entries
     for split in (False, True):
         check_step(torch, R, inp, split=split)
 
 
-def test_fp8_dense_small(torch, R):
-    _log("fp8 dense small")
-    import dataclasses
-    inp = dataclasses.replace(I.make_inputs("v2_fp8_topk", seed=22, batch=2, ctx=(500, 1500), topk=0))
+@pytest.mark.parametrize("name", ["v2_fp8_topk", "v2_fp8g_topk"])
+def test_fp8_dense_small(torch, R, name):
+    _log(f"{name} dense small")
+    inp = I.make_inputs(name, seed=22, batch=2, ctx=(500, 1500), topk=0)
+    check_step(torch, R, inp, split=True)
+    check_step(torch, R, inp, split=False)
+
+
+def test_fp8_group_scales_differ_per_group(torch, R):
+    """Group scales that differ by up to 2^4 across the four groups of a
+    position (and across positions): the per-group dequantisation, not a
+    per-position one, is what matches the oracle (one scale for all groups
+    would be off by the whole latent).  The spread is kept where the scores
+    stay near unit size, the regime the BF16 tolerance is derived for; a
+    2^10 spread gives scores of ~9 sigma, where BF16 rounding of the latent
+    alone moves the peaked softmax past it."""
+    _log("fp8 group scales spread")
+    inp = I.make_inputs("v2_fp8g_topk", seed=24, batch=3, ctx=(200, 700), topk=0)
+    rng = np.random.default_rng(24)
+    inp.c_scales[:] = inp.c_scales * np.exp2(rng.integers(-2, 3, size=inp.c_scales.shape)).astype(np.float32)
     check_step(torch, R, inp, split=True)
 
 
@@ -401,7 +426,17 @@ def test_v2_long_layer_sampled(torch, R):
     check_step(torch, R, inp, split=True, requests=[0], heads=[0, 64, 127])
 
 
-def test_fp8_topk_full_size_sampled(torch, R):
+@pytest.fixture(scope="module")
+def fp8_full():
+    return I.make_inputs("v2_fp8_topk")
+
+
+def test_fp8_topk_full_size_sampled(torch, R, fp8_full):
     _log("v2_fp8_topk full size")
-    inp = I.make_inputs("v2_fp8_topk")
-    check_step(torch, R, inp, split=True, requests=[0, 31], heads=[0, 127])
+    check_step(torch, R, fp8_full, split=True, requests=[0, 31], heads=[0, 127])
+
+
+def test_fp8_group_scales_topk_full_size_sampled(torch, R, fp8_full):
+    _log("v2_fp8g_topk full size (same draw, per-128-channel scales)")
+    inp = I.requantize(fp8_full, I.DTYPE_FP8_G128)
+    check_step(torch, R, inp, split=True, requests=[0, 17, 31], heads=[0, 64, 127])

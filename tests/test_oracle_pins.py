@@ -248,6 +248,45 @@ def test_fp8_latent_dequant_is_per_token_scale():
     np.testing.assert_array_equal(got, [[0.5, 1.0], [-3.0, 0.0]])
 
 
+def test_fp8_latent_dequant_per_128_channel_groups():
+    """One float32 scale per 128 latent dimensions ("DeepSeek's KV Cache",
+    section "Calculating V3.2's KV cache", the 656-byte main KV item): channel
+    d of a token takes scale d // 128.  Values written out by hand."""
+    codes = np.full((2, 512), 0x38, dtype=np.uint8)      # 1.0
+    codes[1] = 0xC0                                      # -2.0
+    scales = np.array([[1.0, 2.0, 4.0, 8.0], [0.5, 0.25, 3.0, 1.0]], dtype=np.float32)
+    got = oracle.dequant_fp8_latent(codes, scales)
+    want = np.array([[1.0] * 128 + [2.0] * 128 + [4.0] * 128 + [8.0] * 128,
+                     [-1.0] * 128 + [-0.5] * 128 + [-6.0] * 128 + [-2.0] * 128])
+    np.testing.assert_array_equal(got, want)
+    # an interleaved reading of the groups (channel d -> scale d % 4) differs
+    assert not np.array_equal(got[0], np.tile([1.0, 2.0, 4.0, 8.0], 128))
+    # equal group scales reduce to the per-token form
+    rng = np.random.default_rng(4)
+    c = rng.integers(0, 256, size=(3, 512)).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0
+    s = np.array([0.5, 3.0, 0.01], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.dequant_fp8_latent(c, np.repeat(s[:, None], 4, axis=1)),
+                                  oracle.dequant_fp8_latent(c, s))
+
+
+def test_group_scaled_latent_through_attention():
+    """With one cached position and a zero query the weighted latent is that
+    position's dequantised latent exactly (probability 1); with two positions
+    and equal scores it is their mean."""
+    codes = np.full((2, 512), 0x38, dtype=np.uint8)
+    codes[1, :] = 0x40                                   # 2.0
+    scales = np.array([[1.0, 2.0, 4.0, 8.0], [1.0, 1.0, 1.0, 1.0]], dtype=np.float32)
+    c = oracle.dequant_fp8_latent(codes, scales)
+    q_lat, q_rope = np.zeros((3, 512)), np.zeros((3, 64))
+    kr = np.zeros((2, 64))
+    o, lse = oracle.latent_decode(q_lat, q_rope, c[:1], kr[:1], 0.1)
+    np.testing.assert_array_equal(o[1], [1.0] * 128 + [2.0] * 128 + [4.0] * 128 + [8.0] * 128)
+    o, lse = oracle.latent_decode(q_lat, q_rope, c, kr, 0.1)
+    np.testing.assert_allclose(o[2], [1.5] * 128 + [2.0] * 128 + [3.0] * 128 + [5.0] * 128, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, np.log(2.0), rtol=0, atol=1e-15)
+
+
 def test_byte_count_closed_forms_match_pages():
     g = _load("byte_counts.json")
     mha = oracle.mha_cache_bytes_per_token(60, 128, 128, 128, 2)
@@ -320,6 +359,25 @@ def test_generator_e4m3_encode_matches_torch():
     ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     # float64 vs float32 input only differs on exact float32 rounding ties; none here
     assert np.array_equal(ours, ref)
+
+
+def test_generator_group_quantiser_uses_full_range():
+    """Per 128-channel group the largest magnitude maps to 448 and every
+    element is the nearest E4M3 value of x / scale (generator check)."""
+    rng = np.random.default_rng(2)
+    c = rng.standard_normal((50, 512)).astype(np.float32)
+    c[3, 128:256] = 0.0                                   # an all-zero group
+    codes, scales = inputs.quantize_fp8_per_group(c)
+    assert codes.shape == (50, 512) and scales.shape == (50, 4)
+    vals = oracle.e4m3_to_f64(codes).reshape(50, 4, 128)
+    amax = np.max(np.abs(vals), axis=2)
+    assert np.all((amax == 448.0) | ((amax == 0.0) & (scales == 1.0)))
+    np.testing.assert_array_equal(scales[3, 1], 1.0)
+    x = (c.reshape(50, 4, 128) / scales[:, :, None]).astype(np.float32).reshape(50, 512)
+    np.testing.assert_array_equal(codes, inputs.encode_e4m3(np.clip(x, -448, 448)))
+    # dequantised error within half a step of E4M3 (3 mantissa bits) per element
+    deq = oracle.dequant_fp8_latent(codes, scales)
+    assert np.all(np.abs(deq - c) <= np.abs(c) * 2.0 ** -4 + np.repeat(scales, 128, axis=1) * 2.0 ** -10)
 
 
 def test_generator_workload_structure():
