@@ -270,6 +270,111 @@ def requantize(inp: DecodeInputs, cache_dtype: str) -> DecodeInputs:
 
 
 # ---------------------------------------------------------------------------
+# Lightning-indexer inputs: per request one indexer query (H_I heads of width
+# d_I, BF16 values), one float32 weight per head, and per cached position one
+# search key of width d_I stored as E4M3 with one float32 scale per position.
+#
+#   v32_indexer   32 requests x 65,536 positions, 64 heads x 128, top-2,048
+#                 (the sparse workload's shape: its index lists come from here)
+#
+# Draw order: lengths, page permutation, keys, queries, head weights.  Keys,
+# queries and weights ~ N(0, 1); queries rounded to BF16; keys quantised per
+# position as the FP8 latent is (scale = max|k| / 448).
+# ---------------------------------------------------------------------------
+INDEXER_WORKLOADS = {
+    "v32_indexer": dict(B=32, ctx=(65536, 65536), H_I=64, d_I=128, topk=2048, seed=6),
+}
+
+
+@dataclasses.dataclass
+class IndexerInputs:
+    H_I: int
+    d_I: int
+    topk: int
+    seq_lens: np.ndarray          # int32 [B]
+    offsets: np.ndarray           # int64 [B+1]
+    q_idx: np.ndarray             # float32 [B, H_I, d_I] (BF16 values)
+    w_idx: np.ndarray             # float32 [B, H_I]
+    k_codes: np.ndarray           # uint8 [sum T, d_I]
+    k_scales: np.ndarray          # float32 [sum T]
+    page_perm: np.ndarray         # int64 [total pages]
+
+    @property
+    def B(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    def request(self, b: int):
+        return int(self.offsets[b]), int(self.offsets[b + 1])
+
+    def pages_of(self, b: int) -> int:
+        return -(-int(self.seq_lens[b]) // PAGE_TOKENS)
+
+
+def make_indexer_inputs(name: str = "v32_indexer", seed: Optional[int] = None, *, batch: Optional[int] = None,
+                        ctx: Optional[tuple] = None, seq_lens=None, topk: Optional[int] = None) -> IndexerInputs:
+    spec = dict(INDEXER_WORKLOADS[name])
+    B = spec["B"] if batch is None else batch
+    lo, hi = spec["ctx"] if ctx is None else ctx
+    k = spec["topk"] if topk is None else topk
+    rng = np.random.default_rng(spec["seed"] if seed is None else seed)
+    H_I, d_I = spec["H_I"], spec["d_I"]
+    if seq_lens is not None:
+        T = np.asarray(seq_lens, dtype=np.int64)
+        B = T.shape[0]
+    elif lo == hi:
+        T = np.full(B, lo, dtype=np.int64)
+    else:
+        T = rng.integers(lo, hi + 1, size=B).astype(np.int64)
+    offsets = np.zeros(B + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(T)
+    n_pages = int(np.sum(-(-T // PAGE_TOKENS)))
+    page_perm = rng.permutation(n_pages).astype(np.int64)
+    keys = rng.standard_normal((int(offsets[-1]), d_I), dtype=np.float32)
+    q = round_to_bf16(rng.standard_normal((B, H_I, d_I), dtype=np.float32))
+    w = rng.standard_normal((B, H_I), dtype=np.float32)
+    codes, scales = quantize_fp8_per_token(keys)
+    return IndexerInputs(H_I=H_I, d_I=d_I, topk=k, seq_lens=T.astype(np.int32), offsets=offsets, q_idx=q,
+                         w_idx=w, k_codes=codes, k_scales=scales, page_perm=page_perm)
+
+
+def key_page_layout(d_I: int):
+    """Search-key page: keys [64][d_I] e4m3, then scales [64] f32, each section
+    16-byte aligned."""
+    s_off = (PAGE_TOKENS * d_I + 15) // 16 * 16
+    return {"k_off": 0, "s_off": s_off, "page_bytes": (s_off + PAGE_TOKENS * 4 + 15) // 16 * 16}
+
+
+def build_key_pool(inp: IndexerInputs, extra_pages: int = 0):
+    """Scatter the search keys into a page pool in the order of
+    ``inp.page_perm``.  Returns (pool uint8 [P, page_bytes], block_table int32
+    [B, max_pages] padded with -1)."""
+    lay = key_page_layout(inp.d_I)
+    P = int(inp.page_perm.shape[0]) + extra_pages
+    pool = np.zeros((P, lay["page_bytes"]), dtype=np.uint8)
+    max_pages = max(inp.pages_of(b) for b in range(inp.B))
+    table = np.full((inp.B, max(max_pages, 1)), -1, dtype=np.int32)
+    first = 0
+    for b in range(inp.B):
+        lo, hi = inp.request(b)
+        np_b = inp.pages_of(b)
+        phys = inp.page_perm[first:first + np_b]
+        table[b, :np_b] = phys
+        first += np_b
+        pad = np_b * PAGE_TOKENS - (hi - lo)
+        kc = np.concatenate([inp.k_codes[lo:hi], np.zeros((pad, inp.d_I), np.uint8)])
+        ks = np.concatenate([inp.k_scales[lo:hi], np.zeros(pad, np.float32)])
+        pool[phys, :PAGE_TOKENS * inp.d_I] = kc.reshape(np_b, -1)
+        pool[phys, lay["s_off"]:lay["s_off"] + PAGE_TOKENS * 4] = ks.reshape(np_b, -1).view(np.uint8)
+    return pool, table
+
+
+def key_bytes_read(inp: IndexerInputs) -> int:
+    """Algorithmic bytes one indexer scan reads: every visible position's key
+    and scale once (the pages' 132-byte search-key item)."""
+    return int(np.sum(inp.seq_lens.astype(np.int64))) * (inp.d_I + 4)
+
+
+# ---------------------------------------------------------------------------
 # Paged pool layout.  One page = 64 tokens, sections stored one after another
 # (structure of arrays inside a page, each section 16-byte aligned):
 #   F32 : c_kv [64][D_C] f32, k_rope [64][D_R] f32
