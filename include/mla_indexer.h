@@ -1,0 +1,86 @@
+/* Lightning indexer and top-k pick for sparse MLA decode, gfx950.
+ *
+ * The two calls produce the per-request index lists that mla_decode_attn
+ * consumes in its sparse mode ("DeepSeek's KV Cache: From 3.9 MB to 890 B per
+ * Token", sections "DSA: three things the indexer builds" and "The score that
+ * picks positions", Figures 8 and 9):
+ *
+ *   1. mla_indexer_scores   I(b, s) = sum_j w[b][j] * ReLU(q[b][j] . k[s])
+ *                           for every cached position s of request b, with the
+ *                           search key k[s] stored as E4M3 values times one
+ *                           float32 scale per position (section "Calculating
+ *                           V3.2's KV cache": the 132-byte search-key item);
+ *   2. mla_topk_select      per request, up to k of the highest-scoring
+ *                           positions 0 .. seq_lens[b]-1, sorted by position.
+ *
+ * Same conventions as mla_absorb.h: every buffer belongs to the caller and
+ * lives in device memory unless stated; the library allocates nothing, keeps
+ * no state and never synchronises; every call checks its host-visible
+ * arguments and enqueues nothing on error; device metadata (block table,
+ * lengths) is never trusted to be in range.
+ */
+#ifndef MLA_INDEXER_H_
+#define MLA_INDEXER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mla_absorb.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The dims with a kernel: 64 indexer heads of width 128 (V3.2). */
+#define MLA_INDEXER_HEADS 64
+#define MLA_INDEXER_DIM 128
+
+/* Byte layout of one search-key page (64 positions, sections 16-byte
+ * aligned): keys [64][dim] e4m3, then scales [64] f32.  For dim = 128 that is
+ * 8,448 bytes, 132 per position.  Host only. */
+mla_status mla_indexer_page_layout(int32_t dim, size_t* page_bytes, size_t* scale_offset);
+
+/* Step 1: indexer scores of every cached position.
+ *   n_heads, dim: must be MLA_INDEXER_HEADS and MLA_INDEXER_DIM
+ *                 (MLA_ERR_UNSUPPORTED otherwise).
+ *   q_idx [batch][n_heads][dim] BF16 (16-byte aligned): indexer queries.
+ *   w_idx [batch][n_heads] float32: head weights (any sign).
+ *   key_pool: num_pages pages in the layout above (16-byte aligned); page
+ *             block_table[b][i] holds positions 64i .. 64i+63 of request b
+ *             (int32 [batch][block_table_stride]).
+ *   seq_lens [batch] int32: cached positions per request.
+ *   scores [batch][score_stride] float32: scores[b][s] is written for
+ *             0 <= s < min(seq_lens[b], score_stride, 64 * block_table_stride);
+ *             other entries are left alone.  A position whose page id is out
+ *             of range gets -infinity.
+ * The FP8 keys are widened exactly to BF16 and contracted with the queries on
+ * the matrix cores in float32; the scale is applied after the ReLU, which is
+ * exact for positive scales (ReLU(s x) = s ReLU(x)).  Errors: null or
+ * misaligned pointers, batch < 1, strides < 1 -> MLA_ERR_INVALID_ARG. */
+mla_status mla_indexer_scores(int32_t n_heads, int32_t dim, const void* q_idx, const float* w_idx,
+                              const void* key_pool, int64_t num_pages, const int32_t* block_table,
+                              int32_t block_table_stride, const int32_t* seq_lens, int32_t batch,
+                              float* scores, int64_t score_stride, void* stream);
+
+/* Workspace bytes mla_topk_select needs for `batch` requests (a histogram
+ * per request; the call clears it itself). */
+size_t mla_topk_workspace_bytes(int32_t batch);
+
+/* Step 2: pick, per request b, min(k, T_b) positions among 0 .. T_b - 1
+ * (T_b = min(seq_lens[b], score_stride); negative lengths count as 0) with the
+ * highest scores[b][s]; among equal scores the lower position comes first.
+ * idx_out [batch][k] int32 receives them in increasing position order, then
+ * -1 up to k: the index-list format mla_decode_attn takes.
+ *   -0 and +0 count as equal; NaN ranks below every other value.
+ *   workspace: mla_topk_workspace_bytes(batch) bytes, 16-byte aligned.
+ * Errors: null or misaligned pointers, batch < 1, k < 1, score_stride < 1, a
+ * too small workspace -> MLA_ERR_INVALID_ARG. */
+mla_status mla_topk_select(const float* scores, int64_t score_stride, const int32_t* seq_lens, int32_t batch,
+                           int32_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_INDEXER_H_ */

@@ -1,4 +1,5 @@
-"""ctypes binding of libmla_absorb.so (C ABI in include/mla_absorb.h).
+"""ctypes binding of libmla_absorb.so (C ABI in include/mla_absorb.h and
+include/mla_indexer.h).
 
 Argument marshalling only: tensors are checked for device, dtype, shape and
 contiguity (the C ABI receives plain pointers and cannot check sizes), then
@@ -27,7 +28,9 @@ EXPORTED = (
     "mla_abi_version", "mla_status_string", "mla_page_layout", "mla_decode_plan",
     "mla_absorb_q", "mla_decode_attn", "mla_combine", "mla_out_up", "mla_combine_out_up",
     "mla_check_decode_inputs_host",
+    "mla_indexer_page_layout", "mla_indexer_scores", "mla_topk_workspace_bytes", "mla_topk_select",
 )
+INDEXER_HEADS, INDEXER_DIM = 64, 128
 
 
 class MlaConfig(ctypes.Structure):
@@ -69,6 +72,10 @@ def _load():
         "mla_out_up": ([cfgp, P, P, P, I32, P], I32),
         "mla_combine_out_up": ([cfgp, P, SZ, P, I32, I32, planp, P, P, P, P], I32),
         "mla_check_decode_inputs_host": ([cfgp, I32, i32p, i32p, I32, I64, i32p, I32, i32p], I32),
+        "mla_indexer_page_layout": ([I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
+        "mla_indexer_scores": ([I32, I32, P, P, P, I64, P, I32, P, I32, P, I64, P], I32),
+        "mla_topk_workspace_bytes": ([I32], SZ),
+        "mla_topk_select": ([P, I64, P, I32, I32, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -248,3 +255,45 @@ def mla_check_decode_inputs_host(cfg: MlaConfig, seq_lens, block_table, num_page
 def raw_lib():
     """The loaded ctypes library (for tests that call the C ABI directly)."""
     return _lib
+
+
+# ---- lightning indexer (include/mla_indexer.h) ------------------------------
+def indexer_page_layout(dim: int = INDEXER_DIM):
+    pb, so = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("mla_indexer_page_layout", _lib.mla_indexer_page_layout(int(dim), ctypes.byref(pb), ctypes.byref(so)))
+    return int(pb.value), int(so.value)
+
+
+def mla_indexer_scores(q_idx, w_idx, key_pool, block_table, seq_lens, scores, stream=None):
+    """scores [B, score_stride] float32 <- I(b, s) for the cached positions."""
+    torch = _torch()
+    B, H, D = q_idx.shape
+    page_bytes, _ = indexer_page_layout(D)
+    if key_pool.dtype != torch.uint8 or key_pool.dim() != 2 or key_pool.shape[1] != page_bytes:
+        raise ValueError(f"key_pool must be uint8 [num_pages, {page_bytes}]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [batch, stride]")
+    if scores.dim() != 2 or scores.shape[0] != B:
+        raise ValueError("scores must be float32 [batch, stride]")
+    st = _lib.mla_indexer_scores(
+        H, D, _dev(q_idx, "q_idx", torch.bfloat16), _dev(w_idx, "w_idx", torch.float32, (B, H)),
+        _dev(key_pool, "key_pool"), int(key_pool.shape[0]), _dev(block_table, "block_table", torch.int32),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, (B,)), B,
+        _dev(scores, "scores", torch.float32), int(scores.shape[1]), _stream(stream))
+    _check("mla_indexer_scores", st)
+
+
+def topk_workspace_bytes(batch: int) -> int:
+    return int(_lib.mla_topk_workspace_bytes(int(batch)))
+
+
+def mla_topk_select(scores, seq_lens, k: int, idx_out, workspace, stream=None):
+    """idx_out [B, k] int32 <- the k best positions of each score row, in
+    increasing order, -1 padded."""
+    torch = _torch()
+    B = scores.shape[0]
+    st = _lib.mla_topk_select(
+        _dev(scores, "scores", torch.float32), int(scores.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, (B,)),
+        B, int(k), _dev(idx_out, "idx_out", torch.int32, (B, k)), _dev(workspace, "workspace"),
+        int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check("mla_topk_select", st)

@@ -33,7 +33,9 @@ SOURCES = [
     ("decode_attn_f32.hip", True),
     ("combine.hip", True),
     ("head_gemm.hip", True),
+    ("indexer.hip", True),
     ("mla_api.cpp", False),
+    ("indexer_api.cpp", False),
 ]
 
 

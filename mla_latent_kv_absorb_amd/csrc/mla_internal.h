@@ -68,6 +68,36 @@ struct HeadGemmArgs {
   int32_t batch, H, M, K;
 };
 
+// lightning indexer scores: 64 heads x 128, FP8 search keys with one
+// float32 scale per position
+struct IndexerArgs {
+  const void* q;            // [batch][64][128] BF16
+  const float* w;           // [batch][64]
+  const uint8_t* pool;      // search-key pages
+  int64_t num_pages, page_bytes, scale_off;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  int32_t batch;
+  float* scores;            // [batch][score_stride]
+  int64_t score_stride;
+};
+
+// top-k pick over score rows
+struct TopkArgs {
+  const float* scores;
+  int64_t score_stride;
+  const int32_t* seq_lens;
+  int32_t batch;
+  int32_t k;
+  int32_t* idx_out;         // [batch][k]
+  uint32_t* hist;           // workspace: [batch][2048]
+};
+
+hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t s);
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
+size_t topk_workspace_bytes(int32_t batch);
+
 // latent storage of the MFMA attention kernels
 enum class CacheKind { kBf16, kFp8Token, kFp8Group128 };
 

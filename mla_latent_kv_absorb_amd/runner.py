@@ -131,3 +131,36 @@ class DeviceWorkload:
             o = ws[: n_o * 2].view(torch.bfloat16).view(slots, H, DC).float()
         l = ws[o_bytes: o_bytes + slots * H * 4].view(torch.float32).view(slots, H)
         return o, l
+
+
+class IndexerWorkload:
+    """Device buffers of one lightning-indexer workload: queries, head
+    weights, the paged FP8 search-key pool, the score rows and the picked
+    index lists, with the two calls (scores, then top-k pick)."""
+
+    def __init__(self, inp: I.IndexerInputs, device="cuda", score_stride=None, pool=None, table=None):
+        import torch
+        self.inp = inp
+        if pool is None:
+            pool, table = I.build_key_pool(inp)
+        self.pool = torch.from_numpy(pool).to(device)
+        self.table = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(device)
+        self.seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(device)
+        self.q = to_device_act(inp.q_idx, I.DTYPE_BF16, device)
+        self.w = torch.from_numpy(np.ascontiguousarray(inp.w_idx, dtype=np.float32)).to(device)
+        stride = int(inp.seq_lens.max()) if score_stride is None else int(score_stride)
+        self.scores = torch.empty((inp.B, stride), dtype=torch.float32, device=device)
+        self.k = int(inp.topk)
+        self.idx = torch.empty((inp.B, self.k), dtype=torch.int32, device=device)
+        self.workspace = torch.empty(B.topk_workspace_bytes(inp.B), dtype=torch.uint8, device=device)
+
+    def score(self, stream=None):
+        B.mla_indexer_scores(self.q, self.w, self.pool, self.table, self.seq_lens, self.scores, stream)
+
+    def select(self, stream=None, scores=None):
+        B.mla_topk_select(self.scores if scores is None else scores, self.seq_lens, self.k, self.idx,
+                          self.workspace, stream)
+
+    def step(self, stream=None):
+        self.score(stream)
+        self.select(stream)

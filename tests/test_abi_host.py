@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mla_absorb.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("mla_absorb.h", "mla_indexer.h")]
 
 
 @pytest.fixture(scope="module")
@@ -20,9 +20,11 @@ def B():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -149,3 +151,22 @@ def test_binding_rejects_bad_tensors(B):
     cfg = v2(B)
     with pytest.raises(ValueError):
         B.mla_absorb_q(cfg, torch.zeros(1, 128, 128), torch.zeros(128, 512, 128), torch.zeros(1, 128, 512))
+
+
+def test_indexer_layout_and_validation(B):
+    # 128 E4M3 values + one float32 scale per position: 132 B, 8,448 per page
+    assert B.indexer_page_layout(128) == (8448, 8192)
+    assert B.topk_workspace_bytes(32) == 32 * 2048 * 4
+    assert B.topk_workspace_bytes(0) == 0
+    lib = B.raw_lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    null = None
+    # unsupported dims, then bad arguments: nothing is launched
+    assert lib.mla_indexer_scores(32, 128, p, p, p, 1, p, 1, p, 1, p, 1, null) == B.MLA_ERR_UNSUPPORTED
+    assert lib.mla_indexer_scores(64, 128, null, p, p, 1, p, 1, p, 1, p, 1, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_indexer_scores(64, 128, p, p, p, 1, p, 1, p, 0, p, 1, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_indexer_scores(64, 128, p, p, p, 1, p, 1, p, 1, p, 0, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_topk_select(p, 16, p, 2, 0, p, p, 1 << 16, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_topk_select(p, 16, p, 2, 4, p, p, 100, null) == B.MLA_ERR_INVALID_ARG   # workspace too small
+    assert lib.mla_topk_select(null, 16, p, 2, 4, p, p, 1 << 16, null) == B.MLA_ERR_INVALID_ARG
