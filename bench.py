@@ -18,7 +18,9 @@ the matrix-core utilisation of the attention and the weight rate of the two
 head GEMMs ("parts"), and a plain streaming read for reference.  --long adds
 one layer of the long-context workload (1 request x 131,072 positions);
 --fp8-topk adds the FP8-cache, top-2,048 workload, with one scale per token
-and, from the same draw, with one scale per 128 latent channels.
+and, from the same draw, with one scale per 128 latent channels.  --indexer
+adds the lightning indexer scan and top-k pick over 32 x 65,536 positions
+(and, with --fp8-topk, the whole sparse decode step fed by its picks).
 """
 
 from __future__ import annotations
@@ -193,6 +195,64 @@ def fp8_topk_step(torch, I, runner, num_cus, inp, lists=8, reps=10):
             "tokens_per_s": round(inp.B / (step_us * 1e-6), 1), "workers": w.plan.num_workers}
 
 
+def indexer_step(torch, I, runner, reps=10, layers=4, attn=None):
+    """The lightning indexer over 32 requests x 65,536 positions (64 heads x
+    128, FP8 search keys, 132 B per position), then the top-2,048 pick.  Four
+    independent draws (277 MB of keys each) are cycled so the scans read HBM.
+    With ``attn`` (an FP8 top-k DeviceWorkload of the same shape) it also
+    times the whole sparse decode step: scores, pick, absorb, attention over
+    the picked positions, merge + up-projection."""
+    ws = []
+    for layer in range(layers):
+        inp = I.make_indexer_inputs(seed=600 + layer)
+        ws.append(runner.IndexerWorkload(inp))
+    key_bytes = I.key_bytes_read(inp)
+    n_pos = int(np.sum(inp.seq_lens.astype(np.int64)))
+    flop = float(n_pos) * 2 * inp.H_I * inp.d_I
+    for w in ws:
+        w.step()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        for w in ws:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            w.score()
+            e[1].record()
+            w.select()
+            e[2].record()
+            ev.append(e)
+    torch.cuda.synchronize()
+    score_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    select_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    res = {"score_us": round(score_us, 2), "select_us": round(select_us, 2),
+           "key_bytes_per_step": int(key_bytes),
+           "score_key_GBps": round(key_bytes / (score_us * 1e-6) / 1e9, 1),
+           "score_hbm_frac": round(key_bytes / (score_us * 1e-6) / (HBM_PEAK_GBPS * 1e9), 4),
+           "score_mfma_util": round(flop / (score_us * 1e-6) / BF16_PEAK_FLOPS, 4)}
+    if attn is not None:
+        # the picked lists of each draw drive the attention over the FP8 cache
+        for w in ws:
+            w.step()
+            attn.topk_idx = w.idx
+            attn.step_fused()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            for w in ws:
+                w.step()
+                attn.topk_idx = w.idx
+                attn.step_fused()
+        b.record()
+        torch.cuda.synchronize()
+        step_us = a.elapsed_time(b) * 1e3 / (reps * layers)
+        res["sparse_decode_step_us"] = round(step_us, 2)
+        res["sparse_decode_tokens_per_s"] = round(inp.B / (step_us * 1e-6), 1)
+        res["sparse_decode_cache"] = attn.inp.cache_dtype
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +263,9 @@ def main():
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--long", action="store_true",
                     help="also time one layer of the long-context workload (1 request, 131,072 positions)")
+    ap.add_argument("--indexer", action="store_true",
+                    help="also time the lightning indexer and top-k pick (32 x 65,536 positions), and with "
+                         "--fp8-topk the whole sparse decode step")
     ap.add_argument("--fp8-topk", action="store_true",
                     help="also time the FP8-cache, top-2,048 workload (32 requests x 65,536 positions)")
     args = ap.parse_args()
@@ -292,8 +355,14 @@ def main():
         # latent channels (the 656-byte item)
         fp8_inp = I.make_inputs("v2_fp8_topk")
         fp8 = fp8_topk_step(torch, I, runner, num_cus, fp8_inp)
-        fp8g = fp8_topk_step(torch, I, runner, num_cus, I.requantize(fp8_inp, I.DTYPE_FP8_G128))
+        g_inp = I.requantize(fp8_inp, I.DTYPE_FP8_G128)
         del fp8_inp
+        fp8g = fp8_topk_step(torch, I, runner, num_cus, g_inp)
+    idx = None
+    if args.indexer:
+        attn = runner.DeviceWorkload(g_inp, split=True, num_cus=num_cus) if args.fp8_topk else None
+        idx = indexer_step(torch, I, runner, attn=attn)
+        del attn
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -344,6 +413,8 @@ def main():
     if fp8 is not None:
         result["fp8_topk_step"] = fp8
         result["fp8_g128_topk_step"] = fp8g
+    if idx is not None:
+        result["indexer_step"] = idx
     print(json.dumps(result), flush=True)
 
 

@@ -62,9 +62,12 @@ mla_status mla_indexer_scores(int32_t n_heads, int32_t dim, const void* q_idx, c
                               int32_t block_table_stride, const int32_t* seq_lens, int32_t batch,
                               float* scores, int64_t score_stride, void* stream);
 
-/* Workspace bytes mla_topk_select needs for `batch` requests (a histogram
- * per request; the call clears it itself). */
-size_t mla_topk_workspace_bytes(int32_t batch);
+/* Workspace bytes mla_topk_select needs for `batch` score rows of
+ * `score_stride` entries: per request a histogram, per-chunk counters and
+ * room to gather up to a whole row of candidates (8 bytes per entry).  The
+ * call clears what must start at zero itself.  0 for batch < 1 or
+ * score_stride < 1. */
+size_t mla_topk_workspace_bytes(int32_t batch, int64_t score_stride);
 
 /* Step 2: pick, per request b, min(k, T_b) positions among 0 .. T_b - 1
  * (T_b = min(seq_lens[b], score_stride); negative lengths count as 0) with the
@@ -72,9 +75,11 @@ size_t mla_topk_workspace_bytes(int32_t batch);
  * idx_out [batch][k] int32 receives them in increasing position order, then
  * -1 up to k: the index-list format mla_decode_attn takes.
  *   -0 and +0 count as equal; NaN ranks below every other value.
- *   workspace: mla_topk_workspace_bytes(batch) bytes, 16-byte aligned.
+ *   workspace: mla_topk_workspace_bytes(batch, score_stride) bytes,
+ *   16-byte aligned.  Calls that share a workspace must not overlap.
  * Errors: null or misaligned pointers, batch < 1, k < 1, score_stride < 1, a
- * too small workspace -> MLA_ERR_INVALID_ARG. */
+ * too small workspace -> MLA_ERR_INVALID_ARG; score_stride above 8,388,608
+ * -> MLA_ERR_UNSUPPORTED. */
 mla_status mla_topk_select(const float* scores, int64_t score_stride, const int32_t* seq_lens, int32_t batch,
                            int32_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
                            void* stream);

@@ -74,7 +74,7 @@ def _load():
         "mla_check_decode_inputs_host": ([cfgp, I32, i32p, i32p, I32, I64, i32p, I32, i32p], I32),
         "mla_indexer_page_layout": ([I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
         "mla_indexer_scores": ([I32, I32, P, P, P, I64, P, I32, P, I32, P, I64, P], I32),
-        "mla_topk_workspace_bytes": ([I32], SZ),
+        "mla_topk_workspace_bytes": ([I32, I64], SZ),
         "mla_topk_select": ([P, I64, P, I32, I32, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
@@ -283,8 +283,8 @@ def mla_indexer_scores(q_idx, w_idx, key_pool, block_table, seq_lens, scores, st
     _check("mla_indexer_scores", st)
 
 
-def topk_workspace_bytes(batch: int) -> int:
-    return int(_lib.mla_topk_workspace_bytes(int(batch)))
+def topk_workspace_bytes(batch: int, score_stride: int) -> int:
+    return int(_lib.mla_topk_workspace_bytes(int(batch), int(score_stride)))
 
 
 def mla_topk_select(scores, seq_lens, k: int, idx_out, workspace, stream=None):

@@ -18,13 +18,15 @@
 // permutation, which leaves every dot product unchanged.
 //
 // Pick: radix selection on an order-preserving 32-bit image of the scores
-// (11 + 11 + 10 bits from the top).  The first digit's histogram is built by
-// many work-groups at once (a chip-wide pass with LDS histograms flushed by
-// global atomics), so its crowded top bins do not serialise one CU's LDS
-// atomics; one work-group per request then finds the digit holding the k-th
-// largest score, refines the two lower digits over the positions that still
-// match, and writes the picked positions in increasing order with a block
-// prefix sum (equal scores: the lowest positions first).
+// (11 + 11 + 10 bits from the top), spread over the chip in chunks of 4,096
+// positions: (1) each chunk adds its first-digit histogram into the
+// request's; (2) each chunk finds the digit holding the k-th largest score,
+// counts its keys above that digit and gathers the keys in that digit's bin;
+// (3) one work-group per request refines the two lower digits among the
+// gathered keys -- the threshold key -- and turns per-chunk counts into
+// per-chunk output offsets (equal keys are taken by position); (4) each chunk
+// writes its picks in increasing order with a block prefix sum.  No work-group
+// walks a whole row.
 #include "attn_common.h"
 
 namespace mla {
@@ -75,49 +77,97 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
   float* out = a.scores + (int64_t)b * a.score_stride;
   const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
 
-  // wave w takes the half pages w, w + 4, ... of the chunk (32 positions each)
-  for (int hp = w; hp < 2 * kIdxChunkPages; hp += 4) {
+  // Wave w takes the half pages w, w + 4, ... of the chunk (32 positions
+  // each); the keys of the next half page are loaded while the current one is
+  // contracted.
+  struct Keys {
+    i32x4 r[4];
+    float sc;
+    bool ok;
+  };
+  auto fetch = [&](int hp, Keys& k) {
     const int64_t p = p0 + (hp >> 1);
-    const int64_t pos0 = p * 64 + 32 * (hp & 1);
-    if (pos0 >= T) break;  // wave-uniform; later half pages are further out
     const int32_t page = sload(bt + p);
-    const int64_t pos = pos0 + col;
-    if (page < 0 || page >= a.num_pages) {
-      if (hl == 0 && pos < T) out[pos] = -INFINITY;
-      continue;
-    }
-    const uint8_t* pg = a.pool + (int64_t)page * a.page_bytes;
+    k.ok = page >= 0 && page < a.num_pages;
+    const uint8_t* pg = a.pool + (k.ok ? (int64_t)page * a.page_bytes : 0);
     const int slot = 32 * (hp & 1) + col;
     const i32x4* src = (const i32x4*)(pg + slot * kIdxKeyRow + 64 * hl);
-    const i32x4 r0 = src[0], r1 = src[1], r2 = src[2], r3 = src[3];
-    const float sc = *(const float*)(pg + a.scale_off + 4 * slot);
-    const uint32_t raw[16] = {(uint32_t)r0[0], (uint32_t)r0[1], (uint32_t)r0[2], (uint32_t)r0[3],
-                              (uint32_t)r1[0], (uint32_t)r1[1], (uint32_t)r1[2], (uint32_t)r1[3],
-                              (uint32_t)r2[0], (uint32_t)r2[1], (uint32_t)r2[2], (uint32_t)r2[3],
-                              (uint32_t)r3[0], (uint32_t)r3[1], (uint32_t)r3[2], (uint32_t)r3[3]};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) k.r[m] = src[m];
+    k.sc = *(const float*)(pg + a.scale_off + 4 * slot);
+  };
+  auto in_range = [&](int hp) { return hp < 2 * kIdxChunkPages && (p0 + (hp >> 1)) * 64 + 32 * (hp & 1) < T; };
+
+  if (!in_range(w)) return;
+  Keys cur, nxt;
+  fetch(w, cur);
+  for (int hp = w; in_range(hp); hp += 4) {
+    const bool more = in_range(hp + 4);
+    if (more) fetch(hp + 4, nxt);
+    const int64_t pos = (p0 + (hp >> 1)) * 64 + 32 * (hp & 1) + col;
     f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const bf16x8 kv = e4m3x8_to_bf16(raw[2 * kb], raw[2 * kb + 1]);
+      const bf16x8 kv = e4m3x8_to_bf16((uint32_t)cur.r[kb >> 1][2 * (kb & 1)], (uint32_t)cur.r[kb >> 1][2 * (kb & 1) + 1]);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][kb], kv, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][kb], kv, acc1, 0, 0, 0);
     }
-    float s = 0.f;
+    float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s = fmaf(wt[0][r], fmaxf(acc0[r], 0.f), s);
-      s = fmaf(wt[1][r], fmaxf(acc1[r], 0.f), s);
+      sum = fmaf(wt[0][r], fmaxf(acc0[r], 0.f), sum);
+      sum = fmaf(wt[1][r], fmaxf(acc1[r], 0.f), sum);
     }
-    s += wave_partner(s);  // the other 32 heads of this position
-    if (hl == 0 && pos < T) out[pos] = s * sc;
+    sum += wave_partner(sum);  // the other 32 heads of this position
+    // a position on a page id out of range scores -infinity (its loads went
+    // to page 0 and are discarded)
+    if (hl == 0 && pos < T) out[pos] = cur.ok ? sum * cur.sc : -INFINITY;
+    if (more) cur = nxt;
   }
 }
 
 // ---- top-k pick ----
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
+// Workspace sections (uint32, per request b):
+//   hist [b][2048]   first-digit histogram
+//   ctrl [b][16]     0: candidates gathered, 1: first digit, 2: picks left
+//                    after it, 3: threshold key, 4: equal keys to take
+//   gt0  [b][C]      per chunk: keys whose first digit is above the threshold's
+//   off  [b][C]      per chunk: output offset of its first pick
+//   take [b][C]      per chunk: threshold-equal keys it contributes
+//   ckey, cpos [b][stride]  keys and positions of the threshold digit's bin
+// with C = ceil(stride / 4096) chunks.
 constexpr int kHistBins = 2048;            // first and second digit: 11 bits
-constexpr int kHistChunk = 4096;           // scores per histogram work-group
+constexpr int kChunk = 4096;               // positions per chunk work-group
+constexpr int kCtrl = 16;
+constexpr int kRefineThreads = 1024;
+constexpr int kMaxChunks = 2048;           // rows up to 8,388,608 positions
+
+struct TopkSpace {
+  uint32_t *hist, *ctrl, *gt0, *off, *take, *ckey, *cpos;
+  int64_t nchunks;
+};
+
+__device__ __host__ inline int64_t topk_chunks(int64_t stride) { return (stride + kChunk - 1) / kChunk; }
+
+__device__ __forceinline__ TopkSpace topk_space(const TopkArgs& a) {
+  TopkSpace w;
+  w.nchunks = topk_chunks(a.score_stride);
+  uint32_t* p = a.hist;
+  w.hist = p;
+  p += (int64_t)a.batch * kHistBins;
+  w.ctrl = p;
+  p += (int64_t)a.batch * kCtrl;
+  w.gt0 = p;
+  p += (int64_t)a.batch * w.nchunks;
+  w.off = p;
+  p += (int64_t)a.batch * w.nchunks;
+  w.take = p;
+  p += (int64_t)a.batch * w.nchunks;
+  w.ckey = p;
+  p += (int64_t)a.batch * a.score_stride;
+  w.cpos = p;
+  return w;
+}
 
 // order-preserving image of a float: larger score -> larger key; -0 == +0;
 // NaN below everything
@@ -135,32 +185,11 @@ __device__ __forceinline__ int64_t sel_len(const TopkArgs& a, int b) {
   return T;
 }
 
-__global__ __launch_bounds__(256) void topk_clear_kernel(uint32_t* hist, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) hist[i] = 0u;
-}
-
-// first digit (top 11 bits of the key) of every score, per request
-__global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a) {
-  __shared__ uint32_t h[kHistBins];
-  const int b = blockIdx.y;
-  const int64_t T = sel_len(a, b);
-  const int64_t i0 = (int64_t)blockIdx.x * kHistChunk;
-  if (T <= a.k || i0 >= T) return;  // nothing to select in this request or chunk
-  for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0u;
-  __syncthreads();
-  const float* s = a.scores + (int64_t)b * a.score_stride;
-  const int64_t i1 = i0 + kHistChunk < T ? i0 + kHistChunk : T;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) atomicAdd(&h[score_key(s[i]) >> 21], 1u);
-  __syncthreads();
-  uint32_t* g = a.hist + (int64_t)b * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += 256)
-    if (h[i] != 0u) atomicAdd(&g[i], h[i]);
-}
-
-// exclusive prefix sum over the work-group in thread order; `total` gets the
-// sum over all threads.  Every thread must call it.
+// exclusive prefix sum over a work-group of NT threads in thread order;
+// `total` gets the sum over all threads.  Every thread must call it.
+template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wave_tot, uint32_t& total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -172,7 +201,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wave_t
   __syncthreads();
   uint32_t off = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const uint32_t t = wave_tot[i];
     off += i < wv ? t : 0u;
     tot += t;
@@ -182,17 +211,18 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wave_t
   return off + x - v;
 }
 
-// Given a histogram of `nbins` bins (LDS) and kleft >= 1 keys still to pick
-// from it, find the bin holding the kleft-th largest: returns the bin and, in
-// `above`, how many keys lie in higher bins.  Threads take bins from the top.
+// Given a histogram of `nbins` bins and kleft >= 1 keys still to pick from
+// it, find the bin holding the kleft-th largest: returns the bin, and in
+// *s_above how many keys lie in higher bins.  Threads take bins from the top.
+template <int NT>
 __device__ __forceinline__ int find_digit(const uint32_t* h, int nbins, uint32_t kleft, uint32_t* wave_tot,
                                           int* s_digit, uint32_t* s_above) {
-  const int per = nbins / kSelThreads;  // 2 or 1
+  const int per = nbins / NT;
   const int t = threadIdx.x;
   uint32_t loc = 0;
   for (int e = 0; e < per; ++e) loc += h[nbins - 1 - (per * t + e)];
   uint32_t total;
-  uint32_t above = block_excl_scan(loc, wave_tot, total);
+  uint32_t above = block_excl_scan<NT>(loc, wave_tot, total);
   for (int e = 0; e < per; ++e) {
     const int bin = nbins - 1 - (per * t + e);
     const uint32_t c = h[bin];
@@ -206,65 +236,242 @@ __device__ __forceinline__ int find_digit(const uint32_t* h, int nbins, uint32_t
   return *s_digit;
 }
 
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
+__global__ __launch_bounds__(256) void topk_clear_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// 1. first digit (top 11 bits of the key) of every score, per request
+__global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a) {
   __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t wave_tot[kSelWaves];
+  const int b = blockIdx.y;
+  const int64_t T = sel_len(a, b);
+  const int64_t i0 = (int64_t)blockIdx.x * kChunk;
+  if (T <= a.k || i0 >= T) return;  // nothing to select in this request or chunk
+  for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0u;
+  __syncthreads();
+  const float* s = a.scores + (int64_t)b * a.score_stride;
+  const int64_t i1 = i0 + kChunk < T ? i0 + kChunk : T;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) atomicAdd(&h[score_key(s[i]) >> 21], 1u);
+  __syncthreads();
+  uint32_t* g = topk_space(a).hist + (int64_t)b * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += 256)
+    if (h[i] != 0u) atomicAdd(&g[i], h[i]);
+}
+
+// four consecutive keys from position i (keys past n are 0 and flagged out)
+__device__ __forceinline__ void keys4(const float* s, int64_t i, int64_t n, bool vec_ok, uint32_t (&key)[4]) {
+  if (vec_ok && i + 3 < n) {
+    const f32x4 v = *(const f32x4*)(s + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[e] = score_key(v[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[e] = i + e < n ? score_key(s[i + e]) : 0u;
+  }
+}
+
+// 2. per chunk: the keys above the threshold's first digit are counted, the
+// keys in its bin are gathered (with their positions) for the refinement
+__global__ __launch_bounds__(256) void topk_gather_kernel(TopkArgs a) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t wave_tot[4];
+  __shared__ int s_digit;
+  __shared__ uint32_t s_above;
+  const int b = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t T = sel_len(a, b);
+  const TopkSpace w = topk_space(a);
+  if (T <= a.k) {
+    // every visible position, then padding (one work-group per request)
+    if (c == 0) {
+      int32_t* out = a.idx_out + (int64_t)b * a.k;
+      for (int64_t i = t; i < a.k; i += 256) out[i] = i < T ? (int32_t)i : -1;
+    }
+    return;
+  }
+  const int64_t i0 = c * kChunk;
+  if (i0 >= T) return;
+  const uint32_t* g = w.hist + (int64_t)b * kHistBins;
+  for (int i = t; i < kHistBins; i += 256) h[i] = g[i];
+  __syncthreads();
+  const uint32_t d0 = (uint32_t)find_digit<256>(h, kHistBins, (uint32_t)a.k, wave_tot, &s_digit, &s_above);
+  uint32_t* ctrl = w.ctrl + (int64_t)b * kCtrl;
+  if (c == 0 && t == 0) {
+    ctrl[1] = d0;
+    ctrl[2] = (uint32_t)a.k - s_above;
+  }
+  const float* s = a.scores + (int64_t)b * a.score_stride;
+  const bool vec_ok = (((uintptr_t)s) & 15) == 0;
+  uint32_t* ckey = w.ckey + (int64_t)b * a.score_stride;
+  uint32_t* cpos = w.cpos + (int64_t)b * a.score_stride;
+  // this thread's 16 keys: four groups of four consecutive positions
+  uint32_t key[kChunk / 1024][4];
+#pragma unroll
+  for (int sb = 0; sb < kChunk / 1024; ++sb) keys4(s, i0 + 1024 * sb + 4 * t, T, vec_ok, key[sb]);
+  uint32_t ngt = 0, nin = 0;
+#pragma unroll
+  for (int sb = 0; sb < kChunk / 1024; ++sb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = i0 + 1024 * sb + 4 * t + e < T;
+      ngt += (ok && (key[sb][e] >> 21) > d0) ? 1u : 0u;
+      nin += (ok && (key[sb][e] >> 21) == d0) ? 1u : 0u;
+    }
+  // one counter update per work-group reserves the chunk's candidate slots
+  uint32_t nin_tot;
+  uint32_t slot = block_excl_scan<256>(nin, wave_tot, nin_tot);
+  if (t == 0) s_above = nin_tot != 0u ? atomicAdd(&ctrl[0], nin_tot) : 0u;
+  __syncthreads();
+  slot += s_above;
+  if (nin != 0u) {
+#pragma unroll
+    for (int sb = 0; sb < kChunk / 1024; ++sb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + 1024 * sb + 4 * t + e;
+        if (i < T && (key[sb][e] >> 21) == d0) {
+          ckey[slot] = key[sb][e];
+          cpos[slot] = (uint32_t)i;
+          ++slot;
+        }
+      }
+  }
+  uint32_t total;
+  block_excl_scan<256>(ngt, wave_tot, total);
+  if (t == 0) w.gt0[(int64_t)b * w.nchunks + c] = total;
+}
+
+// 3. per request: the two lower digits among the gathered keys give the
+// threshold key; then each chunk's share of the output and its offset
+__global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(TopkArgs a) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t cg[kMaxChunks], ce[kMaxChunks];
+  __shared__ uint32_t wave_tot[kRefineThreads / 64];
   __shared__ int s_digit;
   __shared__ uint32_t s_above;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int64_t T = sel_len(a, b);
-  const int k = a.k;
-  int32_t* out = a.idx_out + (int64_t)b * k;
-  const float* s = a.scores + (int64_t)b * a.score_stride;
-
-  if (T <= k) {
-    // every visible position, then padding
-    for (int64_t i = t; i < k; i += kSelThreads) out[i] = i < T ? (int32_t)i : -1;
-    return;
-  }
-
-  // digit 1 (bits 31..21): the chip-wide histogram
-  const uint32_t* g = a.hist + (int64_t)b * kHistBins;
-  for (int i = t; i < kHistBins; i += kSelThreads) h[i] = g[i];
-  __syncthreads();
-  uint32_t kleft = (uint32_t)k;
-  uint32_t prefix = (uint32_t)find_digit(h, kHistBins, kleft, wave_tot, &s_digit, &s_above) << 21;
-  kleft -= s_above;
+  if (T <= a.k) return;
+  const TopkSpace w = topk_space(a);
+  uint32_t* ctrl = w.ctrl + (int64_t)b * kCtrl;
+  const uint32_t nc = ctrl[0];
+  uint32_t prefix = ctrl[1] << 21;
+  uint32_t kleft = ctrl[2];
   uint32_t mask = 0xFFE00000u;
-
-  // digits 2 (bits 20..10) and 3 (bits 9..0) over the keys that still match
+  const uint32_t* ckey = w.ckey + (int64_t)b * a.score_stride;
+  const uint32_t* cpos = w.cpos + (int64_t)b * a.score_stride;
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
     const int nbins = pass == 0 ? 2048 : 1024;
-    for (int i = t; i < nbins; i += kSelThreads) h[i] = 0u;
+    for (int i = t; i < nbins; i += kRefineThreads) h[i] = 0u;
     __syncthreads();
-    for (int64_t i = t; i < T; i += kSelThreads) {
-      const uint32_t key = score_key(s[i]);
+    for (uint32_t i = t; i < nc; i += kRefineThreads) {
+      const uint32_t key = ckey[i];
       if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
     }
     __syncthreads();
-    prefix |= (uint32_t)find_digit(h, nbins, kleft, wave_tot, &s_digit, &s_above) << shift;
+    prefix |= (uint32_t)find_digit<kRefineThreads>(h, nbins, kleft, wave_tot, &s_digit, &s_above) << shift;
     kleft -= s_above;
     mask |= (uint32_t)(nbins - 1) << shift;
-    __syncthreads();  // s_digit / s_above are rewritten by the next pass
+    __syncthreads();
   }
-
-  // The k-th largest key is `prefix`; every larger key is picked, and the
-  // first `kleft` equal ones by position.  Positions are visited in order and
-  // each picked one lands at its rank among the picked: increasing order.
   const uint32_t thr = prefix;
+  // gathered keys above / equal to the threshold, per chunk
+  const int64_t nch = (T + kChunk - 1) / kChunk;
+  for (int64_t i = t; i < nch; i += kRefineThreads) {
+    cg[i] = 0u;
+    ce[i] = 0u;
+  }
+  __syncthreads();
+  for (uint32_t i = t; i < nc; i += kRefineThreads) {
+    const uint32_t key = ckey[i];
+    const uint32_t ch = cpos[i] / kChunk;
+    if (key > thr) atomicAdd(&cg[ch], 1u);
+    else if (key == thr) atomicAdd(&ce[ch], 1u);
+  }
+  __syncthreads();
+  // thread t owns chunks 2t, 2t + 1: the first `kleft` equal keys in
+  // position order are taken, chunk by chunk
+  uint32_t eqs[2], tot[2];
+  uint32_t leq = 0;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int64_t ch = 2 * t + e;
+    eqs[e] = ch < nch ? ce[ch] : 0u;
+    leq += eqs[e];
+  }
+  uint32_t unused;
+  uint32_t eq_before = block_excl_scan<kRefineThreads>(leq, wave_tot, unused);
+  uint32_t take[2];
+  uint32_t ltot = 0;
+  const uint32_t* gt0 = w.gt0 + (int64_t)b * w.nchunks;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int64_t ch = 2 * t + e;
+    take[e] = eq_before >= kleft ? 0u : (kleft - eq_before < eqs[e] ? kleft - eq_before : eqs[e]);
+    eq_before += eqs[e];
+    tot[e] = ch < nch ? gt0[ch] + cg[ch] + take[e] : 0u;
+    ltot += tot[e];
+  }
+  uint32_t off = block_excl_scan<kRefineThreads>(ltot, wave_tot, unused);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int64_t ch = 2 * t + e;
+    if (ch < nch) {
+      w.off[(int64_t)b * w.nchunks + ch] = off;
+      w.take[(int64_t)b * w.nchunks + ch] = take[e];
+    }
+    off += tot[e];
+  }
+  if (t == 0) ctrl[3] = thr;
+}
+
+// 4. per chunk: picked positions (keys above the threshold, and the chunk's
+// share of the equal ones, first by position) in increasing order
+__global__ __launch_bounds__(256) void topk_write_kernel(TopkArgs a) {
+  __shared__ uint32_t wave_tot[4];
+  const int b = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t T = sel_len(a, b);
+  if (T <= a.k) return;
+  const int64_t i0 = c * kChunk;
+  if (i0 >= T) return;
+  const TopkSpace w = topk_space(a);
+  const uint32_t thr = w.ctrl[(int64_t)b * kCtrl + 3];
+  const uint32_t base = w.off[(int64_t)b * w.nchunks + c];
+  const uint32_t take = w.take[(int64_t)b * w.nchunks + c];
+  const float* s = a.scores + (int64_t)b * a.score_stride;
+  const bool vec_ok = (((uintptr_t)s) & 15) == 0;
+  int32_t* out = a.idx_out + (int64_t)b * a.k;
   uint32_t gt_run = 0, eq_run = 0;
-  for (int64_t base = 0; base < T; base += kSelThreads) {
-    const int64_t i = base + t;
-    const uint32_t key = i < T ? score_key(s[i]) : 0u;
-    const bool gt = i < T && key > thr;
-    const bool eq = i < T && key == thr;
+  for (int sb = 0; sb < kChunk / 1024; ++sb) {
+    const int64_t i = i0 + 1024 * sb + 4 * t;
+    uint32_t key[4];
+    keys4(s, i, T, vec_ok, key);
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ngt += (i + e < T && key[e] > thr) ? 1u : 0u;
+      neq += (i + e < T && key[e] == thr) ? 1u : 0u;
+    }
     uint32_t total;
-    const uint32_t ex = block_excl_scan((gt ? 0x10000u : 0u) | (eq ? 1u : 0u), wave_tot, total);
-    const uint32_t gt_before = gt_run + (ex >> 16), eq_before = eq_run + (ex & 0xFFFFu);
-    if (gt) out[gt_before + (eq_before < kleft ? eq_before : kleft)] = (int32_t)i;
-    if (eq && eq_before < kleft) out[gt_before + eq_before] = (int32_t)i;
+    const uint32_t ex = block_excl_scan<256>((ngt << 16) | neq, wave_tot, total);
+    uint32_t gt_before = gt_run + (ex >> 16), eq_before = eq_run + (ex & 0xFFFFu);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (i + e >= T) break;
+      if (key[e] > thr) {
+        out[base + gt_before + (eq_before < take ? eq_before : take)] = (int32_t)(i + e);
+        ++gt_before;
+      } else if (key[e] == thr) {
+        if (eq_before < take) out[base + gt_before + eq_before] = (int32_t)(i + e);
+        ++eq_before;
+      }
+    }
     gt_run += total >> 16;
     eq_run += total & 0xFFFFu;
   }
@@ -278,14 +485,22 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t topk_workspace_bytes(int32_t batch) { return (size_t)batch * kHistBins * 4; }
+int64_t topk_max_stride() { return (int64_t)kMaxChunks * kChunk; }
+
+size_t topk_workspace_bytes(int32_t batch, int64_t score_stride) {
+  const int64_t words = (int64_t)batch * (kHistBins + kCtrl + 3 * topk_chunks(score_stride) + 2 * score_stride);
+  return (size_t)words * 4;
+}
 
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.batch * kHistBins;
+  // clear the histograms and the control words (candidate counters)
+  const int64_t n = (int64_t)a.batch * (kHistBins + kCtrl);
   hipLaunchKernelGGL(topk_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.hist, n);
-  const int64_t chunks = (a.score_stride + kHistChunk - 1) / kHistChunk;
-  hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)chunks, a.batch), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(topk_select_kernel, dim3(a.batch), dim3(kSelThreads), 0, s, a);
+  const dim3 chunks((unsigned)topk_chunks(a.score_stride), a.batch);
+  hipLaunchKernelGGL(topk_hist_kernel, chunks, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(topk_gather_kernel, chunks, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(topk_refine_kernel, dim3(a.batch), dim3(kRefineThreads), 0, s, a);
+  hipLaunchKernelGGL(topk_write_kernel, chunks, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -56,7 +56,9 @@ mla_status mla_indexer_scores(int32_t n_heads, int32_t dim, const void* q_idx, c
   return launch_status(mla::launch_indexer_scores(a, (hipStream_t)stream));
 }
 
-size_t mla_topk_workspace_bytes(int32_t batch) { return batch < 1 ? 0 : mla::topk_workspace_bytes(batch); }
+size_t mla_topk_workspace_bytes(int32_t batch, int64_t score_stride) {
+  return batch < 1 || score_stride < 1 ? 0 : mla::topk_workspace_bytes(batch, score_stride);
+}
 
 mla_status mla_topk_select(const float* scores, int64_t score_stride, const int32_t* seq_lens, int32_t batch,
                            int32_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
@@ -66,7 +68,8 @@ mla_status mla_topk_select(const float* scores, int64_t score_stride, const int3
   if (batch < 1 || batch > 65535 || k < 1 || score_stride < 1) return MLA_ERR_INVALID_ARG;
   if (!aligned(scores, 4) || !aligned(seq_lens, 4) || !aligned(idx_out, 4) || !aligned(workspace, 16))
     return MLA_ERR_INVALID_ARG;
-  if (workspace_bytes < mla::topk_workspace_bytes(batch)) return MLA_ERR_INVALID_ARG;
+  if (score_stride > mla::topk_max_stride()) return MLA_ERR_UNSUPPORTED;
+  if (workspace_bytes < mla::topk_workspace_bytes(batch, score_stride)) return MLA_ERR_INVALID_ARG;
   mla::TopkArgs a{};
   a.scores = scores;
   a.score_stride = score_stride;

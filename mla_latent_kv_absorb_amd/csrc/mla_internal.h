@@ -91,12 +91,13 @@ struct TopkArgs {
   int32_t batch;
   int32_t k;
   int32_t* idx_out;         // [batch][k]
-  uint32_t* hist;           // workspace: [batch][2048]
+  uint32_t* hist;           // workspace (layout in the pick kernels)
 };
 
 hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
-size_t topk_workspace_bytes(int32_t batch);
+size_t topk_workspace_bytes(int32_t batch, int64_t score_stride);
+int64_t topk_max_stride();
 
 // latent storage of the MFMA attention kernels
 enum class CacheKind { kBf16, kFp8Token, kFp8Group128 };

@@ -152,7 +152,7 @@ class IndexerWorkload:
         self.scores = torch.empty((inp.B, stride), dtype=torch.float32, device=device)
         self.k = int(inp.topk)
         self.idx = torch.empty((inp.B, self.k), dtype=torch.int32, device=device)
-        self.workspace = torch.empty(B.topk_workspace_bytes(inp.B), dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(B.topk_workspace_bytes(inp.B, stride), dtype=torch.uint8, device=device)
 
     def score(self, stream=None):
         B.mla_indexer_scores(self.q, self.w, self.pool, self.table, self.seq_lens, self.scores, stream)

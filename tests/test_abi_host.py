@@ -156,8 +156,9 @@ def test_binding_rejects_bad_tensors(B):
 def test_indexer_layout_and_validation(B):
     # 128 E4M3 values + one float32 scale per position: 132 B, 8,448 per page
     assert B.indexer_page_layout(128) == (8448, 8192)
-    assert B.topk_workspace_bytes(32) == 32 * 2048 * 4
-    assert B.topk_workspace_bytes(0) == 0
+    # histogram, control words, 3 counters per 4,096-position chunk, gathered keys and positions
+    assert B.topk_workspace_bytes(32, 65536) == 32 * (2048 + 16 + 3 * 16 + 2 * 65536) * 4
+    assert B.topk_workspace_bytes(0, 65536) == 0 and B.topk_workspace_bytes(2, 0) == 0
     lib = B.raw_lib()
     buf = ctypes.create_string_buffer(1 << 16)
     p = ctypes.cast(buf, ctypes.c_void_p)
@@ -170,3 +171,4 @@ def test_indexer_layout_and_validation(B):
     assert lib.mla_topk_select(p, 16, p, 2, 0, p, p, 1 << 16, null) == B.MLA_ERR_INVALID_ARG
     assert lib.mla_topk_select(p, 16, p, 2, 4, p, p, 100, null) == B.MLA_ERR_INVALID_ARG   # workspace too small
     assert lib.mla_topk_select(null, 16, p, 2, 4, p, p, 1 << 16, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_topk_select(p, 2048 * 4096 + 1, p, 1, 4, p, p, 1 << 40, null) == B.MLA_ERR_UNSUPPORTED

@@ -127,7 +127,7 @@ def test_topk_select_bit_exact(torch, R, k):
     scores = torch.from_numpy(s).cuda()
     seq = torch.from_numpy(lens).cuda()
     idx = torch.full((6, k), -7, dtype=torch.int32, device="cuda")
-    ws = torch.empty(B.topk_workspace_bytes(6), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(B.topk_workspace_bytes(6, stride), dtype=torch.uint8, device="cuda")
     for rep in range(2):  # the workspace is reused: the call clears it itself
         B.mla_topk_select(scores, seq, k, idx, ws)
         torch.cuda.synchronize()
@@ -146,7 +146,7 @@ def test_topk_select_long_row_and_zero_length(torch, R):
     lens = np.array([131072, 0], np.int32)
     k = 2048
     idx = torch.empty((2, k), dtype=torch.int32, device="cuda")
-    ws = torch.empty(B.topk_workspace_bytes(2), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(B.topk_workspace_bytes(2, stride), dtype=torch.uint8, device="cuda")
     B.mla_topk_select(torch.from_numpy(s).cuda(), torch.from_numpy(lens).cuda(), k, idx, ws)
     torch.cuda.synchronize()
     got = idx.cpu().numpy()
