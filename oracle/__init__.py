@@ -8,3 +8,4 @@ computes and which passages it follows.
 from .mla_oracle import *  # noqa: F401,F403
 from .mla_oracle import __all__  # noqa: F401
 from . import dsa_indexer  # noqa: F401,E402
+from . import cache_append  # noqa: F401,E402
