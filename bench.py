@@ -195,6 +195,34 @@ def fp8_topk_step(torch, I, runner, num_cus, inp, lists=8, reps=10):
             "tokens_per_s": round(inp.B / (step_us * 1e-6), 1), "workers": w.plan.num_workers}
 
 
+def cache_append_part(torch, I, w, reps=200):
+    """mla_cache_append for the workload's 64 requests (one token each, with
+    RoPE from float32 tables), timed after the decode steps; it rewrites each
+    request's last cached position, so the timed steps are unaffected."""
+    from mla_latent_kv_absorb_amd import binding as B
+    inp = w.inp
+    rows = int(inp.seq_lens.max())
+    theta = 10000.0 ** (-np.arange(0, inp.D_R, 2) / inp.D_R)
+    ang = np.arange(rows)[:, None] * theta[None, :]
+    cos = torch.from_numpy(np.cos(ang).astype(np.float32)).cuda()
+    sin = torch.from_numpy(np.sin(ang).astype(np.float32)).cuda()
+    rng = np.random.default_rng(77)
+    c_new = torch.from_numpy(rng.standard_normal((inp.B, inp.D_C)).astype(np.float32)).cuda().bfloat16()
+    k_new = torch.from_numpy(rng.standard_normal((inp.B, inp.D_R)).astype(np.float32)).cuda().bfloat16()
+    pos = (w.seq_lens - 1).contiguous()
+    call = lambda: B.mla_cache_append(w.cfg, c_new, k_new, pos, w.pool, w.table, cos, sin)
+    call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    return {"us": round(us, 2), "bytes_written": int(inp.B * (inp.D_C + inp.D_R) * 2)}
+
+
 def indexer_step(torch, I, runner, reps=10, layers=4, attn=None):
     """The lightning indexer over 32 requests x 65,536 positions (64 heads x
     128, FP8 search keys, 132 B per position), then the top-2,048 pick.  Four
@@ -347,6 +375,7 @@ def main():
         "attention": {"us": round(attn_avg_ms * 1e3, 2), "mfma_util": round(attn_flop / (attn_avg_ms * 1e-3) / BF16_PEAK_FLOPS, 4)},
         "combine_out_up": gemm(tail_ms, part_bytes + inp.B * inp.H * inp.D_V * 2),
     }
+    parts["cache_append"] = cache_append_part(torch, I, w)
     ceiling = read_ceiling(torch)
     long_layer = long_context_layer(torch, I, runner, num_cus) if args.long else None
     fp8 = fp8g = None

@@ -118,6 +118,36 @@ const char* mla_status_string(mla_status status);
 mla_status mla_page_layout(const mla_config* cfg, size_t* page_bytes, size_t* rope_offset,
                            size_t* scale_offset);
 
+/* Append one new token per request to the cache, before the decode step
+ * that reads it ("DeepSeek's KV Cache", section "MLA: the cache holds one
+ * latent", Figure 3: the latent is stored without rotation, the shared rotary
+ * key with RoPE applied; section "Calculating V3.2's KV cache" for the FP8
+ * item).
+ *   c_new [batch][D_C], k_new [batch][D_R]: activation dtype (16-byte
+ *     aligned); k_new is the rotary key before rotation.
+ *   rope_cos, rope_sin [rope_rows][D_R / 2] float32, or both NULL to store
+ *     k_new as given: pair i (elements 2i, 2i+1) of the key at position p
+ *     becomes (x cos - y sin, x sin + y cos) with cos = rope_cos[p][i],
+ *     sin = rope_sin[p][i].
+ *   positions [batch] int32: the position the token takes; it is written to
+ *     row p % 64 of page block_table[b][p / 64].
+ *   kv_pool, num_pages, block_table, block_table_stride: as mla_decode_attn.
+ * Storage: F32 and BF16 caches store the values (BF16 activations as they
+ * are); FP8 caches store scale = max|c| / 448 over the token (over each 128
+ * channels for MLA_FP8_E4M3_G128; 1 when that maximum is 0) and the E4M3
+ * codes nearest to c / scale (float32 quotient clamped to +-448, ties to
+ * even), the rotary key in BF16 (rounded to nearest even).  Only the token's
+ * row of each section is written.  A request whose position is negative, not
+ * below 64 * block_table_stride (or rope_rows when tables are given), or on a
+ * page id out of range writes nothing.
+ * Errors: null or misaligned pointers, batch < 1, only one table given,
+ * rope_rows < 1 with tables -> MLA_ERR_INVALID_ARG; odd d_rope ->
+ * MLA_ERR_UNSUPPORTED. */
+mla_status mla_cache_append(const mla_config* cfg, const void* c_new, const void* k_new, const float* rope_cos,
+                            const float* rope_sin, int32_t rope_rows, const int32_t* positions, void* kv_pool,
+                            int64_t num_pages, const int32_t* block_table, int32_t block_table_stride,
+                            int32_t batch, void* stream);
+
 /* Choose the number of workers for a batch and size the partial workspace.
  * seq_lens_host: host copy of the per-request lengths (used only to count
  * tiles; may be NULL, then every request is assumed to be max_len long).

@@ -27,7 +27,7 @@ TILE_TOKENS = 32
 EXPORTED = (
     "mla_abi_version", "mla_status_string", "mla_page_layout", "mla_decode_plan",
     "mla_absorb_q", "mla_decode_attn", "mla_combine", "mla_out_up", "mla_combine_out_up",
-    "mla_check_decode_inputs_host",
+    "mla_check_decode_inputs_host", "mla_cache_append",
     "mla_indexer_page_layout", "mla_indexer_scores", "mla_topk_workspace_bytes", "mla_topk_select",
 )
 INDEXER_HEADS, INDEXER_DIM = 64, 128
@@ -72,6 +72,7 @@ def _load():
         "mla_out_up": ([cfgp, P, P, P, I32, P], I32),
         "mla_combine_out_up": ([cfgp, P, SZ, P, I32, I32, planp, P, P, P, P], I32),
         "mla_check_decode_inputs_host": ([cfgp, I32, i32p, i32p, I32, I64, i32p, I32, i32p], I32),
+        "mla_cache_append": ([cfgp, P, P, P, P, I32, P, P, I64, P, I32, I32, P], I32),
         "mla_indexer_page_layout": ([I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
         "mla_indexer_scores": ([I32, I32, P, P, P, I64, P, I32, P, I32, P, I64, P], I32),
         "mla_topk_workspace_bytes": ([I32, I64], SZ),
@@ -255,6 +256,33 @@ def mla_check_decode_inputs_host(cfg: MlaConfig, seq_lens, block_table, num_page
 def raw_lib():
     """The loaded ctypes library (for tests that call the C ABI directly)."""
     return _lib
+
+
+def mla_cache_append(cfg: MlaConfig, c_new, k_new, positions, kv_pool, block_table, rope_cos=None, rope_sin=None,
+                     stream=None):
+    """Write one token per request (row positions[b] of its pages)."""
+    torch = _torch()
+    B = c_new.shape[0]
+    dt = _act(cfg)
+    page_bytes = page_layout(cfg)[0]
+    if kv_pool.dtype != torch.uint8 or kv_pool.dim() != 2 or kv_pool.shape[1] != page_bytes:
+        raise ValueError(f"kv_pool must be uint8 [num_pages, {page_bytes}]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [batch, stride]")
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("give both rope tables or neither")
+    rows = 0
+    cp = sp = None
+    if rope_cos is not None:
+        rows = int(rope_cos.shape[0])
+        cp = _dev(rope_cos, "rope_cos", torch.float32, (rows, cfg.d_rope // 2))
+        sp = _dev(rope_sin, "rope_sin", torch.float32, (rows, cfg.d_rope // 2))
+    st = _lib.mla_cache_append(ctypes.byref(cfg), _dev(c_new, "c_new", dt, (B, cfg.d_latent)),
+                               _dev(k_new, "k_new", dt, (B, cfg.d_rope)), cp, sp, rows,
+                               _dev(positions, "positions", torch.int32, (B,)), _dev(kv_pool, "kv_pool"),
+                               int(kv_pool.shape[0]), _dev(block_table, "block_table", torch.int32),
+                               int(block_table.shape[1]), B, _stream(stream))
+    _check("mla_cache_append", st)
 
 
 # ---- lightning indexer (include/mla_indexer.h) ------------------------------

@@ -34,6 +34,7 @@ SOURCES = [
     ("combine.hip", True),
     ("head_gemm.hip", True),
     ("indexer.hip", True),
+    ("cache_append.hip", True),
     ("mla_api.cpp", False),
     ("indexer_api.cpp", False),
 ]

@@ -141,6 +141,45 @@ mla_status mla_decode_plan(const mla_config* cfg, int32_t batch, const int32_t* 
   return MLA_OK;
 }
 
+mla_status mla_cache_append(const mla_config* cfg, const void* c_new, const void* k_new, const float* rope_cos,
+                            const float* rope_sin, int32_t rope_rows, const int32_t* positions, void* kv_pool,
+                            int64_t num_pages, const int32_t* block_table, int32_t block_table_stride,
+                            int32_t batch, void* stream) {
+  Path path;
+  mla_status st = check_config(cfg, &path);
+  if (st != MLA_OK) return st;
+  if (c_new == nullptr || k_new == nullptr || positions == nullptr || kv_pool == nullptr || block_table == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_INVALID_ARG;
+  if (rope_cos != nullptr && rope_rows < 1) return MLA_ERR_INVALID_ARG;
+  if (batch < 1 || num_pages < 1 || block_table_stride < 1) return MLA_ERR_INVALID_ARG;
+  if (!aligned(c_new, 16) || !aligned(k_new, 16) || !aligned(positions, 4) || !aligned(kv_pool, 16) ||
+      !aligned(block_table, 4) || (rope_cos && (!aligned(rope_cos, 4) || !aligned(rope_sin, 4))))
+    return MLA_ERR_INVALID_ARG;
+  if (cfg->d_rope % 2 != 0) return MLA_ERR_UNSUPPORTED;
+  size_t page, rope_off, scale_off;
+  layout(cfg, &page, &rope_off, &scale_off);
+  mla::AppendArgs a{};
+  a.c_new = c_new;
+  a.k_new = k_new;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.rope_rows = rope_rows;
+  a.positions = positions;
+  a.pool = (uint8_t*)kv_pool;
+  a.num_pages = num_pages;
+  a.page_bytes = (int64_t)page;
+  a.rope_off = (int64_t)rope_off;
+  a.scale_off = (int64_t)scale_off;
+  a.block_table = block_table;
+  a.bt_stride = block_table_stride;
+  a.batch = batch;
+  a.D_C = cfg->d_latent;
+  a.D_R = cfg->d_rope;
+  const int kind = path == Path::kF32 ? 0 : path == Path::kMfmaBf16 ? 1 : path == Path::kMfmaFp8 ? 2 : 3;
+  return launch_status(mla::launch_cache_append(a, kind, (hipStream_t)stream));
+}
+
 mla_status mla_absorb_q(const mla_config* cfg, const void* q_nope, const void* w_uk, void* q_lat,
                         int32_t batch, void* stream) {
   Path path;

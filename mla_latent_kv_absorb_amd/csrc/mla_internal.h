@@ -68,6 +68,25 @@ struct HeadGemmArgs {
   int32_t batch, H, M, K;
 };
 
+// one new token per request written into its page slot
+struct AppendArgs {
+  const void* c_new;        // [batch][D_C], activation dtype
+  const void* k_new;        // [batch][D_R], activation dtype, before rotation
+  const float* rope_cos;    // [rope_rows][D_R / 2] or null
+  const float* rope_sin;
+  int32_t rope_rows;
+  const int32_t* positions; // [batch]
+  uint8_t* pool;
+  int64_t num_pages, page_bytes, rope_off, scale_off;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  int32_t batch, D_C, D_R;
+};
+
+// kind: 0 F32 cache, 1 BF16, 2 FP8 with one scale per token, 3 FP8 with one
+// scale per 128 latent channels
+hipError_t launch_cache_append(const AppendArgs& a, int kind, hipStream_t s);
+
 // lightning indexer scores: 64 heads x 128, FP8 search keys with one
 // float32 scale per position
 struct IndexerArgs {
