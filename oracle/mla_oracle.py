@@ -43,6 +43,7 @@ __all__ = [
     "visible_positions",
     "decode_unabsorbed",
     "decode_unabsorbed_batch",
+    "prefill_unabsorbed",
     "absorb_query",
     "latent_decode",
     "up_project",
@@ -159,6 +160,25 @@ def decode_unabsorbed(c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, scale, picked=No
         o_lat[i] = p @ c
         lse[i] = m + np.log(z)
     return out, lse, o_lat
+
+
+def prefill_unabsorbed(c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, scale, q_start, heads=None):
+    """N new queries of one request at positions q_start .. q_start + N - 1,
+    each attending causally to the cached positions up to and including its
+    own ("Shared KV Memory", section 1: M_tj = 0 for j <= t): query i is the
+    decode of position q_start + i over positions 0 .. q_start + i.
+    q_nope [N, H, D_N], q_rope [N, H, D_R].  Returns (out [N, H', D_V],
+    lse [N, H']) for the heads asked for."""
+    q_nope = np.asarray(q_nope)
+    N = q_nope.shape[0]
+    outs, lses = [], []
+    for i in range(N):
+        visible = np.arange(q_start + i + 1)
+        o, l, _ = decode_unabsorbed(c_kv, k_rope, q_nope[i], q_rope[i], w_uk, w_uv, scale, picked=visible,
+                                    heads=heads)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
 
 
 def decode_unabsorbed_batch(inputs_per_request, scale, heads=None):

@@ -392,3 +392,31 @@ def test_generator_workload_structure():
     for b in range(2):
         row = inp2.topk_idx[b]
         assert np.all(np.diff(row) > 0) and row.min() >= 0 and row.max() < 3000
+
+
+def test_prefill_is_causal_attention_over_expanded_keys():
+    """Prefill pin against a library routine: with the keys and values
+    expanded per head ([KV] Figure 5 (1), Figure 6 (1)), the N new queries are
+    the last N rows of causal scaled-dot-product attention (torch's CPU SDPA,
+    float64) over all T positions."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    T, N, H, D_C, D_R, D_N, D_V = 20, 7, 3, 16, 8, 8, 6
+    c, kr = rng.standard_normal((T, D_C)), rng.standard_normal((T, D_R))
+    qn, qr = rng.standard_normal((N, H, D_N)), rng.standard_normal((N, H, D_R))
+    wuk, wuv = rng.standard_normal((H, D_C, D_N)), rng.standard_normal((H, D_V, D_C))
+    scale = 1.0 / np.sqrt(D_N + D_R)
+    out, lse = oracle.prefill_unabsorbed(c, kr, qn, qr, wuk, wuv, scale, q_start=T - N)
+    for h in range(H):
+        K = np.concatenate([c @ wuk[h], kr], axis=1)            # [T, D_N + D_R]
+        V = c @ wuv[h].T                                         # [T, D_V]
+        # full-length causal attention; only the last N query rows are real
+        Q = np.zeros((T, D_N + D_R))
+        Q[T - N:] = np.concatenate([qn[:, h], qr[:, h]], axis=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+            is_causal=True, scale=scale)[0].numpy()
+        np.testing.assert_allclose(out[:, h], ref[T - N:], rtol=1e-12, atol=1e-12)
+    # query i sees q_start + i + 1 positions: the first query sees T - N + 1
+    o1, _, _ = oracle.decode_unabsorbed(c[:T - N + 1], kr[:T - N + 1], qn[0], qr[0], wuk, wuv, scale)
+    np.testing.assert_allclose(out[0], o1, rtol=1e-13, atol=1e-13)
