@@ -148,6 +148,40 @@ mla_status mla_cache_append(const mla_config* cfg, const void* c_new, const void
                             int64_t num_pages, const int32_t* block_table, int32_t block_table_stride,
                             int32_t batch, void* stream);
 
+/* ---- Prefill (many queries of one request) on the expanded path ----
+ * With many queries a key expanded once is shared by all of them ("DeepSeek's
+ * KV Cache", the paragraph after Figure 5 on when absorption wins; Figure 5
+ * (1) and Figure 6 (1) for the expanded forms).  V2 dims, BF16 cache and
+ * activations, d_nope = d_v = 128 (MLA_ERR_UNSUPPORTED otherwise).
+ *
+ * mla_prepare_w_uk_t: the weight layout the expansion reads, once per set of
+ * weights: w_uk_t[h][n][c] = w_uk[h][c][n] ([H][D_N][D_C], BF16). */
+mla_status mla_prepare_w_uk_t(const mla_config* cfg, const void* w_uk, void* w_uk_t, void* stream);
+
+/* mla_prefill_expand: for positions 0 .. T-1 of one request (pages
+ * block_table[0 .. ceil(T/64) - 1] of kv_pool), write
+ *   k_nope[s][h][n] = sum_c c_s[c] w_uk[h][c][n]   [T][H][D_N] BF16
+ *   v[s][h][n]      = sum_c w_uv[h][n][c] c_s[c]    [T][H][D_V] BF16
+ *   k_rope[s][r]    = the cached rotary key         [T][D_R]    BF16
+ * (float32 accumulation, one BF16 rounding).  Positions on a page id out of
+ * range get unspecified values (never a fault).  Errors: null or misaligned
+ * pointers, T < 1 -> MLA_ERR_INVALID_ARG. */
+mla_status mla_prefill_expand(const mla_config* cfg, const void* kv_pool, int64_t num_pages,
+                              const int32_t* block_table, int32_t T, const void* w_uk_t, const void* w_uv,
+                              void* k_nope, void* v, void* k_rope, void* stream);
+
+/* mla_prefill_attn: n_queries queries at positions q_start .. q_start +
+ * n_queries - 1 (q_start + n_queries <= T), query i attending to positions
+ * 0 .. q_start + i of the expanded keys and values:
+ *   q_nope [n][H][D_N], q_rope [n][H][D_R] BF16 (rotated);
+ *   out [n][H][D_V] BF16 = softmax(scale (q_nope . k_nope + q_rope . k_rope)) v;
+ *   lse_out [n][H] float32 (natural log of the softmax sum) or NULL.
+ * Errors: null or misaligned pointers, n_queries < 1, q_start < 0,
+ * q_start + n_queries > T -> MLA_ERR_INVALID_ARG. */
+mla_status mla_prefill_attn(const mla_config* cfg, const void* q_nope, const void* q_rope, const void* k_nope,
+                            const void* v, const void* k_rope, int32_t T, int32_t q_start, int32_t n_queries,
+                            void* out, float* lse_out, void* stream);
+
 /* Choose the number of workers for a batch and size the partial workspace.
  * seq_lens_host: host copy of the per-request lengths (used only to count
  * tiles; may be NULL, then every request is assumed to be max_len long).

@@ -28,6 +28,7 @@ EXPORTED = (
     "mla_abi_version", "mla_status_string", "mla_page_layout", "mla_decode_plan",
     "mla_absorb_q", "mla_decode_attn", "mla_combine", "mla_out_up", "mla_combine_out_up",
     "mla_check_decode_inputs_host", "mla_cache_append",
+    "mla_prepare_w_uk_t", "mla_prefill_expand", "mla_prefill_attn",
     "mla_indexer_page_layout", "mla_indexer_scores", "mla_topk_workspace_bytes", "mla_topk_select",
 )
 INDEXER_HEADS, INDEXER_DIM = 64, 128
@@ -73,6 +74,9 @@ def _load():
         "mla_combine_out_up": ([cfgp, P, SZ, P, I32, I32, planp, P, P, P, P], I32),
         "mla_check_decode_inputs_host": ([cfgp, I32, i32p, i32p, I32, I64, i32p, I32, i32p], I32),
         "mla_cache_append": ([cfgp, P, P, P, P, I32, P, P, I64, P, I32, I32, P], I32),
+        "mla_prepare_w_uk_t": ([cfgp, P, P, P], I32),
+        "mla_prefill_expand": ([cfgp, P, I64, P, I32, P, P, P, P, P, P], I32),
+        "mla_prefill_attn": ([cfgp, P, P, P, P, P, I32, I32, I32, P, P, P], I32),
         "mla_indexer_page_layout": ([I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
         "mla_indexer_scores": ([I32, I32, P, P, P, I64, P, I32, P, I32, P, I64, P], I32),
         "mla_topk_workspace_bytes": ([I32, I64], SZ),
@@ -283,6 +287,45 @@ def mla_cache_append(cfg: MlaConfig, c_new, k_new, positions, kv_pool, block_tab
                                int(kv_pool.shape[0]), _dev(block_table, "block_table", torch.int32),
                                int(block_table.shape[1]), B, _stream(stream))
     _check("mla_cache_append", st)
+
+
+def mla_prepare_w_uk_t(cfg: MlaConfig, w_uk, w_uk_t, stream=None):
+    torch = _torch()
+    H, DC, DN = cfg.num_heads, cfg.d_latent, cfg.d_nope
+    _check("mla_prepare_w_uk_t", _lib.mla_prepare_w_uk_t(
+        ctypes.byref(cfg), _dev(w_uk, "w_uk", torch.bfloat16, (H, DC, DN)),
+        _dev(w_uk_t, "w_uk_t", torch.bfloat16, (H, DN, DC)), _stream(stream)))
+
+
+def mla_prefill_expand(cfg: MlaConfig, kv_pool, block_row, T: int, w_uk_t, w_uv, k_nope, v, k_rope, stream=None):
+    """Expanded keys / values of positions 0 .. T-1 of one request (its page
+    ids in block_row, int32 [>= ceil(T / 64)])."""
+    torch = _torch()
+    H, DC, DN, DV, DR = cfg.num_heads, cfg.d_latent, cfg.d_nope, cfg.d_v, cfg.d_rope
+    page_bytes = page_layout(cfg)[0]
+    if kv_pool.dtype != torch.uint8 or kv_pool.dim() != 2 or kv_pool.shape[1] != page_bytes:
+        raise ValueError(f"kv_pool must be uint8 [num_pages, {page_bytes}]")
+    if block_row.dim() != 1 or block_row.shape[0] < -(-T // PAGE_TOKENS):
+        raise ValueError("block_row must hold the request's ceil(T / 64) page ids")
+    _check("mla_prefill_expand", _lib.mla_prefill_expand(
+        ctypes.byref(cfg), _dev(kv_pool, "kv_pool"), int(kv_pool.shape[0]), _dev(block_row, "block_row", torch.int32),
+        int(T), _dev(w_uk_t, "w_uk_t", torch.bfloat16, (H, DN, DC)), _dev(w_uv, "w_uv", torch.bfloat16, (H, DV, DC)),
+        _dev(k_nope, "k_nope", torch.bfloat16, (T, H, DN)), _dev(v, "v", torch.bfloat16, (T, H, DV)),
+        _dev(k_rope, "k_rope", torch.bfloat16, (T, DR)), _stream(stream)))
+
+
+def mla_prefill_attn(cfg: MlaConfig, q_nope, q_rope, k_nope, v, k_rope, q_start: int, out, lse_out=None,
+                     stream=None):
+    torch = _torch()
+    N = q_nope.shape[0]
+    T = k_nope.shape[0]
+    H, DN, DV, DR = cfg.num_heads, cfg.d_nope, cfg.d_v, cfg.d_rope
+    _check("mla_prefill_attn", _lib.mla_prefill_attn(
+        ctypes.byref(cfg), _dev(q_nope, "q_nope", torch.bfloat16, (N, H, DN)),
+        _dev(q_rope, "q_rope", torch.bfloat16, (N, H, DR)), _dev(k_nope, "k_nope", torch.bfloat16, (T, H, DN)),
+        _dev(v, "v", torch.bfloat16, (T, H, DV)), _dev(k_rope, "k_rope", torch.bfloat16, (T, DR)), int(T),
+        int(q_start), int(N), _dev(out, "out", torch.bfloat16, (N, H, DV)),
+        None if lse_out is None else _dev(lse_out, "lse_out", torch.float32, (N, H)), _stream(stream)))
 
 
 # ---- lightning indexer (include/mla_indexer.h) ------------------------------

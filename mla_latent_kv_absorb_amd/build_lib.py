@@ -35,6 +35,7 @@ SOURCES = [
     ("head_gemm.hip", True),
     ("indexer.hip", True),
     ("cache_append.hip", True),
+    ("prefill.hip", True),
     ("mla_api.cpp", False),
     ("indexer_api.cpp", False),
 ]

@@ -180,6 +180,87 @@ mla_status mla_cache_append(const mla_config* cfg, const void* c_new, const void
   return launch_status(mla::launch_cache_append(a, kind, (hipStream_t)stream));
 }
 
+namespace {
+mla_status check_prefill(const mla_config* cfg) {
+  Path path;
+  mla_status st = check_config(cfg, &path);
+  if (st != MLA_OK) return st;
+  if (path != Path::kMfmaBf16 || cfg->d_nope != 128 || cfg->d_v != 128) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+}  // namespace
+
+mla_status mla_prepare_w_uk_t(const mla_config* cfg, const void* w_uk, void* w_uk_t, void* stream) {
+  mla_status st = check_prefill(cfg);
+  if (st != MLA_OK) return st;
+  if (w_uk == nullptr || w_uk_t == nullptr || !aligned(w_uk, 16) || !aligned(w_uk_t, 16)) return MLA_ERR_INVALID_ARG;
+  return launch_status(mla::launch_transpose_w_uk(w_uk, w_uk_t, cfg->num_heads, cfg->d_latent, cfg->d_nope,
+                                                  (hipStream_t)stream));
+}
+
+mla_status mla_prefill_expand(const mla_config* cfg, const void* kv_pool, int64_t num_pages,
+                              const int32_t* block_table, int32_t T, const void* w_uk_t, const void* w_uv,
+                              void* k_nope, void* v, void* k_rope, void* stream) {
+  mla_status st = check_prefill(cfg);
+  if (st != MLA_OK) return st;
+  if (kv_pool == nullptr || block_table == nullptr || w_uk_t == nullptr || w_uv == nullptr || k_nope == nullptr ||
+      v == nullptr || k_rope == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  if (T < 1 || num_pages < 1) return MLA_ERR_INVALID_ARG;
+  if (!aligned(kv_pool, 16) || !aligned(block_table, 4) || !aligned(w_uk_t, 16) || !aligned(w_uv, 16) ||
+      !aligned(k_nope, 16) || !aligned(v, 16) || !aligned(k_rope, 16))
+    return MLA_ERR_INVALID_ARG;
+  size_t page, rope_off, scale_off;
+  layout(cfg, &page, &rope_off, &scale_off);
+  mla::ExpandArgs a{};
+  a.pool = (const uint8_t*)kv_pool;
+  a.page_bytes = (int64_t)page;
+  a.rope_off = (int64_t)rope_off;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.T = T;
+  a.N = (int64_t)cfg->num_heads * cfg->d_nope;
+  hipStream_t s = (hipStream_t)stream;
+  a.w = (const __bf16*)w_uk_t;
+  a.out = (__bf16*)k_nope;
+  a.k_rope = (__bf16*)k_rope;
+  hipError_t e = mla::launch_expand(a, s);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  a.w = (const __bf16*)w_uv;
+  a.out = (__bf16*)v;
+  a.k_rope = nullptr;
+  return launch_status(mla::launch_expand(a, s));
+}
+
+mla_status mla_prefill_attn(const mla_config* cfg, const void* q_nope, const void* q_rope, const void* k_nope,
+                            const void* v, const void* k_rope, int32_t T, int32_t q_start, int32_t n_queries,
+                            void* out, float* lse_out, void* stream) {
+  mla_status st = check_prefill(cfg);
+  if (st != MLA_OK) return st;
+  if (q_nope == nullptr || q_rope == nullptr || k_nope == nullptr || v == nullptr || k_rope == nullptr ||
+      out == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  if (n_queries < 1 || q_start < 0 || T < 1 || (int64_t)q_start + n_queries > T || n_queries > 65535 * 128)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(k_nope, 16) || !aligned(v, 16) ||
+      !aligned(k_rope, 16) || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
+    return MLA_ERR_INVALID_ARG;
+  mla::PrefillArgs a{};
+  a.qn = (const __bf16*)q_nope;
+  a.qr = (const __bf16*)q_rope;
+  a.kn = (const __bf16*)k_nope;
+  a.v = (const __bf16*)v;
+  a.kr = (const __bf16*)k_rope;
+  a.out = (__bf16*)out;
+  a.lse = lse_out;
+  a.H = cfg->num_heads;
+  a.T = T;
+  a.q_start = q_start;
+  a.N = n_queries;
+  a.scale = cfg->softmax_scale;
+  return launch_status(mla::launch_prefill_attn(a, (hipStream_t)stream));
+}
+
 mla_status mla_absorb_q(const mla_config* cfg, const void* q_nope, const void* w_uk, void* q_lat,
                         int32_t batch, void* stream) {
   Path path;

@@ -68,6 +68,35 @@ struct HeadGemmArgs {
   int32_t batch, H, M, K;
 };
 
+// prefill: per-head expansion of one request's latent (NT GEMM over D_C)
+struct ExpandArgs {
+  const uint8_t* pool;
+  int64_t page_bytes, rope_off, num_pages;
+  const int32_t* block_table;  // the request's pages
+  int64_t T;
+  const __bf16* w;             // [N][512]
+  __bf16* out;                 // [T][N]
+  int64_t N;                   // H * 128
+  __bf16* k_rope;              // [T][64] or null
+};
+
+// prefill: causal attention over the expanded keys and values
+struct PrefillArgs {
+  const __bf16* qn;            // [N][H][128]
+  const __bf16* qr;            // [N][H][64]
+  const __bf16* kn;            // [T][H][128]
+  const __bf16* v;             // [T][H][128]
+  const __bf16* kr;            // [T][64]
+  __bf16* out;                 // [N][H][128]
+  float* lse;                  // [N][H] or null
+  int64_t H, T, q_start, N;
+  float scale;
+};
+
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t s);
+hipError_t launch_transpose_w_uk(const void* w_uk, void* w_uk_t, int H, int D_C, int D_N, hipStream_t s);
+hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t s);
+
 // one new token per request written into its page slot
 struct AppendArgs {
   const void* c_new;        // [batch][D_C], activation dtype

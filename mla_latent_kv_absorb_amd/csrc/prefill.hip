@@ -1,0 +1,338 @@
+// Prefill on the expanded path, gfx950.
+//
+// With many queries per request a key expanded once is shared by all of them
+// ("DeepSeek's KV Cache", section on absorption after Figure 5, and Figure 5
+// (1) / Figure 6 (1)), so prefill expands the cached latent per head once --
+// K_nope[s][h] = W_UK[h]^T c_s and V[s][h] = W_UV[h] c_s -- and then runs
+// causal attention with 192-wide keys (content + the shared rotary key) and
+// 128-wide values.
+//
+// expand_kernel: an NT GEMM out[s][n] = sum_k C[s][k] W[n][k] over the 512
+// latent channels, C gathered row by row from the cache pages, W one of the
+// two weights viewed as [H * 128][512] (W_UV as stored; W_UK transposed once
+// by transpose_w_uk_kernel).  Tiles of 128 positions x 128 features, K in
+// chunks of 64 moved HBM -> LDS without registers (double buffered), four
+// waves of 64 x 64 on MFMA 32x32x16.
+//
+// prefill_attn_kernel: per work-group one head and 128 queries (32 per wave,
+// one query per lane column).  Tiles of 32 positions (content key, rotary key,
+// value) stream through a 4-stage LDS ring; S^T[pos][query] on MFMA, online
+// softmax per query with the causal bound, O^T[v][query] += V^T P^T with V^T
+// from transposing LDS reads -- the decode kernel's pattern with queries in
+// place of heads.
+#include "attn_common.h"
+
+namespace mla {
+namespace {
+
+// ---------------- expansion GEMM ----------------
+constexpr int kGM = 128, kGN = 128, kGK = 64;
+constexpr int kGRow = kGK * 2;          // bytes of one LDS row (one K chunk)
+constexpr int kGTile = kGM * kGRow;     // 16 KiB per operand tile
+constexpr int kGChunks = kLatent / kGK; // 8
+
+__device__ __forceinline__ int gswz(int r) { return r & 7; }
+
+__global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * 2 * kGTile];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t m0 = (int64_t)blockIdx.y * kGM;
+  const int64_t n0 = (int64_t)blockIdx.x * kGN;
+  const int row = lane & 31, hi = lane >> 5;
+  const uint32_t base = (uint32_t)(uintptr_t)lds;
+
+  // this lane's share of a chunk's loads: 4 rows-of-8 per operand per wave
+  const int rl = lane >> 3, cc = lane & 7;
+  const uint8_t* asrc[4];
+  const __bf16* bsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (4 * w + i) + rl;  // tile row 0..127
+    int64_t s = m0 + r;
+    if (s >= a.T) s = a.T - 1;           // rows past the end load a valid row; never stored
+    int32_t page = a.block_table[s >> 6];
+    if (page < 0 || page >= a.num_pages) page = 0;  // out-of-range ids read page 0 (values unspecified)
+    asrc[i] = a.pool + (int64_t)page * a.page_bytes + (s & 63) * kCRow + 16 * (cc ^ gswz(r));
+    bsrc[i] = a.w + (n0 + r) * kLatent + 8 * (cc ^ gswz(r));
+  }
+  auto issue = [&](int buf, int kc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t dst = base + buf * 2 * kGTile + 8 * (4 * w + i) * kGRow;
+      dma16(asrc[i] + kc * kGRow, dst);
+      dma16(bsrc[i] + kc * kGK, dst + kGTile);
+    }
+  };
+
+  const int wm = w >> 1, wn = w & 1;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  issue(0, 0);
+  for (int kc = 0; kc < kGChunks; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < kGChunks) {
+      issue(buf ^ 1, kc + 1);
+      wait_vmcnt<8>();  // chunk kc landed (chunk kc + 1 may be in flight)
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const LDS char* A = (const LDS char*)lds + buf * 2 * kGTile;
+    const LDS char* Bt = A + kGTile;
+#pragma unroll
+    for (int kb = 0; kb < kGK / 16; ++kb) {
+      bf16x8 av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ra = 64 * wm + 32 * i + row, rb = 64 * wn + 32 * i + row;
+        av[i] = *(const LDS bf16x8*)(A + ra * kGRow + 16 * ((2 * kb + hi) ^ gswz(ra)));
+        bv[i] = *(const LDS bf16x8*)(Bt + rb * kGRow + 16 * ((2 * kb + hi) ^ gswz(rb)));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();  // the buffer is refilled two chunks later
+  }
+
+  // D[s][n]: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 hi + r % 4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = n0 + 64 * wn + 32 * j + row;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t s = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (s < a.T) a.out[s * a.N + n] = (__bf16)acc[i][j][r];
+      }
+    }
+
+  // the shared rotary keys of the tile's positions (once, by the first column of tiles)
+  if (a.k_rope != nullptr && blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < kGM * (kRope / 8); e += 256) {
+      const int r = e / (kRope / 8), c = e % (kRope / 8);
+      const int64_t s = m0 + r;
+      if (s >= a.T) continue;
+      int32_t page = a.block_table[s >> 6];
+      if (page < 0 || page >= a.num_pages) page = 0;
+      const bf16x8 v = *(const bf16x8*)(a.pool + (int64_t)page * a.page_bytes + a.rope_off + (s & 63) * kRRow + 16 * c);
+      *(bf16x8*)(a.k_rope + s * kRope + 8 * c) = v;
+    }
+  }
+}
+
+// W_UK [H][512][128] -> [H][128][512] (done once per set of weights)
+__global__ __launch_bounds__(256) void transpose_w_uk_kernel(const __bf16* in, __bf16* out, int H, int D_C, int D_N) {
+  __shared__ __bf16 t[64][65];
+  const int h = blockIdx.z;
+  const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int kk = e / 64, nn = e % 64;
+    if (k0 + kk < D_C && n0 + nn < D_N) t[kk][nn] = in[((int64_t)h * D_C + k0 + kk) * D_N + n0 + nn];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int nn = e / 64, kk = e % 64;
+    if (k0 + kk < D_C && n0 + nn < D_N) out[((int64_t)h * D_N + n0 + nn) * D_C + k0 + kk] = t[kk][nn];
+  }
+}
+
+// ---------------- causal attention over the expanded keys ----------------
+constexpr int kPDv = 128;              // value and content-key width
+constexpr int kPQ = 128;               // queries per work-group (32 per wave)
+constexpr int kPRow = kPDv * 2;         // bytes of a content-key or value row (256)
+constexpr int kPK = kTile * kPRow;     // 8 KiB
+constexpr int kPR = kTile * kRRow;     // 4 KiB
+constexpr int kPStage = 2 * kPK + kPR; // content key, value, rotary key
+constexpr int kPNS = 4;
+
+__global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kPNS * kPStage];
+  LDS char* L = (LDS char*)smem;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x;
+  const int64_t q0 = (int64_t)blockIdx.y * kPQ;
+  const int col = lane & 31, hi = lane >> 5;
+  const int64_t qi = q0 + 32 * w + col;            // this lane's query
+  const bool qvalid = qi < a.N;
+  const int64_t qc = qvalid ? qi : a.N - 1;
+  const int64_t qpos = a.q_start + qc;             // its position: sees 0 .. qpos
+  const float scale_log2 = a.scale * kLog2e;
+  const int64_t H = a.H;
+
+  // B operand: query rows, content dims then rotary dims
+  bf16x8 q[12];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) q[kb] = *(const bf16x8*)(a.qn + (qc * H + h) * kPDv + 16 * kb + 8 * hi);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) q[8 + kb] = *(const bf16x8*)(a.qr + (qc * H + h) * kRope + 16 * kb + 8 * hi);
+
+  // positions the work-group needs: up to its last query's position
+  int64_t span = a.q_start + q0 + kPQ;
+  if (span > a.T) span = a.T;
+  const int32_t nt = (int32_t)((span + kTile - 1) / kTile);
+
+  // per-lane LDS offsets (content key / value rows: 16 chunks, swizzle swz;
+  // rotary rows: 8 chunks, swizzle swz_r)
+  int k_off[8], r_off[4], tr_off[2][4];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) k_off[v] = col * kPRow + 16 * ((2 * v + hi) ^ swz(col));
+#pragma unroll
+  for (int v = 0; v < 4; ++v) r_off[v] = col * kRRow + 16 * ((2 * v + hi) ^ swz_r(col));
+  {
+    const int j16 = lane & 15, g16 = lane >> 4, hh = g16 >> 1, ch = g16 & 1;
+    const int tr_row = 4 * hh + (j16 >> 2);
+    const int lo = 2 * ch + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        tr_off[h8][e] = (tr_row + 8 * h8) * kPRow + 16 * ((4 * e + lo) ^ swz(tr_row + 8 * h8)) + (j16 & 1) * 8;
+  }
+
+  // loads of tile t into stage st: this wave's rows 8w .. 8w + 7
+  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+  auto issue = [&](int st, int32_t t) {
+    const uint32_t sb = sbase + st * kPStage;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * w + 4 * i + (lane >> 4), c = lane & 15;
+      int64_t s = (int64_t)t * kTile + r;
+      if (s >= a.T) s = a.T - 1;  // past the end: a valid row, masked below
+      const int64_t off = (s * H + h) * kPDv + 8 * (c ^ swz(r));
+      dma16(a.kn + off, sb + (8 * w + 4 * i) * kPRow);
+      dma16(a.v + off, sb + kPK + (8 * w + 4 * i) * kPRow);
+    }
+    {
+      const int r = 8 * w + (lane >> 3), c = lane & 7;
+      int64_t s = (int64_t)t * kTile + r;
+      if (s >= a.T) s = a.T - 1;
+      dma16(a.kr + s * kRope + 8 * (c ^ swz_r(r)), sb + 2 * kPK + 8 * w * kRRow);
+    }
+  };
+  constexpr int kDmaPerTile = 5;
+
+  f32x16 O[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) O[mb] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int pro = nt < kPNS - 1 ? nt : kPNS - 1;
+  for (int t = 0; t < pro; ++t) issue(t, t);
+  for (int32_t t = 0; t < nt; ++t) {
+    const int st = t % kPNS;
+    // tile t landed: at most (tiles issued after it) loads of this wave pending
+    const int ahead = (nt - 1 - t) < (kPNS - 2) ? (nt - 1 - t) : (kPNS - 2);
+    if (ahead >= 2) wait_vmcnt<2 * kDmaPerTile>();
+    else if (ahead == 1) wait_vmcnt<kDmaPerTile>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (t + kPNS - 1 < nt) issue((t + kPNS - 1) % kPNS, t + kPNS - 1);
+    const LDS char* Kt = L + st * kPStage;
+    const LDS char* Vt = Kt + kPK;
+    const LDS char* Rt = Kt + 2 * kPK;
+
+    // S^T[pos][query]
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < 12; ++kb) {
+      const bf16x8 kv = kb < 8 ? *(const LDS bf16x8*)(Kt + k_off[kb]) : *(const LDS bf16x8*)(Rt + r_off[kb - 8]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, q[kb], sacc, 0, 0, 0);
+    }
+    // causal bound and the context end; position of accumulator r:
+    // t * 32 + 8 (r / 4) + 4 hi + r % 4
+    float s[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t kp = (int64_t)t * kTile + 8 * (r >> 2) + 4 * hi + (r & 3);
+      s[r] = (kp <= qpos && kp < a.T) ? sacc[r] : -INFINITY;
+    }
+    float mloc = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
+    mloc = fmaxf(mloc, wave_partner(mloc)) * scale_log2;
+    const float m_new = fmaxf(m_run, mloc);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[mb][r] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+    float lsum = 0.f;
+    bf16x8 P[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, neg_m));
+      lsum += p;
+      P[r >> 3][r & 7] = (__bf16)p;
+    }
+    l_run += lsum;
+
+    // O^T[v][query] += V^T[v][pos] P^T[pos][query]
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const LDS char* p1 = Vt + tr_off[0][mb] + 16 * kPRow * kb2;
+        const LDS char* p2 = Vt + tr_off[1][mb] + 16 * kPRow * kb2;
+        s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p1);
+        s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p2);
+        typedef __attribute__((ext_vector_type(8))) short s16x8;
+        const bf16x8 vt = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, P[kb2], O[mb], 0, 0, 0);
+      }
+  }
+  wait_vmcnt<0>();
+
+  const float l_tot = l_run + wave_partner(l_run);
+  if (!qvalid) return;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  __bf16* o = a.out + (qi * H + h) * kPDv + 4 * hi;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(O[mb][4 * g + e] * inv);
+      *(bf16x4*)(o + 32 * mb + 8 * g) = v;
+    }
+  if (a.lse != nullptr && hi == 0) a.lse[qi * H + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.N / kGN), (unsigned)((a.T + kGM - 1) / kGM));
+  hipLaunchKernelGGL(expand_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_w_uk(const void* w_uk, void* w_uk_t, int H, int D_C, int D_N, hipStream_t s) {
+  const dim3 grid((D_N + 63) / 64, (D_C + 63) / 64, H);
+  hipLaunchKernelGGL(transpose_w_uk_kernel, grid, dim3(256), 0, s, (const __bf16*)w_uk, (__bf16*)w_uk_t, H, D_C, D_N);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t s) {
+  // x = head: work-groups of one head share an XCD's L2 (launch order is
+  // round-robin over the 8 XCDs and 128 heads is a multiple of 8)
+  const dim3 grid((unsigned)a.H, (unsigned)((a.N + kPQ - 1) / kPQ));
+  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

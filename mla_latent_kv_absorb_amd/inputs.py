@@ -258,6 +258,18 @@ def make_inputs(name: str, seed: Optional[int] = None, *, batch: Optional[int] =
                         page_perm=page_perm, c_codes=codes, c_scales=scales, topk_idx=idx)
 
 
+def make_prefill_queries(inp: DecodeInputs, n: int, seed: int):
+    """N new queries for prefill of a one-request workload: q_nope [N, H,
+    D_N] and q_rope [N, H, D_R] ~ N(0, 1), rounded to BF16 for BF16
+    activations (the queries at positions T - N .. T - 1)."""
+    rng = np.random.default_rng(seed)
+    qn = rng.standard_normal((n, inp.H, inp.D_N), dtype=np.float32)
+    qr = rng.standard_normal((n, inp.H, inp.D_R), dtype=np.float32)
+    if inp.act_dtype == DTYPE_BF16:
+        qn, qr = round_to_bf16(qn), round_to_bf16(qr)
+    return qn, qr
+
+
 def requantize(inp: DecodeInputs, cache_dtype: str) -> DecodeInputs:
     """The same draw with the latent stored in the other FP8 format (from the
     pre-quantisation values the FP8 workloads keep)."""

@@ -164,3 +164,44 @@ class IndexerWorkload:
     def step(self, stream=None):
         self.score(stream)
         self.select(stream)
+
+
+class PrefillWorkload:
+    """One request's prefill on the expanded path: the request's cache pages,
+    the weights (W_UK transposed once), the N new queries at positions
+    T - N .. T - 1, and the expanded keys / values."""
+
+    def __init__(self, inp: I.DecodeInputs, q_nope, q_rope, device="cuda"):
+        import torch
+        assert inp.B == 1
+        self.inp = inp
+        self.cfg = B.make_config(inp.H, inp.D_C, inp.D_R, inp.D_N, inp.D_V, inp.scale, B.MLA_BF16, B.MLA_BF16)
+        pool, table = I.build_paged_pool(inp)
+        self.pool = torch.from_numpy(pool).to(device)
+        self.block_row = torch.from_numpy(np.ascontiguousarray(table[0], dtype=np.int32)).to(device)
+        self.T = int(inp.seq_lens[0])
+        self.w_uk = to_device_act(inp.w_uk, I.DTYPE_BF16, device)
+        self.w_uv = to_device_act(inp.w_uv, I.DTYPE_BF16, device)
+        self.w_uk_t = torch.empty((inp.H, inp.D_N, inp.D_C), dtype=torch.bfloat16, device=device)
+        B.mla_prepare_w_uk_t(self.cfg, self.w_uk, self.w_uk_t)
+        self.q_nope = to_device_act(q_nope, I.DTYPE_BF16, device)
+        self.q_rope = to_device_act(q_rope, I.DTYPE_BF16, device)
+        self.N = int(q_nope.shape[0])
+        T, H = self.T, inp.H
+        self.k_nope = torch.empty((T, H, inp.D_N), dtype=torch.bfloat16, device=device)
+        self.v = torch.empty((T, H, inp.D_V), dtype=torch.bfloat16, device=device)
+        self.k_rope = torch.empty((T, inp.D_R), dtype=torch.bfloat16, device=device)
+        self.out = torch.empty((self.N, H, inp.D_V), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((self.N, H), dtype=torch.float32, device=device)
+
+    def expand(self, stream=None):
+        B.mla_prefill_expand(self.cfg, self.pool, self.block_row, self.T, self.w_uk_t, self.w_uv, self.k_nope,
+                             self.v, self.k_rope, stream)
+
+    def attend(self, stream=None):
+        B.mla_prefill_attn(self.cfg, self.q_nope, self.q_rope, self.k_nope, self.v, self.k_rope, self.T - self.N,
+                           self.out, self.lse, stream)
+
+    def step(self, stream=None):
+        self.expand(stream)
+        self.attend(stream)
