@@ -21,6 +21,7 @@ one layer of the long-context workload (1 request x 131,072 positions);
 and, from the same draw, with one scale per 128 latent channels.  --indexer
 adds the lightning indexer scan and top-k pick over 32 x 65,536 positions
 (and, with --fp8-topk, the whole sparse decode step fed by its picks).
+--prefill adds prefill of a 4,096-token prompt on the expanded path.
 """
 
 from __future__ import annotations
@@ -195,6 +196,39 @@ def fp8_topk_step(torch, I, runner, num_cus, inp, lists=8, reps=10):
             "tokens_per_s": round(inp.B / (step_us * 1e-6), 1), "workers": w.plan.num_workers}
 
 
+def prefill_leg(torch, I, runner, T=4096, reps=10):
+    """Prefill of a T-token prompt of one request at V2 dims on the expanded
+    path: expansion of the cached latent per head (two GEMMs over the 512
+    latent channels) and causal attention of the T queries.  Reports the time
+    of each and their matrix-core rates (dense BF16 peak)."""
+    inp = I.make_inputs("v2_single", ctx=(T, T))
+    qn, qr = I.make_prefill_queries(inp, T, seed=56)
+    w = runner.PrefillWorkload(inp, qn, qr)
+    w.step()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        w.expand()
+        e[1].record()
+        w.attend()
+        e[2].record()
+        ev.append(e)
+    torch.cuda.synchronize()
+    exp_us = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    att_us = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    H = inp.H
+    exp_flop = 2.0 * T * inp.D_C * H * (inp.D_N + inp.D_V)
+    pairs = T * (T + 1) / 2.0                       # causal (query, key) pairs
+    att_flop = 2.0 * pairs * H * (inp.D_N + inp.D_R + inp.D_V)
+    return {"tokens": T, "expand_us": round(exp_us, 1), "attn_us": round(att_us, 1),
+            "expand_TFLOPs": round(exp_flop / (exp_us * 1e-6) / 1e12, 1),
+            "attn_TFLOPs": round(att_flop / (att_us * 1e-6) / 1e12, 1),
+            "attn_mfma_util": round(att_flop / (att_us * 1e-6) / BF16_PEAK_FLOPS, 4),
+            "prefill_tokens_per_s": round(T / ((exp_us + att_us) * 1e-6), 1)}
+
+
 def cache_append_part(torch, I, w, reps=200):
     """mla_cache_append for the workload's 64 requests (one token each, with
     RoPE from float32 tables), timed after the decode steps; it rewrites each
@@ -213,14 +247,29 @@ def cache_append_part(torch, I, w, reps=200):
     call = lambda: B.mla_cache_append(w.cfg, c_new, k_new, pos, w.pool, w.table, cos, sin)
     call()
     torch.cuda.synchronize()
+    # A single call is shorter than its launch from Python, so the calls are
+    # captured once in a HIP graph (the kernel records no memset) and the
+    # replays are timed: device time per call, without the host's share.
+    per_graph = 20
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(per_graph):
+                call()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(reps):
-        call()
+    for _ in range(reps // per_graph):
+        g.replay()
     b.record()
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / reps
-    return {"us": round(us, 2), "bytes_written": int(inp.B * (inp.D_C + inp.D_R) * 2)}
+    us = a.elapsed_time(b) * 1e3 / (reps // per_graph * per_graph)
+    return {"us": round(us, 2), "bytes_written": int(inp.B * (inp.D_C + inp.D_R) * 2),
+            "timing": "HIP graph replays of 20 calls"}
 
 
 def indexer_step(torch, I, runner, reps=10, layers=4, attn=None):
@@ -291,6 +340,8 @@ def main():
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--long", action="store_true",
                     help="also time one layer of the long-context workload (1 request, 131,072 positions)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="also time prefill of a 4,096-token prompt on the expanded path")
     ap.add_argument("--indexer", action="store_true",
                     help="also time the lightning indexer and top-k pick (32 x 65,536 positions), and with "
                          "--fp8-topk the whole sparse decode step")
@@ -387,6 +438,7 @@ def main():
         g_inp = I.requantize(fp8_inp, I.DTYPE_FP8_G128)
         del fp8_inp
         fp8g = fp8_topk_step(torch, I, runner, num_cus, g_inp)
+    pre = prefill_leg(torch, I, runner) if args.prefill else None
     idx = None
     if args.indexer:
         attn = runner.DeviceWorkload(g_inp, split=True, num_cus=num_cus) if args.fp8_topk else None
@@ -444,6 +496,8 @@ def main():
         result["fp8_g128_topk_step"] = fp8g
     if idx is not None:
         result["indexer_step"] = idx
+    if pre is not None:
+        result["prefill_4096"] = pre
     print(json.dumps(result), flush=True)
 
 
