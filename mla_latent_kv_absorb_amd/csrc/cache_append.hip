@@ -9,6 +9,7 @@
 // (per token), or the maximum over each 128-channel group, which is the same
 // pair index of every lane.
 #include "attn_common.h"
+#include "side_calls.h"
 
 namespace mla {
 namespace {

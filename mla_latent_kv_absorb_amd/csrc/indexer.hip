@@ -28,6 +28,7 @@
 // writes its picks in increasing order with a block prefix sum.  No work-group
 // walks a whole row.
 #include "attn_common.h"
+#include "side_calls.h"
 
 namespace mla {
 namespace {

@@ -2,6 +2,7 @@
 // launches.  Nothing here allocates device memory or synchronises a stream.
 #include "../../include/mla_indexer.h"
 #include "mla_internal.h"
+#include "side_calls.h"
 
 namespace {
 

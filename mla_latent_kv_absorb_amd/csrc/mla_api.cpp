@@ -6,6 +6,7 @@
 
 #include "../../include/mla_absorb.h"
 #include "mla_internal.h"
+#include "side_calls.h"
 
 namespace {
 

@@ -21,6 +21,7 @@
 // from transposing LDS reads -- the decode kernel's pattern with queries in
 // place of heads.
 #include "attn_common.h"
+#include "side_calls.h"
 
 namespace mla {
 namespace {
