@@ -154,7 +154,7 @@ constexpr int kPR = kTile * kRRow;     // 4 KiB
 constexpr int kPStage = 2 * kPK + kPR; // content key, value, rotary key
 constexpr int kPNS = 4;
 
-__global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kPNS * kPStage];
   LDS char* L = (LDS char*)smem;
   const int lane = threadIdx.x & 63;
@@ -260,15 +260,19 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
     for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
     mloc = fmaxf(mloc, wave_partner(mloc)) * scale_log2;
+    // lazy rescale: the reference maximum moves only when the tile's
+    // maximum exceeds it by more than 8 (log2 units), so probabilities stay
+    // <= 256 and the accumulator is rescaled rarely
     const float m_new = fmaxf(m_run, mloc);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-      const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    const bool need = m_new > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[mb][r] *= alpha;
-      m_run = m_new;
+      m_run = need ? m_new : m_run;
     }
     const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
     float lsum = 0.f;
