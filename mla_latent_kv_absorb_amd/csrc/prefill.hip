@@ -102,18 +102,28 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
     __syncthreads();  // the buffer is refilled two chunks later
   }
 
-  // D[s][n]: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 hi + r % 4
+  // D[s][n]: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 hi + r % 4.
+  // The wave's 64 x 64 block goes through LDS (free after the last chunk) so
+  // the global stores are whole 16-byte pieces of 128-byte row segments.
+  constexpr int kOPitch = 64 * 2 + 16;  // padded row: the column-wise writes spread over the banks
+  LDS char* ob = (LDS char*)lds + w * 64 * kOPitch;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + 64 * wn + 32 * j + row;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t s = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (s < a.T) a.out[s * a.N + n] = (__bf16)acc[i][j][r];
+        const int sr = 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
+        *(LDS __bf16*)(ob + sr * kOPitch + 2 * (32 * j + row)) = (__bf16)acc[i][j][r];
       }
-    }
+  // each wave reads back only its own block: no barrier needed
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int sr = 8 * it + (lane >> 3), c = lane & 7;
+    const int64_t s = m0 + 64 * wm + sr;
+    const bf16x8 v = *(const LDS bf16x8*)(ob + sr * kOPitch + 16 * c);
+    if (s < a.T) *(bf16x8*)(a.out + s * a.N + n0 + 64 * wn + 8 * c) = v;
+  }
 
   // the shared rotary keys of the tile's positions (once, by the first column of tiles)
   if (a.k_rope != nullptr && blockIdx.x == 0) {
