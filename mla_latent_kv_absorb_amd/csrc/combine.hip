@@ -58,6 +58,7 @@ struct MergePlan {
   int64_t p_first, W, P;
   int32_t np, nchunks;
   float mref, inv, tot;
+  float lc[4];           // this lane's lse in chunks 0..3 (loaded once, together)
   const float* lse_col;  // slot s: lse_col[s * H]
   int H;
   bool some_empty;
@@ -85,17 +86,25 @@ struct MergePlan {
     // Workers are empty only when there are fewer units than workers; then
     // p * W < P * P and the test needs no 64-bit division.
     some_empty = W < P;
-    float mx = -INFINITY;
-    for (int32_t c = 0; c < nchunks; ++c) mx = fmaxf(mx, lane_lse(c));
+    // the first 256 candidates' lse in one burst of loads, kept in registers
+#pragma unroll
+    for (int c = 0; c < 4; ++c) lc[c] = c < nchunks ? lane_lse(c) : -INFINITY;
+    float mx = fmaxf(fmaxf(lc[0], lc[1]), fmaxf(lc[2], lc[3]));
+    for (int32_t c = 4; c < nchunks; ++c) mx = fmaxf(mx, lane_lse(c));
     mx = wave_max(mx);
     mref = (mx == -INFINITY) ? 0.f : mx;
     float t = 0.f;
     for (int32_t c = 0; c < nchunks; ++c) {
-      const float l = lane_lse(c);
+      const float l = chunk_lse(c);
       t += (l == -INFINITY) ? 0.f : expf(l - mref);
     }
     tot = wave_sum(t);
     inv = tot > 0.f ? 1.0f / tot : 0.f;
+  }
+  // lse of chunk c for this lane: from registers for the first four chunks
+  __device__ __forceinline__ float chunk_lse(int32_t c) const {
+    if (c < 4) return c == 0 ? lc[0] : c == 1 ? lc[1] : c == 2 ? lc[2] : lc[3];
+    return lane_lse(c);
   }
   // lse of partial p_first + 64c + lane; an empty worker wrote nothing and
   // counts as lse = -inf
@@ -126,7 +135,7 @@ __device__ __forceinline__ void merge_cols(const MergePlan& m, const PT* row0, i
   acc = 0.f;
   if (j_hi > m.np) j_hi = m.np;
   for (int32_t c = j_lo >> 6; 64 * c < j_hi; ++c) {
-    const float l = m.lane_lse(c);
+    const float l = m.chunk_lse(c);
     const float wl = (l == -INFINITY) ? 0.f : expf(l - m.mref) * m.inv;  // lane's weight
     const int32_t n = j_hi - 64 * c < 64 ? j_hi - 64 * c : 64;
     for (int32_t j = j_lo - 64 * c > 0 ? j_lo - 64 * c : 0; j < n; j += kUnroll) {
@@ -235,17 +244,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 }
 
 // ---- merge and value up-projection in one launch (V2 dims, BF16) ----
-// Work-group (head h, 32 requests), 16 waves: each wave merges two requests'
+// Work-group (head h, 32 requests), 8 waves: each wave merges four requests'
 // partials of head h into BF16 rows in LDS (the same arithmetic as
-// combine_kernel, rounded to BF16 as o_lat would be).  With fewer than 16
-// requests in the group, the 16 / n waves of a request split its partials
+// combine_kernel, rounded to BF16 as o_lat would be).  With fewer than 8
+// requests in the group, the 8 / n waves of a request split its partials
 // into contiguous ranges and their float32 sums are added in LDS, so a lone
-// long request (hundreds of partials) is merged by all 16 waves.  Then waves
-// 0..3 each
-// multiply 32 rows of W_UV[h] (128 x 512) by the 32 rows on MFMA 32x32x16:
-// out^T[m][b] = sum_k W_UV[h][m][k] o[b][k] ("DeepSeek's KV Cache",
-// Figure 6, form (2)).  The merged latent never goes to HBM.
-constexpr int kCuThreads = 1024;
+// long request (hundreds of partials) is merged by all 8 waves.  Each wave
+// loads its slice of W_UV[h] (32 rows, half of K) before merging, so those
+// reads overlap the merge; then every wave multiplies its slice by the merged
+// rows on MFMA 32x32x16, the two K halves meet in LDS, and waves 0..3 store
+// out^T[m][b] = sum_k W_UV[h][m][k] o[b][k] for 32 rows m each ("DeepSeek's
+// KV Cache", Figure 6, form (2)).  The merged latent never goes to HBM.
+constexpr int kCuThreads = 512;
 constexpr int kCuWaves = kCuThreads / 64;
 constexpr int kCuReq = 32;                // requests per work-group (MFMA N)
 constexpr int kCuRow = kLatent * 2 + 16;  // LDS row pitch in bytes (padded against bank conflicts)
@@ -256,7 +266,8 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
 __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u) {
   __shared__ __attribute__((aligned(16))) char olds[kCuReq * kCuRow];
-  __shared__ __attribute__((aligned(16))) float red[kCuWaves * kLatent];  // per-wave sums (small groups)
+  // per-wave float32 sums: the merge of small groups, then the up-projection's K quarters
+  __shared__ __attribute__((aligned(16))) float red[kCuWaves * 1024];
   __shared__ int64_t below_s[kCuReq + 1];  // units below each request of the group; [kCuReq] = total
   const CombineArgs& a = u.c;
   const int h = blockIdx.x;
@@ -265,6 +276,19 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int64_t row_stride = (int64_t)kHeads * kLatent;
+
+  // This wave's share of the up-projection: rows 32 (wv % 4) .. +31 of
+  // W_UV[h], latent columns 256 (wv / 4) .. +255.  Loaded first, so the
+  // weight reads overlap the merge.
+  constexpr int kKB = kLatent / 16 / (kCuWaves / 4);  // K-blocks per wave
+  const int rb = wv & 3, kq = wv >> 2;
+  bf16x8 wreg[kKB];
+  {
+    const __bf16* wp = (const __bf16*)u.w_uv + ((int64_t)h * kDv + 32 * rb + (lane & 31)) * kLatent +
+                       16 * kKB * kq + 8 * (lane >> 5);
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) wreg[kb] = *(const bf16x8*)(wp + 16 * kb);
+  }
 
   if (wv == 0) {
     // exclusive prefix of the request spans, once for the whole group
@@ -342,29 +366,27 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
     *(bf16x8*)(olds + bl * kCuRow + 16 * lane) = o;
   }
   __syncthreads();
-  if (wv >= kDv / 32) return;
 
-  // A: W_UV[h] rows 32 wv + (lane % 32), 8 columns per lane per K-block;
-  // B: merged row (lane % 32), the same 8 columns
-  const __bf16* wp = (const __bf16*)u.w_uv + ((int64_t)h * kDv + 32 * wv + (lane & 31)) * kLatent + 8 * (lane >> 5);
-  const char* op = olds + (lane & 31) * kCuRow + 16 * (lane >> 5);
+  // A: W_UV[h] rows 32 rb + (lane % 32), 8 columns per lane per K-block;
+  // B: merged row (lane % 32), the same 8 columns; this wave's K half
+  const char* op = olds + (lane & 31) * kCuRow + 16 * (lane >> 5) + 32 * kKB * kq;
   f32x16 acc = f32x16{};
-  constexpr int U = 8;
 #pragma unroll
-  for (int kk = 0; kk < kLatent / 16; kk += U) {
-    bf16x8 av[U], bv[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      av[i] = *(const bf16x8*)(wp + 16 * (kk + i));
-      bv[i] = *(const bf16x8*)(op + 32 * (kk + i));
-    }
-#pragma unroll
-    for (int i = 0; i < U; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[i], acc, 0, 0, 0);
+  for (int kb = 0; kb < kKB; ++kb) {
+    const bf16x8 bv = *(const bf16x8*)(op + 32 * kb);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wreg[kb], bv, acc, 0, 0, 0);
   }
-  // lane holds rows m = 32 wv + 8 g + 4 (lane / 32) + e of request lane % 32
+  // the two K halves of each row block meet in LDS
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[wv * 1024 + r * 64 + lane] = acc[r];
+  __syncthreads();
+  if (wv >= kDv / 32) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] += red[(rb + 4) * 1024 + r * 64 + lane];
+  // lane holds rows m = 32 rb + 8 g + 4 (lane / 32) + e of request lane % 32
   const int bl = lane & 31;
   if (bl < nb) {
-    __bf16* y = (__bf16*)u.out + ((int64_t)(b0 + bl) * kHeads + h) * kDv + 32 * wv + 4 * (lane >> 5);
+    __bf16* y = (__bf16*)u.out + ((int64_t)(b0 + bl) * kHeads + h) * kDv + 32 * rb + 4 * (lane >> 5);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       bf16x4 v;
