@@ -172,3 +172,32 @@ def test_indexer_layout_and_validation(B):
     assert lib.mla_topk_select(p, 16, p, 2, 4, p, p, 100, null) == B.MLA_ERR_INVALID_ARG   # workspace too small
     assert lib.mla_topk_select(null, 16, p, 2, 4, p, p, 1 << 16, null) == B.MLA_ERR_INVALID_ARG
     assert lib.mla_topk_select(p, 2048 * 4096 + 1, p, 1, 4, p, p, 1 << 40, null) == B.MLA_ERR_UNSUPPORTED
+
+
+def test_append_and_prefill_validation(B):
+    """Host-side checks of mla_cache_append and the prefill calls: bad
+    arguments are refused before anything is enqueued."""
+    lib = B.raw_lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.c_void_p((ctypes.addressof(buf) + 15) // 16 * 16)
+    null = None
+    cfg = v2(B)
+    c = ctypes.byref(cfg)
+    # append: both tables or neither; rows >= 1 with tables; batch >= 1
+    assert lib.mla_cache_append(c, p, p, p, null, 4, p, p, 1, p, 1, 1, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(c, p, p, p, p, 0, p, p, 1, p, 1, 1, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(c, p, p, null, null, 0, p, p, 1, p, 1, 0, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(c, null, p, null, null, 0, p, p, 1, p, 1, 1, null) == B.MLA_ERR_INVALID_ARG
+    odd = B.make_config(4, 16, 7, 8, 8, 0.25, B.MLA_F32, B.MLA_F32)
+    assert lib.mla_cache_append(ctypes.byref(odd), p, p, null, null, 0, p, p, 1, p, 1, 1, null) == B.MLA_ERR_UNSUPPORTED
+    # prefill: BF16 V2 dims only; counts and ranges checked
+    fp8 = v2(B, B.MLA_FP8_E4M3)
+    assert lib.mla_prepare_w_uk_t(ctypes.byref(fp8), p, p, null) == B.MLA_ERR_UNSUPPORTED
+    assert lib.mla_prepare_w_uk_t(c, null, p, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill_expand(c, p, 1, p, 0, p, p, p, p, p, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill_expand(c, p, 1, p, 64, p, p, null, p, p, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill_attn(c, p, p, p, p, p, 100, 90, 11, p, null, null) == B.MLA_ERR_INVALID_ARG   # past T
+    assert lib.mla_prefill_attn(c, p, p, p, p, p, 100, -1, 10, p, null, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill_attn(c, p, p, p, p, p, 100, 0, 0, p, null, null) == B.MLA_ERR_INVALID_ARG
+    tiny = B.make_config(4, 16, 8, 8, 8, 0.25, B.MLA_F32, B.MLA_F32)
+    assert lib.mla_prefill_attn(ctypes.byref(tiny), p, p, p, p, p, 100, 0, 10, p, null, null) == B.MLA_ERR_UNSUPPORTED
