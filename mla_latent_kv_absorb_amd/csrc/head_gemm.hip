@@ -18,6 +18,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 // Work-group: 4 waves, 64 batch columns (two 32-column accumulators per
 // wave, so each weight row is read from HBM once per 64 requests).
@@ -107,6 +108,77 @@ __global__ __launch_bounds__(256) void head_gemm_bf16_kernel(HeadGemmArgs a) {
   }
 }
 
+// K = 128 (the absorb at V2 dims): the work-group's 128 x 128 block of w
+// (32 KiB, contiguous in HBM) and its 64 x 128 block of x (16 KiB) are first
+// copied to LDS with fully coalesced 16-byte loads, each row's 16-byte chunks
+// XOR-swizzled by the row index so the operand reads below are free of bank
+// conflicts; then every wave reads its MFMA operands from LDS.  Each weight
+// byte is read from HBM once, in whole cache lines, and x once per
+// work-group.
+constexpr int kAbK = 128;
+constexpr int kAbRow = kAbK * 2;  // bytes per row
+__device__ __forceinline__ int ab_off(int row, int chunk) { return row * kAbRow + 16 * (chunk ^ (row & 15)); }
+
+__global__ __launch_bounds__(256) void absorb_k128_kernel(HeadGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char ws[128 * kAbRow];
+  __shared__ __attribute__((aligned(16))) char xs[64 * kAbRow];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int h = blockIdx.y;
+  const int mb = blockIdx.x * 128;  // first row of w
+  const int n0 = blockIdx.z * 64;   // first batch column
+  {
+    const char* wsrc = (const char*)a.w + ((int64_t)h * a.M + mb) * kAbRow;
+    i32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = *(const i32x4*)(wsrc + 16 * (t + 256 * i));
+    i32x4 xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = t + 256 * i, col = n0 + (q >> 4);
+      xv[i] = col < a.batch ? *(const i32x4*)((const char*)a.x + ((int64_t)col * a.H + h) * kAbRow + 16 * (q & 15))
+                            : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = t + 256 * i;
+      *(i32x4*)(ws + ab_off(q >> 4, q & 15)) = v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = t + 256 * i;
+      *(i32x4*)(xs + ab_off(q >> 4, q & 15)) = xv[i];
+    }
+  }
+  __syncthreads();
+  // wave wv: rows 32 wv .. +31 of the block; lane: row / column lane % 32,
+  // K chunk 2 kk + lane / 32
+  const int r = 32 * wv + (lane & 31), c = lane & 31, kg = lane >> 5;
+  f32x16 accA = f32x16{}, accB = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < kAbK / 16; ++kk) {
+    const bf16x8 av = *(const bf16x8*)(ws + ab_off(r, 2 * kk + kg));
+    const bf16x8 ba = *(const bf16x8*)(xs + ab_off(c, 2 * kk + kg));
+    const bf16x8 bb = *(const bf16x8*)(xs + ab_off(c + 32, 2 * kk + kg));
+    accA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ba, accA, 0, 0, 0);
+    accB = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bb, accB, 0, 0, 0);
+  }
+  // lane holds rows mb + 32 wv + 8g + 4 kg + e (e = 0..3) of its column
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int col = n0 + c + 32 * half;
+    if (col >= a.batch) continue;
+    const f32x16& acc = half ? accB : accA;
+    __bf16* yp = (__bf16*)a.y + ((int64_t)col * a.H + h) * a.M + mb + 32 * wv + 4 * kg;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * g + e];
+      *(bf16x4*)(yp + 8 * g) = v;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void head_gemm_f32_kernel(HeadGemmArgs a) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.batch * a.H * a.M;
@@ -125,7 +197,10 @@ __global__ __launch_bounds__(256) void head_gemm_f32_kernel(HeadGemmArgs a) {
 
 hipError_t launch_head_gemm_bf16(const HeadGemmArgs& a, hipStream_t s) {
   // requires M % 32 == 0 and K % 16 == 0 (checked by the caller)
-  if (a.K >= 256 && a.K % 64 == 0) {
+  if (a.K == kAbK && a.M % 128 == 0) {
+    const dim3 grid(a.M / 128, a.H, (a.batch + 63) / 64);
+    hipLaunchKernelGGL(absorb_k128_kernel, grid, dim3(256), 0, s, a);
+  } else if (a.K >= 256 && a.K % 64 == 0) {
     const dim3 grid(a.M / 32, a.H, (a.batch + 63) / 64);
     hipLaunchKernelGGL(head_gemm_bf16_kernel<4>, grid, dim3(256), 0, s, a);
   } else {
