@@ -5,7 +5,7 @@
 // 128, with the search key k_s stored as E4M3 values times one float32 scale
 // per position (section "Calculating V3.2's KV cache").
 //
-// Per work-group: 16 pages (1,024 positions) of one request, 4 waves, each
+// Per work-group: 64 pages (4,096 positions) of one request, 4 waves, each
 // wave 32 positions at a time.  The 64 x 128 query block of the request is the
 // MFMA A operand (two 32-head blocks, held in registers for the whole
 // work-group); the keys of 32 positions are the B operand, widened exactly
@@ -36,7 +36,7 @@ namespace {
 constexpr int kIdxHeads = 64;
 constexpr int kIdxDim = 128;
 constexpr int kIdxKeyRow = kIdxDim;          // bytes of one E4M3 key
-constexpr int kIdxChunkPages = 16;           // pages per score work-group
+constexpr int kIdxChunkPages = 64;           // pages per score work-group
 
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   // exact: every E4M3 value is a BF16 value (unit scale)

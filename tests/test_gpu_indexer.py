@@ -74,9 +74,12 @@ def check_pick_valid(idx_row, ref, T, k, what):
     assert not np.any(mask[ref < thr - band]), what
 
 
-def test_indexer_scores_ragged(torch, R):
-    _log("indexer scores, ragged lengths")
-    inp = I.make_indexer_inputs(seed=61, batch=3, ctx=(100, 2500), topk=64)
+@pytest.mark.parametrize("ctx", [(100, 2500), (4097, 9000)])
+def test_indexer_scores_ragged(torch, R, ctx):
+    """Lengths inside one work-group's 4,096-position chunk, and lengths that
+    span two or three chunks with a partial last one."""
+    _log(f"indexer scores, ragged lengths {ctx}")
+    inp = I.make_indexer_inputs(seed=61, batch=3, ctx=ctx, topk=64)
     w = R.IndexerWorkload(inp, score_stride=int(inp.seq_lens.max()) + 77)
     w.scores.fill_(12345.0)
     w.score()
