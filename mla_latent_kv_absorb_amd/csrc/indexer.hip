@@ -37,6 +37,13 @@ constexpr int kIdxHeads = 64;
 constexpr int kIdxDim = 128;
 constexpr int kIdxKeyRow = kIdxDim;          // bytes of one E4M3 key
 constexpr int kIdxChunkPages = 64;           // pages per score work-group
+constexpr int kIdxStages = 4;                // LDS ring stages per wave
+constexpr int kIdxStage = 32 * kIdxKeyRow + 256;  // keys of a half page + its page's scales
+constexpr int kIdxDmaPerStage = 5;           // load instructions per stage
+
+// chunk swizzle of key row r inside a stage (8 chunks of 16 bytes per row)
+__device__ __forceinline__ constexpr int idx_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
 
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   // exact: every E4M3 value is a BF16 value (unit scale)
@@ -79,37 +86,61 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
   const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
 
   // Wave w takes the half pages w, w + 4, ... of the chunk (32 positions
-  // each); the keys of the next half page are loaded while the current one is
-  // contracted.
-  struct Keys {
-    i32x4 r[4];
-    float sc;
+  // each) through a ring of kIdxStages LDS stages of its own: the keys (4 KiB)
+  // and the page's 64 scales are moved HBM -> LDS by the load unit, so the
+  // next stages are in flight while the current one is contracted, and the
+  // waits are explicit counts.  A stage holds key row r's 16-byte chunk c at
+  // chunk c ^ idx_swz(r), so the operand reads (row = lane % 32, 64 bytes at
+  // 64 (lane / 32)) hit distinct banks; the swizzle is folded into the HBM
+  // address of each lane, and every load instruction still covers 8 whole
+  // rows (1 KiB contiguous).  No other wave touches the ring: no barriers.
+  __shared__ __attribute__((aligned(16))) char idx_ring[4 * kIdxStages * kIdxStage];
+  LDS char* ring = (LDS char*)idx_ring + w * kIdxStages * kIdxStage;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+  const int64_t last_t = (T - 1) / 32 - 2 * p0;  // last half page before the context end
+  const int last_hp = (int)(last_t < 2 * kIdxChunkPages - 1 ? last_t : 2 * kIdxChunkPages - 1);
+  auto page_of = [&](int hp, bool& ok) {
+    const int32_t page = sload(bt + p0 + (hp >> 1));
+    ok = page >= 0 && page < a.num_pages;
+    return a.pool + (ok ? (int64_t)page * a.page_bytes : 0);
+  };
+  // half pages past the context end load the last one again (never read), so
+  // every iteration issues the same number of loads
+  auto issue = [&](int hp, int st) {
+    hp = hp <= last_hp ? hp : last_hp;
     bool ok;
-  };
-  auto fetch = [&](int hp, Keys& k) {
-    const int64_t p = p0 + (hp >> 1);
-    const int32_t page = sload(bt + p);
-    k.ok = page >= 0 && page < a.num_pages;
-    const uint8_t* pg = a.pool + (k.ok ? (int64_t)page * a.page_bytes : 0);
-    const int slot = 32 * (hp & 1) + col;
-    const i32x4* src = (const i32x4*)(pg + slot * kIdxKeyRow + 64 * hl);
+    const uint8_t* pg = page_of(hp, ok);
+    const uint8_t* keys = pg + 32 * (hp & 1) * kIdxKeyRow;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) k.r[m] = src[m];
-    k.sc = *(const float*)(pg + a.scale_off + 4 * slot);
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      dma16(keys + row * kIdxKeyRow + 16 * ((lane & 7) ^ idx_swz(row)), ring_addr + st * kIdxStage + 1024 * i);
+    }
+    dma4(pg + a.scale_off + 4 * ((32 * (hp & 1) + lane) & 63), ring_addr + st * kIdxStage + 4096);
   };
-  auto in_range = [&](int hp) { return hp < 2 * kIdxChunkPages && (p0 + (hp >> 1)) * 64 + 32 * (hp & 1) < T; };
 
-  if (!in_range(w)) return;
-  Keys cur, nxt;
-  fetch(w, cur);
-  for (int hp = w; in_range(hp); hp += 4) {
-    const bool more = in_range(hp + 4);
-    if (more) fetch(hp + 4, nxt);
+  if (w > last_hp) return;
+  // the query block and weights first: the loop's waits count ring loads only
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int d = 0; d < kIdxStages; ++d) issue(w + 4 * d, d);
+  int st = 0;
+  for (int hp = w; hp <= last_hp; hp += 4) {
+    // this stage's loads are done when at most the newer stages' are pending
+    wait_vmcnt<kIdxDmaPerStage * (kIdxStages - 1)>();
+    __builtin_amdgcn_sched_barrier(0);
+    const LDS char* sg = ring + st * kIdxStage;
+    i32x4 kr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) kr[m] = *(const LDS i32x4*)(sg + col * kIdxKeyRow + 16 * ((4 * hl + m) ^ idx_swz(col)));
+    const float sc = *(const LDS float*)(sg + 4096 + 4 * col);
+    bool ok;
+    (void)page_of(hp, ok);
     const int64_t pos = (p0 + (hp >> 1)) * 64 + 32 * (hp & 1) + col;
     f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const bf16x8 kv = e4m3x8_to_bf16((uint32_t)cur.r[kb >> 1][2 * (kb & 1)], (uint32_t)cur.r[kb >> 1][2 * (kb & 1) + 1]);
+      const bf16x8 kv = e4m3x8_to_bf16((uint32_t)kr[kb >> 1][2 * (kb & 1)], (uint32_t)kr[kb >> 1][2 * (kb & 1) + 1]);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][kb], kv, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][kb], kv, acc1, 0, 0, 0);
     }
@@ -122,9 +153,14 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
     sum += wave_partner(sum);  // the other 32 heads of this position
     // a position on a page id out of range scores -infinity (its loads went
     // to page 0 and are discarded)
-    if (hl == 0 && pos < T) out[pos] = cur.ok ? sum * cur.sc : -INFINITY;
-    if (more) cur = nxt;
+    if (hl == 0 && pos < T) out[pos] = ok ? sum * sc : -INFINITY;
+    // refill the stage just read (its reads returned before the MFMAs above)
+    __builtin_amdgcn_sched_barrier(0);
+    issue(hp + 4 * kIdxStages, st);
+    st = st + 1 == kIdxStages ? 0 : st + 1;
   }
+  // no load may still be writing this work-group's LDS when it ends
+  wait_vmcnt<0>();
 }
 
 // ---- top-k pick ----
