@@ -274,11 +274,12 @@ def cache_append_part(torch, I, w, reps=200):
 
 def indexer_step(torch, I, runner, reps=10, layers=4, attn=None):
     """The lightning indexer over 32 requests x 65,536 positions (64 heads x
-    128, FP8 search keys, 132 B per position), then the top-2,048 pick.  Four
-    independent draws (277 MB of keys each) are cycled so the scans read HBM.
-    With ``attn`` (an FP8 top-k DeviceWorkload of the same shape) it also
-    times the whole sparse decode step: scores, pick, absorb, attention over
-    the picked positions, merge + up-projection."""
+    128, FP8 search keys, 132 B per position), then the top-2,048 pick, as two
+    calls and as one (mla_indexer_topk).  Four independent draws (277 MB of
+    keys each) are cycled so the scans read HBM.  With ``attn`` (an FP8 top-k
+    DeviceWorkload of the same shape) it also times the whole sparse decode
+    step: scores and pick (one call), absorb, attention over the picked
+    positions, merge + up-projection."""
     ws = []
     for layer in range(layers):
         inp = I.make_indexer_inputs(seed=600 + layer)
@@ -302,7 +303,17 @@ def indexer_step(torch, I, runner, reps=10, layers=4, attn=None):
     torch.cuda.synchronize()
     score_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
     select_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    # both steps as one call (the first histogram built by the score kernel)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        for w in ws:
+            w.score_and_select()
+    b.record()
+    torch.cuda.synchronize()
+    fused_us = a.elapsed_time(b) * 1e3 / (reps * layers)
     res = {"score_us": round(score_us, 2), "select_us": round(select_us, 2),
+           "score_and_select_one_call_us": round(fused_us, 2),
            "key_bytes_per_step": int(key_bytes),
            "score_key_GBps": round(key_bytes / (score_us * 1e-6) / 1e9, 1),
            "score_hbm_frac": round(key_bytes / (score_us * 1e-6) / (HBM_PEAK_GBPS * 1e9), 4),
@@ -310,7 +321,7 @@ def indexer_step(torch, I, runner, reps=10, layers=4, attn=None):
     if attn is not None:
         # the picked lists of each draw drive the attention over the FP8 cache
         for w in ws:
-            w.step()
+            w.score_and_select()
             attn.topk_idx = w.idx
             attn.step_fused()
         torch.cuda.synchronize()
@@ -318,7 +329,7 @@ def indexer_step(torch, I, runner, reps=10, layers=4, attn=None):
         a.record()
         for _ in range(reps):
             for w in ws:
-                w.step()
+                w.score_and_select()
                 attn.topk_idx = w.idx
                 attn.step_fused()
         b.record()

@@ -13,6 +13,8 @@
  *   2. mla_topk_select      per request, up to k of the highest-scoring
  *                           positions 0 .. seq_lens[b]-1, sorted by position.
  *
+ * mla_indexer_topk runs both in one call.
+ *
  * Same conventions as mla_absorb.h: every buffer belongs to the caller and
  * lives in device memory unless stated; the library allocates nothing, keeps
  * no state and never synchronises; every call checks its host-visible
@@ -83,6 +85,22 @@ size_t mla_topk_workspace_bytes(int32_t batch, int64_t score_stride);
 mla_status mla_topk_select(const float* scores, int64_t score_stride, const int32_t* seq_lens, int32_t batch,
                            int32_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* Steps 1 and 2 in one call: the scores of mla_indexer_scores, then the pick
+ * of mla_topk_select over them, with the pick's first radix histogram built
+ * while the scores are computed (one pass over the score rows fewer).  The
+ * arguments are those of the two calls; T_b here is
+ * min(seq_lens[b], score_stride, 64 * block_table_stride), the positions that
+ * get a score, so idx_out equals what the two calls give whenever
+ * seq_lens[b] <= 64 * block_table_stride.  scores is written as by step 1.
+ *   workspace: mla_topk_workspace_bytes(batch, score_stride) bytes, 16-byte
+ *   aligned; calls that share a workspace must not overlap.
+ * Errors: those of the two calls. */
+mla_status mla_indexer_topk(int32_t n_heads, int32_t dim, const void* q_idx, const float* w_idx,
+                            const void* key_pool, int64_t num_pages, const int32_t* block_table,
+                            int32_t block_table_stride, const int32_t* seq_lens, int32_t batch,
+                            float* scores, int64_t score_stride, int32_t k, int32_t* idx_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,6 +30,7 @@ EXPORTED = (
     "mla_check_decode_inputs_host", "mla_cache_append",
     "mla_prepare_w_uk_t", "mla_prefill_expand", "mla_prefill_attn",
     "mla_indexer_page_layout", "mla_indexer_scores", "mla_topk_workspace_bytes", "mla_topk_select",
+    "mla_indexer_topk",
 )
 INDEXER_HEADS, INDEXER_DIM = 64, 128
 
@@ -81,6 +82,7 @@ def _load():
         "mla_indexer_scores": ([I32, I32, P, P, P, I64, P, I32, P, I32, P, I64, P], I32),
         "mla_topk_workspace_bytes": ([I32, I64], SZ),
         "mla_topk_select": ([P, I64, P, I32, I32, P, P, SZ, P], I32),
+        "mla_indexer_topk": ([I32, I32, P, P, P, I64, P, I32, P, I32, P, I64, I32, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -368,3 +370,26 @@ def mla_topk_select(scores, seq_lens, k: int, idx_out, workspace, stream=None):
         B, int(k), _dev(idx_out, "idx_out", torch.int32, (B, k)), _dev(workspace, "workspace"),
         int(workspace.numel() * workspace.element_size()), _stream(stream))
     _check("mla_topk_select", st)
+
+
+def mla_indexer_topk(q_idx, w_idx, key_pool, block_table, seq_lens, scores, k: int, idx_out, workspace,
+                     stream=None):
+    """scores as mla_indexer_scores, then idx_out [B, k] as mla_topk_select,
+    in one call."""
+    torch = _torch()
+    B, H, D = q_idx.shape
+    page_bytes, _ = indexer_page_layout(D)
+    if key_pool.dtype != torch.uint8 or key_pool.dim() != 2 or key_pool.shape[1] != page_bytes:
+        raise ValueError(f"key_pool must be uint8 [num_pages, {page_bytes}]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [batch, stride]")
+    if scores.dim() != 2 or scores.shape[0] != B:
+        raise ValueError("scores must be float32 [batch, stride]")
+    st = _lib.mla_indexer_topk(
+        H, D, _dev(q_idx, "q_idx", torch.bfloat16), _dev(w_idx, "w_idx", torch.float32, (B, H)),
+        _dev(key_pool, "key_pool"), int(key_pool.shape[0]), _dev(block_table, "block_table", torch.int32),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, (B,)), B,
+        _dev(scores, "scores", torch.float32), int(scores.shape[1]), int(k),
+        _dev(idx_out, "idx_out", torch.int32, (B, k)), _dev(workspace, "workspace"),
+        int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check("mla_indexer_topk", st)

@@ -56,6 +56,17 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// order-preserving image of a float: larger score -> larger key; -0 == +0;
+// NaN below everything
+__device__ __forceinline__ uint32_t score_key(float x) {
+  if (x != x) return 0u;
+  uint32_t u = __float_as_uint(x);
+  if (x == 0.f) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kHistBins = 2048;            // first and second digit: 11 bits
+
 __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -67,6 +78,13 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
   if (T > (int64_t)a.bt_stride * 64) T = (int64_t)a.bt_stride * 64;
   const int64_t p0 = (int64_t)blockIdx.x * kIdxChunkPages;
   if (T <= 0 || p0 * 64 >= T) return;
+  // fused pick: first-digit histogram of this work-group's scores in LDS
+  __shared__ uint32_t hist_l[kHistBins];
+  const bool do_hist = a.hist != nullptr && T > a.topk;  // work-group uniform
+  if (do_hist) {
+    for (int i = threadIdx.x; i < kHistBins; i += 256) hist_l[i] = 0u;
+    __syncthreads();
+  }
 
   // A operand: query rows 32 mb + col, dims 64 hl + 8 kb .. +7
   const __bf16* qb = (const __bf16*)a.q + (int64_t)b * kIdxHeads * kIdxDim;
@@ -119,11 +137,15 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
     dma4(pg + a.scale_off + 4 * ((32 * (hp & 1) + lane) & 63), ring_addr + st * kIdxStage + 4096);
   };
 
-  if (w > last_hp) return;
+  // a wave with no half page skips the loop but still meets the barrier of
+  // the histogram flush
+  const bool any = w <= last_hp;
   // the query block and weights first: the loop's waits count ring loads only
   wait_vmcnt<0>();
+  if (any) {
 #pragma unroll
-  for (int d = 0; d < kIdxStages; ++d) issue(w + 4 * d, d);
+    for (int d = 0; d < kIdxStages; ++d) issue(w + 4 * d, d);
+  }
   int st = 0;
   for (int hp = w; hp <= last_hp; hp += 4) {
     // this stage's loads are done when at most the newer stages' are pending
@@ -153,7 +175,11 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
     sum += wave_partner(sum);  // the other 32 heads of this position
     // a position on a page id out of range scores -infinity (its loads went
     // to page 0 and are discarded)
-    if (hl == 0 && pos < T) out[pos] = ok ? sum * sc : -INFINITY;
+    if (hl == 0 && pos < T) {
+      const float v = ok ? sum * sc : -INFINITY;
+      out[pos] = v;
+      if (do_hist) atomicAdd(&hist_l[score_key(v) >> 21], 1u);
+    }
     // refill the stage just read (its reads returned before the MFMAs above)
     __builtin_amdgcn_sched_barrier(0);
     issue(hp + 4 * kIdxStages, st);
@@ -161,6 +187,12 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
   }
   // no load may still be writing this work-group's LDS when it ends
   wait_vmcnt<0>();
+  if (do_hist) {
+    __syncthreads();
+    uint32_t* g = a.hist + (int64_t)b * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256)
+      if (hist_l[i] != 0u) atomicAdd(&g[i], hist_l[i]);
+  }
 }
 
 // ---- top-k pick ----
@@ -173,7 +205,6 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
 //   take [b][C]      per chunk: threshold-equal keys it contributes
 //   ckey, cpos [b][stride]  keys and positions of the threshold digit's bin
 // with C = ceil(stride / 4096) chunks.
-constexpr int kHistBins = 2048;            // first and second digit: 11 bits
 constexpr int kChunk = 4096;               // positions per chunk work-group
 constexpr int kCtrl = 16;
 constexpr int kRefineThreads = 1024;
@@ -206,19 +237,12 @@ __device__ __forceinline__ TopkSpace topk_space(const TopkArgs& a) {
   return w;
 }
 
-// order-preserving image of a float: larger score -> larger key; -0 == +0;
-// NaN below everything
-__device__ __forceinline__ uint32_t score_key(float x) {
-  if (x != x) return 0u;
-  uint32_t u = __float_as_uint(x);
-  if (x == 0.f) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 __device__ __forceinline__ int64_t sel_len(const TopkArgs& a, int b) {
   int64_t T = sload(a.seq_lens + b);
   if (T < 0) T = 0;
   if (T > a.score_stride) T = a.score_stride;
+  if (T > a.len_cap) T = a.len_cap;
   return T;
 }
 
@@ -538,6 +562,18 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(topk_gather_kernel, chunks, dim3(256), 0, s, a);
   hipLaunchKernelGGL(topk_refine_kernel, dim3(a.batch), dim3(kRefineThreads), 0, s, a);
   hipLaunchKernelGGL(topk_write_kernel, chunks, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_topk(const IndexerArgs& a, const TopkArgs& t, hipStream_t s) {
+  const int64_t n = (int64_t)t.batch * (kHistBins + kCtrl);
+  hipLaunchKernelGGL(topk_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, t.hist, n);
+  const dim3 grid((a.bt_stride + kIdxChunkPages - 1) / kIdxChunkPages, a.batch);
+  hipLaunchKernelGGL(indexer_score_kernel, grid, dim3(256), 0, s, a);
+  const dim3 chunks((unsigned)topk_chunks(t.score_stride), t.batch);
+  hipLaunchKernelGGL(topk_gather_kernel, chunks, dim3(256), 0, s, t);
+  hipLaunchKernelGGL(topk_refine_kernel, dim3(t.batch), dim3(kRefineThreads), 0, s, t);
+  hipLaunchKernelGGL(topk_write_kernel, chunks, dim3(256), 0, s, t);
   return hipGetLastError();
 }
 

@@ -70,6 +70,11 @@ struct IndexerArgs {
   int32_t batch;
   float* scores;            // [batch][score_stride]
   int64_t score_stride;
+  // fused pick: when set, each score's first radix digit is also counted
+  // into this request's histogram of the pick workspace (requests with more
+  // than topk positions only)
+  uint32_t* hist;
+  int32_t topk;
 };
 
 // top-k pick over score rows
@@ -81,10 +86,14 @@ struct TopkArgs {
   int32_t k;
   int32_t* idx_out;         // [batch][k]
   uint32_t* hist;           // workspace (layout in the pick kernels)
+  int64_t len_cap;          // positions at or past it are not candidates
 };
 
 hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
+// scores, with the pick's first histogram built by the score kernel, then the
+// rest of the pick (a.hist and t.hist are the same workspace)
+hipError_t launch_indexer_topk(const IndexerArgs& a, const TopkArgs& t, hipStream_t s);
 size_t topk_workspace_bytes(int32_t batch, int64_t score_stride);
 int64_t topk_max_stride();
 

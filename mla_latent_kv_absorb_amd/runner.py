@@ -165,6 +165,11 @@ class IndexerWorkload:
         self.score(stream)
         self.select(stream)
 
+    def score_and_select(self, stream=None):
+        """Both calls as one (mla_indexer_topk)."""
+        B.mla_indexer_topk(self.q, self.w, self.pool, self.table, self.seq_lens, self.scores, self.k, self.idx,
+                           self.workspace, stream)
+
 
 class PrefillWorkload:
     """One request's prefill on the expanded path: the request's cache pages,

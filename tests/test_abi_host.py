@@ -172,6 +172,15 @@ def test_indexer_layout_and_validation(B):
     assert lib.mla_topk_select(p, 16, p, 2, 4, p, p, 100, null) == B.MLA_ERR_INVALID_ARG   # workspace too small
     assert lib.mla_topk_select(null, 16, p, 2, 4, p, p, 1 << 16, null) == B.MLA_ERR_INVALID_ARG
     assert lib.mla_topk_select(p, 2048 * 4096 + 1, p, 1, 4, p, p, 1 << 40, null) == B.MLA_ERR_UNSUPPORTED
+    # both steps in one call: the checks of the two
+    ws = 1 << 16
+    assert lib.mla_indexer_topk(32, 128, p, p, p, 1, p, 1, p, 1, p, 16, 4, p, p, ws, null) == B.MLA_ERR_UNSUPPORTED
+    assert lib.mla_indexer_topk(64, 128, p, p, p, 1, p, 1, p, 1, p, 16, 0, p, p, ws, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_indexer_topk(64, 128, p, p, p, 1, p, 1, p, 1, p, 16, 4, null, p, ws, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_indexer_topk(64, 128, p, p, p, 1, p, 0, p, 1, p, 16, 4, p, p, ws, null) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_indexer_topk(64, 128, p, p, p, 1, p, 1, p, 1, p, 16, 4, p, p, 100, null) == B.MLA_ERR_INVALID_ARG
+    assert (lib.mla_indexer_topk(64, 128, p, p, p, 1, p, 1, p, 1, p, 2048 * 4096 + 1, 4, p, p, 1 << 40, null)
+            == B.MLA_ERR_UNSUPPORTED)
 
 
 def test_append_and_prefill_validation(B):

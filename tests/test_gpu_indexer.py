@@ -169,16 +169,64 @@ def test_indexer_then_pick_small(torch, R):
         check_pick_valid(idx[b], oracle_scores(inp, b), T, inp.topk, f"b={b}")
 
 
+def _two_calls_then_fused(torch, w):
+    """(scores, idx) of the two calls, then of the one-call form, on w."""
+    w.step()
+    torch.cuda.synchronize()
+    s2, i2 = w.scores.cpu().numpy().copy(), w.idx.cpu().numpy().copy()
+    w.scores.fill_(777.0)
+    w.idx.fill_(-7)
+    w.score_and_select()
+    torch.cuda.synchronize()
+    return s2, i2, w.scores.cpu().numpy(), w.idx.cpu().numpy()
+
+
+def test_fused_indexer_topk_equals_two_calls(torch, R):
+    """mla_indexer_topk builds the pick's first histogram inside the score
+    kernel: same float32 scores, same picks (bit-exact), on ragged rows that
+    span several chunks, with some rows at or below k."""
+    _log("indexer + pick in one call, ragged")
+    # request 1 has exactly k positions and request 3 fewer: every position
+    # is picked and no histogram is built for them
+    inp = I.make_indexer_inputs(seed=64, seq_lens=[3000, 2048, 9500, 1500, 7001], topk=2048)
+    w = R.IndexerWorkload(inp, score_stride=int(inp.seq_lens.max()) + 50)
+    s2, i2, s1, i1 = _two_calls_then_fused(torch, w)
+    for b in range(inp.B):
+        T = int(inp.seq_lens[b])
+        assert np.array_equal(s1[b, :T].view(np.uint32), s2[b, :T].view(np.uint32)), f"scores b={b}"
+    assert np.array_equal(i1, i2)
+    check_pick_valid(i1[0], oracle_scores(inp, 0), int(inp.seq_lens[0]), inp.topk, "b=0")
+
+
+def test_fused_indexer_topk_caps_at_block_table(torch, R):
+    """Positions past 64 * block_table_stride have no page: the one-call form
+    scores and picks among min(seq_len, 64 * stride) positions, which is what
+    the two calls give with the lengths capped there."""
+    _log("indexer + pick in one call, short block table")
+    inp = I.make_indexer_inputs(seed=65, batch=3, ctx=(6000, 9000), topk=512)
+    pool, table = I.build_key_pool(inp)
+    n = 80                                        # 5,120 positions reachable
+    short = np.ascontiguousarray(table[:, :n])
+    w = R.IndexerWorkload(inp, pool=pool, table=short, score_stride=int(inp.seq_lens.max()))
+    w.score_and_select()
+    torch.cuda.synchronize()
+    i1 = w.idx.cpu().numpy().copy()
+    w.seq_lens.copy_(torch.from_numpy(np.minimum(inp.seq_lens, 64 * n).astype(np.int32)))
+    w.step()
+    torch.cuda.synchronize()
+    assert np.array_equal(i1, w.idx.cpu().numpy())
+
+
 def test_indexer_then_pick_full_size_sampled(torch, R):
     """32 requests x 65,536 positions, top-2,048: the sizes and launch shape
-    the benchmark times; scores and picks checked on sampled requests."""
+    the benchmark times; scores and picks checked on sampled requests, and the
+    one-call form equal to the two calls on every request."""
     _log("indexer full size")
     inp = I.make_indexer_inputs()
     w = R.IndexerWorkload(inp)
-    w.step()
-    torch.cuda.synchronize()
-    scores = w.scores.cpu().numpy()
-    idx = w.idx.cpu().numpy()
+    scores, idx, s1, i1 = _two_calls_then_fused(torch, w)
+    assert np.array_equal(s1.view(np.uint32), scores.view(np.uint32))
+    assert np.array_equal(i1, idx)
     for b in (0, 13, 31):
         ref = oracle_scores(inp, b)
         check_scores(scores[b], ref, f"b={b}")
