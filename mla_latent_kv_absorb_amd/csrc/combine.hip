@@ -257,7 +257,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 // KV Cache", Figure 6, form (2)).  The merged latent never goes to HBM.
 constexpr int kCuThreads = 512;
 constexpr int kCuWaves = kCuThreads / 64;
-constexpr int kCuReq = 32;                // requests per work-group (MFMA N)
+constexpr int kCuReq = 32;                // MFMA N: requests per work-group at most
+// requests per work-group: 16 up to 32 requests, so that 32 requests still
+// make two work-groups per head and fill the chip (the MFMA columns of the
+// missing requests are zero)
+__host__ __device__ constexpr int cu_group(int batch) { return batch <= 32 ? 16 : kCuReq; }
 constexpr int kCuRow = kLatent * 2 + 16;  // LDS row pitch in bytes (padded against bank conflicts)
 constexpr int kDv = 128;
 
@@ -271,8 +275,9 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
   __shared__ int64_t below_s[kCuReq + 1];  // units below each request of the group; [kCuReq] = total
   const CombineArgs& a = u.c;
   const int h = blockIdx.x;
-  const int32_t b0 = blockIdx.y * kCuReq;
-  const int32_t nb = a.batch - b0 < kCuReq ? a.batch - b0 : kCuReq;
+  const int grp = cu_group(a.batch);
+  const int32_t b0 = blockIdx.y * grp;
+  const int32_t nb = a.batch - b0 < grp ? a.batch - b0 : grp;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int64_t row_stride = (int64_t)kHeads * kLatent;
@@ -421,7 +426,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 
 hipError_t launch_combine_up(const CombineUpArgs& u, hipStream_t s) {
   // V2 dims, BF16 partials and output (checked by the caller)
-  const dim3 grid(kHeads, (u.c.batch + kCuReq - 1) / kCuReq);
+  const int grp = cu_group(u.c.batch);
+  const dim3 grid(kHeads, (u.c.batch + grp - 1) / grp);
   hipLaunchKernelGGL(combine_up_kernel, grid, dim3(kCuThreads), 0, s, u);
   return hipGetLastError();
 }

@@ -214,13 +214,14 @@ def test_v2_absorb_and_up_projection_alone(torch, R, v2_ragged):
     assert_close(to_np(w.out), oracle.up_project(x, inp.w_uv), what="out_up")
 
 
-@pytest.mark.parametrize("batch", [3, 37])
+@pytest.mark.parametrize("batch", [3, 20, 37])
 def test_v2_fused_combine_up(torch, R, batch):
     """mla_combine_out_up: against the oracle, and against mla_combine then
     mla_out_up on the same partials.  The merge is the same code, so lse is
     bit-identical; out may differ in the last BF16 bit (GEMM summation order).
-    37 requests span two request blocks of the fused kernel, the second one
-    partial."""
+    The fused kernel takes requests in blocks of 16 (up to 32 requests) or 32:
+    20 requests make a full block and a partial one of 16, 37 a full one and a
+    partial one of 32."""
     _log(f"fused merge + up-projection, batch {batch}")
     inp = I.make_inputs("v2_batched", seed=31, batch=batch, ctx=(40, 900))
     for nw in (None, 7):
