@@ -99,6 +99,11 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) wt[mb][r] = a.w[(int64_t)b * kIdxHeads + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3)];
+  float wh[2][16];  // halved weights (see the ReLU below)
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wh[mb][r] = 0.5f * wt[mb][r];
 
   float* out = a.scores + (int64_t)b * a.score_stride;
   const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
@@ -166,11 +171,15 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][kb], kv, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][kb], kv, acc1, 0, 0, 0);
     }
+    // w ReLU(x) as (w / 2)(x + |x|): one add with an abs modifier and the
+    // fma, where fmaxf(x, 0) costs two instructions (it quiets x first).  The
+    // product is exactly w x for x > 0 (halving and doubling are exact) and
+    // +0 otherwise, so the sum is the same to the bit.
     float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sum = fmaf(wt[0][r], fmaxf(acc0[r], 0.f), sum);
-      sum = fmaf(wt[1][r], fmaxf(acc1[r], 0.f), sum);
+      sum = fmaf(wh[0][r], acc0[r] + fabsf(acc0[r]), sum);
+      sum = fmaf(wh[1][r], acc1[r] + fabsf(acc1[r]), sum);
     }
     sum += wave_partner(sum);  // the other 32 heads of this position
     // a position on a page id out of range scores -infinity (its loads went
