@@ -421,9 +421,12 @@ def test_v2_batched_full_size_sampled(torch, R):
     check_step(torch, R, inp, split=True, requests=[0, 31, 63], heads=[0, 77, 127])
 
 
-def test_v2_long_layer_sampled(torch, R):
-    _log("v2_long one layer")
-    inp = I.make_inputs("v2_long", layer=29)
+@pytest.mark.parametrize("layer", [0, 29, 59])
+def test_v2_long_layer_sampled(torch, R, layer):
+    """Long context (1 request x 131,072 positions): the first, middle and
+    last of the 60 independently drawn layers, on sampled heads."""
+    _log(f"v2_long layer {layer}")
+    inp = I.make_inputs("v2_long", layer=layer)
     check_step(torch, R, inp, split=True, requests=[0], heads=[0, 64, 127])
 
 
