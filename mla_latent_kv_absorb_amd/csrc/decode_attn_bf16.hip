@@ -406,20 +406,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
               s[r] = pos < nvis ? s[r] : -INFINITY;
             }
           }
-          mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+          mt = max3_raw(max3_raw(s[0], s[1], s[2]), max3_raw(s[3], s[4], s[5]), max_raw(s[6], s[7]));
           asm volatile("" : "+v"(mt));
         } else if (k == 1) {
-          mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
-                               fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+          mt = max3_raw(max3_raw(mt, s[8], s[9]), max3_raw(s[10], s[11], s[12]), max3_raw(s[13], s[14], s[15]));
           asm volatile("" : "+v"(mt));
         } else if (k == 2) {
-          mt = fmaxf(mt, wave_partner(mt)) * scale_log2;
+          mt = max_raw(mt, wave_partner(mt)) * scale_log2;
           asm volatile("" : "+v"(mt));
         } else if (k == 3) {
           // Lazy rescale: keep the reference maximum unless the tile's
           // maximum exceeds it by more than 8 (log2 units), so probabilities
           // stay <= 256 and the accumulator is rescaled rarely.
-          const float m_new = fmaxf(m_run, mt);
+          const float m_new = max_raw(m_run, mt);
           need = m_new > m_run + 8.0f;
           m_use = need ? m_new : m_run;
           neg_m = (m_use == -INFINITY) ? 0.f : -m_use;
