@@ -25,15 +25,39 @@ constexpr int kUnroll = 8;  // partials whose loads are in flight together
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
+// Wave-wide reductions without the LDS crossbar: butterflies inside each
+// 16-lane row by DPP (swap neighbours, swap pairs, mirror 8, mirror 16), then
+// the neighbouring row and the other half of the wave by the permlane swaps.
+// Every lane ends with the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_partner(float v) {
+  // value held by lane l ^ 16
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float half_partner(float v) {
+  // value held by lane l ^ 32
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm 1,0,3,2
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm 2,3,0,1
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  v = fmaxf(v, row_partner(v));
+  return fmaxf(v, half_partner(v));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  v += row_partner(v);
+  return v + half_partner(v);
 }
 
 // 8 consecutive partial values starting at src, as FP32
