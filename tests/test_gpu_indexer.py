@@ -181,21 +181,28 @@ def _two_calls_then_fused(torch, w):
     return s2, i2, w.scores.cpu().numpy(), w.idx.cpu().numpy()
 
 
-def test_fused_indexer_topk_equals_two_calls(torch, R):
+@pytest.mark.parametrize("stride", ["wide", 5000])
+def test_fused_indexer_topk_equals_two_calls(torch, R, stride):
     """mla_indexer_topk builds the pick's first histogram inside the score
     kernel: same float32 scores, same picks (bit-exact), on ragged rows that
-    span several chunks, with some rows at or below k."""
-    _log("indexer + pick in one call, ragged")
+    span several chunks, with some rows at or below k.  With score rows of
+    5,000 entries the longer requests are cut to the row width in both
+    paths."""
+    _log(f"indexer + pick in one call, ragged, stride {stride}")
     # request 1 has exactly k positions and request 3 fewer: every position
     # is picked and no histogram is built for them
     inp = I.make_indexer_inputs(seed=64, seq_lens=[3000, 2048, 9500, 1500, 7001], topk=2048)
-    w = R.IndexerWorkload(inp, score_stride=int(inp.seq_lens.max()) + 50)
+    width = int(inp.seq_lens.max()) + 50 if stride == "wide" else stride
+    w = R.IndexerWorkload(inp, score_stride=width)
     s2, i2, s1, i1 = _two_calls_then_fused(torch, w)
     for b in range(inp.B):
-        T = int(inp.seq_lens[b])
+        T = min(int(inp.seq_lens[b]), width)
         assert np.array_equal(s1[b, :T].view(np.uint32), s2[b, :T].view(np.uint32)), f"scores b={b}"
     assert np.array_equal(i1, i2)
     check_pick_valid(i1[0], oracle_scores(inp, 0), int(inp.seq_lens[0]), inp.topk, "b=0")
+    if stride != "wide":
+        # request 2 (9,500 positions) is picked among its first 5,000
+        check_pick_valid(i1[2], oracle_scores(inp, 2)[:width], width, inp.topk, "b=2 cut to the row")
 
 
 def test_fused_indexer_topk_caps_at_block_table(torch, R):
