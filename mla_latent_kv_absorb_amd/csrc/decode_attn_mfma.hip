@@ -305,15 +305,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8*)(ql + 16 * kb);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) qr[kb] = *(const bf16x8*)(qp + 16 * kb);
+      }
+      __syncthreads();  // the row list is complete
+      // the first tiles go in flight while the queries are still loading
+      const int32_t pro = clen < NS - 1 ? clen : NS - 1;
+      for (int32_t k = 0; k < pro; ++k) ld.issue(k, tc0 + k, tc0, T, list, smem);
+      if (tc0 == ct) {
+        // take the queries here, once per segment, so the wait for them is
+        // placed before the tile loop and not inside it
 #pragma unroll
         for (int kb = 0; kb < 32; ++kb) asm volatile("" ::"v"(q[kb]));
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) asm volatile("" ::"v"(qr[kb]));
       }
-      wait_vmcnt<0>();
-      __syncthreads();
-      const int32_t pro = clen < NS - 1 ? clen : NS - 1;
-      for (int32_t k = 0; k < pro; ++k) ld.issue(k, tc0 + k, tc0, T, list, smem);
 
       for (int32_t j = 0; j < clen; ++j) {
         const int st = j % NS;
