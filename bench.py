@@ -1,26 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark: weight-absorbed MLA decode on one MI355X.
 
-Workload: DeepSeek-V2 dims (128 heads, latent 512, rotary 64, head dim 128),
-BF16 latent cache in 64-token pages shuffled across one pool, batch 64 with
-per-request contexts uniform in [16,384, 32,768]; one decode step per request.
-A step is the whole path: absorb_q -> decode_attn -> combine + out_up (one
-launch, mla_combine_out_up), on one stream, inputs resident in HBM before
-timing starts.
+Headline workload: DeepSeek-V2 dims (128 heads, latent 512, rotary 64, head
+dim 128), BF16 latent cache in 64-token pages shuffled across one pool, batch
+64 with per-request contexts uniform in [16,384, 32,768]; one decode step per
+request.  A step is the whole path: absorb_q -> decode_attn -> combine +
+out_up (one launch, mla_combine_out_up), on one stream, inputs resident in HBM
+before timing starts.  Before the W warmup steps, untimed steps run for
+--settle-s seconds so the GPU clock has left its idle level; a clock probe
+around the timed region reports the mean shader clock over it.
 
 Prints one JSON line.  `value` is the latent-KV read rate of the whole step:
 cache bytes read per step (each visible position's 1,152-byte item once) over
 the step time.  Also reported: decode tokens/s, the attention kernel's own
 rate against the HBM roofline (HIP events around every attention launch in
-the timed region), the float64 CPU oracle timed on whole requests of the
-same workload on the host cores (about 15 s of work), each launch's time with
-the matrix-core utilisation of the attention and the weight rate of the two
-head GEMMs ("parts"), and a plain streaming read for reference.  --long adds
-one layer of the long-context workload (1 request x 131,072 positions);
---fp8-topk adds the FP8-cache, top-2,048 workload, with one scale per token
-and, from the same draw, with one scale per 128 latent channels.  --indexer
-adds the lightning indexer scan and top-k pick over 32 x 65,536 positions
-(and, with --fp8-topk, the whole sparse decode step fed by its picks).
+the timed region), each launch's time (mean and median) with the matrix-core
+utilisation of the attention and the weight rate of the two head GEMMs
+("parts"), a hand-written streaming read for reference, and the float64 CPU
+oracle on whole requests of the same workload on the host cores.
+
+`configs` times the other workloads in the same process, each beside its
+oracle time: the tiny float32 step; the single 4,096-token request (cycled
+over 64 pool copies so it reads HBM); one token of the 131,072-token workload
+over 60 independent layers (one HIP graph); the FP8 top-2,048 workload with
+one scale per position and with one per 128 channels.  The long-context and
+FP8 workloads are drawn on the device (see device_inputs.py).  --indexer adds
+the lightning indexer scan and pick, and the sparse decode step they feed;
 --prefill adds prefill of a 4,096-token prompt on the expanded path.
 """
 
@@ -72,128 +77,342 @@ def traffic_from_profile():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, budget_s=15.0):
-    """The float64 oracle, as it stands, on whole requests of the same
-    workload (all heads, unabsorbed) on the host cores: requests 0, 1, ...
-    until about budget_s seconds have passed.  Rate in the metric's unit:
-    cache bytes of the requests done per second."""
-    import oracle
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def _oracle_requests(inp, requests):
+    """Run the float64 oracle on whole requests (all heads, unabsorbed);
+    returns per-request seconds."""
+    import oracle
+    times = []
+    for b in requests:
+        lo, hi = inp.request(b)
+        if inp.cache_dtype in ("fp8_e4m3", "fp8_e4m3_g128"):
+            c = oracle.dequant_fp8_latent(inp.c_codes[lo:hi], inp.c_scales[lo:hi])
+        else:
+            c = inp.c_kv[lo:hi]
+        picked = None if inp.topk_idx is None else inp.topk_idx[b]
+        t = time.perf_counter()
+        oracle.decode_unabsorbed(c, inp.k_rope[lo:hi], inp.q_nope[b], inp.q_rope[b], inp.w_uk, inp.w_uv,
+                                 inp.scale, picked=picked)
+        times.append(time.perf_counter() - t)
+    return times
+
+
+def cpu_baseline(inp, budget_s=12.0, full=False):
+    """The float64 oracle, as it stands, on whole requests of the batched
+    workload (all heads, unabsorbed) on the host cores: requests 0, 1, ...
+    until about budget_s seconds have passed (every request with full=True).
+    Rate in the metric's unit: cache bytes of the requests done per second
+    (their total over their total time; the median per-request rate is given
+    beside it)."""
     item = (inp.D_C + inp.D_R) * 2
-    done_bytes, done, positions = 0, 0, 0
+    times, done = [], []
     t0 = time.perf_counter()
     for b in range(inp.B):
-        lo, hi = inp.request(b)
-        oracle.decode_unabsorbed(inp.c_kv[lo:hi], inp.k_rope[lo:hi], inp.q_nope[b], inp.q_rope[b], inp.w_uk,
-                                 inp.w_uv, inp.scale)
-        done += 1
-        positions += hi - lo
-        done_bytes += (hi - lo) * item
-        if time.perf_counter() - t0 >= budget_s:
+        times += _oracle_requests(inp, [b])
+        done.append(b)
+        if not full and time.perf_counter() - t0 >= budget_s:
             break
-    dt = time.perf_counter() - t0
+    lens = np.array([int(inp.seq_lens[b]) for b in done], dtype=np.float64)
+    t = np.array(times)
     return {
-        "value": round(done_bytes / dt / 1e9, 6),
+        "value": round(float(lens.sum()) * item / t.sum() / 1e9, 6),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": _blas_threads(),
         "kind": "oracle",
-        "sample": f"requests 0..{done - 1} of {inp.B} ({positions} positions, all {inp.H} heads) in "
-                  f"{dt:.1f} s; float64 numpy, unabsorbed (expands keys and values per head)",
-        "seconds_per_request": round(dt / done, 3),
+        "sample": (f"all {inp.B} requests" if len(done) == inp.B else f"requests 0..{done[-1]} of {inp.B}")
+                  + f" ({int(lens.sum())} positions, all {inp.H} heads) in {t.sum():.1f} s; float64 numpy, "
+                    "unabsorbed (expands keys and values per head)",
+        "median_GBps_per_request": round(float(np.median(lens * item / t)) / 1e9, 6),
+        "seconds_per_request_median": round(float(np.median(t)), 3),
         "host_cpus": len(os.sched_getaffinity(0)),
     }
 
 
-def read_ceiling(torch, gib=2, reps=10):
-    """A plain streaming read for reference: torch's sum over a 2 GiB float64
-    buffer resident in HBM (bytes read / time, HIP events); of the reductions
-    tried it reads fastest."""
+def cpu_baselines_other(I):
+    """The oracle on the other configurations, on the host cores: the tiny
+    float32 one and the single 4,096-token request in full, one layer of the
+    131,072-token workload (times 60 for a token), and the sparse FP8
+    workload's 32 requests x 2,048 picked positions (the oracle reads only the
+    picked rows, so the context is drawn at 4,096 positions to keep the host
+    draw short; the work timed is that of the full workload)."""
+    res = {}
+    cores = _blas_threads()
+
+    def one(name, inp, item, scale_to=1, note=""):
+        t = _oracle_requests(inp, list(range(inp.B)))
+        n = int(np.sum(inp.topk_idx >= 0)) if inp.topk_idx is not None else int(np.sum(inp.seq_lens))
+        total = float(np.sum(t)) * scale_to
+        res[name] = {"seconds": round(total, 4), "GBps": round(n * item * scale_to / total / 1e9, 6),
+                     "cores": cores, "kind": "oracle", "sample": note}
+
+    one("tiny_fp32", I.make_inputs("tiny_fp32"), (16 + 8) * 4, note="the whole step (1 request x 64 positions)")
+    one("v2_single", I.make_inputs("v2_single"), 1152, note="the whole step (1 request x 4,096 positions)")
+    one("v2_long_token", I.make_inputs("v2_long", layer=0), 1152, scale_to=60,
+        note="layer 0 (131,072 positions, all heads) timed, times 60 layers per token")
+    one("v2_fp8_topk", I.make_inputs("v2_fp8_topk", ctx=(4096, 4096)), 644,
+        note="32 requests x 2,048 picked positions (all heads); contexts drawn at 4,096")
+    return res
+
+
+class ClockProbe:
+    """Mean shader clock over a region of the stream: each probe launch records
+    s_memtime (shader clock counter) and s_memrealtime (100 MHz) per XCD;
+    the clock over the region is delta(memtime) / delta(realtime) between two
+    probes, per XCD.  Also drives the hand-written streaming read."""
+
+    GROUPS = 256
+
+    def __init__(self, torch):
+        import ctypes
+        path = os.path.join(ROOT, "mla_latent_kv_absorb_amd", "libmla_bench.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: run the build first")
+        self.lib = ctypes.CDLL(path)
+        self.lib.mlab_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+        self.lib.mlab_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+        self.torch = torch
+        self.bufs = []
+
+    def mark(self):
+        t = self.torch.zeros(self.GROUPS * 4, dtype=self.torch.int64, device="cuda")
+        st = self.lib.mlab_clock_probe(t.data_ptr(), self.GROUPS, self.torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"clock probe failed ({st})")
+        self.bufs.append(t)
+        return len(self.bufs) - 1
+
+    def mhz(self, i0, i1):
+        """Mean clock between two marks, from the work-groups of the two probes
+        that ran on the same compute unit (same XCD, shader engine, array and
+        CU id): the median over those units, with the per-XCD medians."""
+        a = self.bufs[i0].cpu().numpy().reshape(-1, 4)
+        b = self.bufs[i1].cpu().numpy().reshape(-1, 4)
+        unit = lambda r: (int(r[2]), int(r[3]) & 0xFF00)   # xcc, (se, sh, cu) bits of HW_ID
+        first = {}
+        for r in a:
+            first.setdefault(unit(r), r)
+        per_unit = []
+        for r in b:
+            u = unit(r)
+            if u in first:
+                dm, dr = float(r[0] - first[u][0]), float(r[1] - first[u][1])
+                if dr > 0 and dm > 0:
+                    per_unit.append((u[0], dm / dr * 100.0))
+        if not per_unit:
+            return {"mean_MHz": None, "units": 0}
+        vals = np.array([v for _, v in per_unit])
+        per_xcd = {}
+        for x in sorted({x for x, _ in per_unit}):
+            per_xcd[str(x)] = round(float(np.median([v for xx, v in per_unit if xx == x])), 1)
+        return {"mean_MHz": round(float(np.median(vals)), 1), "units": len(per_unit), "per_xcd_MHz": per_xcd,
+                "realtime_ticks": int(np.median(b[:, 1]) - np.median(a[:, 1]))}
+
+    def stream_read(self, buf, groups):
+        sink = self.torch.zeros(groups, dtype=self.torch.int32, device="cuda")
+        st = self.lib.mlab_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), groups, sink.data_ptr(),
+                                       self.torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"stream read failed ({st})")
+
+
+def _median_ms(torch, fn, reps):
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    return float(np.median(ms))
+
+
+def read_ceiling(torch, probe, gib=4, reps=10):
+    """A plain streaming read for reference, written here: every byte of a
+    4 GiB buffer resident in HBM loaded once with 16-byte loads (median over
+    reps, HIP events).  torch's float64 sum over the same buffer is given
+    beside it."""
     x = torch.ones((gib << 30) // 8, dtype=torch.float64, device="cuda")
+    nbytes = gib << 30
+    out = {}
+    for groups in (1024, 2048, 4096):
+        probe.stream_read(x, groups)
+        torch.cuda.synchronize()
+        out[groups] = nbytes / (_median_ms(torch, lambda: probe.stream_read(x, groups), reps) * 1e-3) / 1e9
+    best = max(out, key=out.get)
     x.sum()
+    torch.cuda.synchronize()
+    torch_gbps = nbytes / (_median_ms(torch, lambda: x.sum(), reps) * 1e-3) / 1e9
+    del x
+    return {"GBps": round(out[best], 1), "kind": f"hand-written streaming read, 4 GiB, {best} work-groups",
+            "by_groups_GBps": {str(k): round(v, 1) for k, v in out.items()},
+            "torch_sum_GBps": round(torch_gbps, 1)}
+
+
+def tiny_leg(torch, I, runner, reps=200):
+    """The tiny float32 configuration (4 heads, latent 16, 64 positions): the
+    four calls, direct mode; launch-latency bound."""
+    inp = I.make_inputs("tiny_fp32")
+    w = runner.DeviceWorkload(inp, split=False)
+    w.step()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
-        x.sum()
+        w.step()
     b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
-    del x
-    return {"GBps": round((gib << 30) / (ms * 1e-3) / 1e9, 1), "kind": "torch.sum over 2 GiB float64"}
+    us = a.elapsed_time(b) * 1e3 / reps
+    return {"step_us": round(us, 2), "cache_bytes_per_step": int(I.cache_bytes_read(inp)),
+            "note": "absorb, attention (direct mode), merge, up-projection; launch-latency bound"}
 
 
-def long_context_layer(torch, I, runner, num_cus, layers=4, reps=8):
-    """One decode step of the long-context workload (1 request, 131,072
-    positions) per layer: four independent layer draws are cycled so that
-    every launch reads its cache from HBM rather than from the last-level
-    cache.  Reports the average step time per layer and the per-token rate
-    over the workload's 60 layers."""
+def single_leg(torch, I, runner, num_cus, copies=64, reps=4):
+    """The single 4,096-token request: its 4.7 MB of cache would sit in the
+    last-level cache, so the step cycles over `copies` copies of the pool at
+    different addresses (302 MB in all) and every launch reads HBM."""
+    inp = I.make_inputs("v2_single")
+    w = runner.DeviceWorkload(inp, split=True, num_cus=num_cus)
+    n = w.pool.shape[0]
+    big = w.pool.repeat(copies, 1)
+    tables = [(w.table + i * n).contiguous() for i in range(copies)]
+    w.pool = big
+    for t in tables:
+        w.table = t
+        w.step_fused()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        for t in tables:
+            w.table = t
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+            w.absorb()
+            e[1].record()
+            w.attend()
+            e[2].record()
+            w.combine_up()
+            e[3].record()
+            ev.append(e)
+    torch.cuda.synchronize()
+    cache_bytes = I.cache_bytes_read(inp)
+    step_us = float(np.median([e[0].elapsed_time(e[3]) for e in ev])) * 1e3
+    attn_us = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    return {"step_us_median": round(step_us, 2), "attn_us_median": round(attn_us, 2),
+            "cache_GBps": round(cache_bytes / (step_us * 1e-6) / 1e9, 1),
+            "attn_GBps": round(cache_bytes / (attn_us * 1e-6) / 1e9, 1),
+            "tokens_per_s": round(1e6 / step_us, 1), "cache_bytes_per_step": int(cache_bytes),
+            "workers": w.plan.num_workers, "copies": copies}
+
+
+def long_context_token(torch, I, runner, DI, num_cus, layers=60, tokens=10):
+    """One generated token of the long-context workload: 60 independent layers
+    (1 request x 131,072 positions each, 9.06 GB of cache in all), each layer
+    absorb -> attention -> merge + up-projection.  The layers are drawn on the
+    device (seed 4000 + layer).  The 180 launches of a token are captured in
+    one HIP graph and the graph is replayed; one eager token with events
+    between launches gives the per-layer attention time."""
     ws = []
     for layer in range(layers):
-        inp = I.make_inputs("v2_long", layer=layer)
-        ws.append(runner.DeviceWorkload(inp, split=True, num_cus=num_cus))
-    cache_bytes = I.cache_bytes_read(inp)
+        t = DI.draw_bf16_layer(torch, 4000 + layer, [131072])
+        ws.append(runner.DeviceWorkload(t["shell"], split=True, num_cus=num_cus, tensors=t))
+    cache_bytes = I.cache_bytes_read(ws[0].inp) * layers
     for w in ws:
         w.step_fused()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        for w in ws:
-            w.step_fused()
-    b.record()
+    ev = []
+    for w in ws:
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        w.absorb()
+        e[1].record()
+        w.attend()
+        e[2].record()
+        w.combine_up()
+        ev.append(e)
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / (reps * layers)
-    return {"us_per_layer": round(us, 2), "cache_GBps": round(cache_bytes / (us * 1e-6) / 1e9, 1),
-            "tokens_per_s_60_layers": round(1e6 / (60 * us), 1), "workers": ws[0].plan.num_workers}
+    attn_us = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for w in ws:
+                w.step_fused()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    tok_ms = _median_ms(torch, g.replay, tokens)
+    eager_ms = _median_ms(torch, lambda: [w.step_fused() for w in ws], 3)
+    del g, ws
+    return {"ms_per_token_median": round(tok_ms, 3), "tokens_per_s": round(1e3 / tok_ms, 1),
+            "cache_GBps": round(cache_bytes / (tok_ms * 1e-3) / 1e9, 1),
+            "cache_bytes_per_token": int(cache_bytes), "layers": layers,
+            "attn_us_per_layer_median": round(attn_us, 2),
+            "attn_GBps": round(cache_bytes / layers / (attn_us * 1e-6) / 1e9, 1),
+            "eager_ms_per_token": round(eager_ms, 3), "tokens_timed": tokens,
+            "timing": "HIP graph of the 60 layers' 180 launches, replayed; layers drawn on the device"}
 
 
-def fp8_topk_step(torch, I, runner, num_cus, inp, lists=8, reps=10):
-    """The FP8-cache workload with a top-2,048 index list per request.  One
-    step reads 42 MB out of a 1.35 GB pool, which would otherwise stay in the
-    last-level cache, so the steps cycle over `lists` independently drawn
-    index-list sets (338 MB of distinct rows).  Reports the step and attention
-    times, the cache rate and both roofline fractions (HBM, and BF16 matrix
-    cores: the FP8 latent is dequantised to BF16 for the MFMAs)."""
-    w = runner.DeviceWorkload(inp, split=True, num_cus=num_cus)
-    rng = np.random.default_rng(5005)
-    sets = []
-    for _ in range(lists):
-        idx = np.stack([np.sort(rng.choice(int(inp.seq_lens[b]), inp.topk_idx.shape[1], replace=False))
-                        for b in range(inp.B)]).astype(np.int32)
-        sets.append(torch.from_numpy(idx).to(w.topk_idx.device))
+def fp8_topk_step(torch, I, runner, DI, num_cus, group128, lists=16, reps=6):
+    """The FP8-cache workload with a top-2,048 index list per request (32
+    requests x 65,536 positions, drawn on the device; one scale per position,
+    or one per 128 latent channels).  One step reads 42 MB out of a 1.35 GB
+    pool, which would otherwise stay in the last-level cache, so the steps
+    cycle over `lists` independently drawn index-list sets (675 MB of distinct
+    rows).  Reports the step and attention times (medians), the cache rate and
+    both roofline fractions (HBM, and BF16 matrix cores: the FP8 latent is
+    widened to BF16 for the MFMAs).  Returns (result, workload)."""
+    t = DI.draw_fp8_topk(torch, 5, group128=group128)
+    w = runner.DeviceWorkload(t["shell"], split=True, num_cus=num_cus, tensors=t)
+    inp = w.inp
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5005)
+    sets = [DI.draw_topk_lists(torch, g, inp.seq_lens, w.topk) for _ in range(lists)]
     cache_bytes = I.cache_bytes_read(inp)
-    n_pos = int(np.sum(inp.topk_idx >= 0))
+    n_pos = inp.B * w.topk
     flop = float(n_pos) * 2 * inp.H * (inp.D_C + inp.D_R + inp.D_C)
-    for t in sets:
-        w.topk_idx = t
+    for s_ in sets:
+        w.topk_idx = s_
         w.step_fused()
     torch.cuda.synchronize()
     step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    att = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * lists)]
+    att = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps * lists)]
     step_ev[0].record()
     for r in range(reps):
-        for i, t in enumerate(sets):
-            w.topk_idx = t
+        for i, s_ in enumerate(sets):
+            e = att[r * lists + i]
+            w.topk_idx = s_
+            e[0].record()
             w.absorb()
-            att[r * lists + i][0].record()
+            e[1].record()
             w.attend()
-            att[r * lists + i][1].record()
+            e[2].record()
             w.combine_up()
+            e[3].record()
     step_ev[1].record()
     torch.cuda.synchronize()
     step_us = step_ev[0].elapsed_time(step_ev[1]) * 1e3 / (reps * lists)
-    attn_us = float(np.mean([a.elapsed_time(b) for a, b in att])) * 1e3
-    return {"step_us": round(step_us, 2), "attn_us": round(attn_us, 2),
-            "cache_bytes_per_step": int(cache_bytes),
-            "attn_cache_GBps": round(cache_bytes / (attn_us * 1e-6) / 1e9, 1),
-            "attn_hbm_frac": round(cache_bytes / (attn_us * 1e-6) / (HBM_PEAK_GBPS * 1e9), 4),
-            "attn_mfma_util": round(flop / (attn_us * 1e-6) / BF16_PEAK_FLOPS, 4),
-            "tokens_per_s": round(inp.B / (step_us * 1e-6), 1), "workers": w.plan.num_workers}
+    attn_us = float(np.median([e[1].elapsed_time(e[2]) for e in att])) * 1e3
+    tail_us = float(np.median([e[2].elapsed_time(e[3]) for e in att])) * 1e3
+    absorb_us = float(np.median([e[0].elapsed_time(e[1]) for e in att])) * 1e3
+    res = {"step_us": round(step_us, 2), "attn_us_median": round(attn_us, 2),
+           "absorb_us_median": round(absorb_us, 2), "combine_out_up_us_median": round(tail_us, 2),
+           "cache_bytes_per_step": int(cache_bytes),
+           "attn_cache_GBps": round(cache_bytes / (attn_us * 1e-6) / 1e9, 1),
+           "attn_hbm_frac": round(cache_bytes / (attn_us * 1e-6) / (HBM_PEAK_GBPS * 1e9), 4),
+           "attn_mfma_util": round(flop / (attn_us * 1e-6) / BF16_PEAK_FLOPS, 4),
+           "tokens_per_s": round(inp.B / (step_us * 1e-6), 1), "workers": w.plan.num_workers,
+           "data": "drawn on the device (seed 5), index sets cycled"}
+    return res, w
 
 
 def prefill_leg(torch, I, runner, T=4096, reps=10):
@@ -346,18 +565,21 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps, so the GPU clock has settled "
+                         "at its loaded level when timing starts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle on all 64 requests of the batched workload (about 1.5 minutes)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
-    ap.add_argument("--long", action="store_true",
-                    help="also time one layer of the long-context workload (1 request, 131,072 positions)")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time only the batched workload (no other configurations, no reference read)")
     ap.add_argument("--prefill", action="store_true",
                     help="also time prefill of a 4,096-token prompt on the expanded path")
     ap.add_argument("--indexer", action="store_true",
-                    help="also time the lightning indexer and top-k pick (32 x 65,536 positions), and with "
-                         "--fp8-topk the whole sparse decode step")
-    ap.add_argument("--fp8-topk", action="store_true",
-                    help="also time the FP8-cache, top-2,048 workload (32 requests x 65,536 positions)")
+                    help="also time the lightning indexer and top-k pick (32 x 65,536 positions) and the whole "
+                         "sparse decode step fed by its picks")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
@@ -368,6 +590,7 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
         sys.exit(1)
+    from mla_latent_kv_absorb_amd import device_inputs as DI
     from mla_latent_kv_absorb_amd import inputs as I
     from mla_latent_kv_absorb_amd import runner
 
@@ -376,6 +599,7 @@ def main():
     log(f"inputs drawn in {time.time() - t0:.1f} s; contexts {inp.seq_lens.min()}..{inp.seq_lens.max()}")
     num_cus = torch.cuda.get_device_properties(0).multi_processor_count
     w = runner.DeviceWorkload(inp, split=True, num_cus=num_cus)
+    probe = ClockProbe(torch)
     torch.cuda.synchronize()
     log(f"resident on GPU after {time.time() - t0:.1f} s; workers {w.plan.num_workers}, "
         f"workspace {w.plan.workspace_bytes / 1e6:.1f} MB")
@@ -388,19 +612,40 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # settle: untimed steps until the clock has reached its loaded level
+    settle_steps = 0
+    ts = time.perf_counter()
+    while time.perf_counter() - ts < args.settle_s:
+        for _ in range(20):
+            w.step_fused()
+        settle_steps += 20
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         w.step_fused()
     torch.cuda.synchronize()
-    log("warmup done")
+    log(f"settle {settle_steps} steps, warmup {args.warmup} done")
 
     stream = torch.cuda.current_stream()
-    # events between the three launches of every timed step, on the launch
-    # stream: absorb, attention, merge + up-projection (one launch)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # the timed region: K whole steps, HIP events only at its two ends (an
+    # event recorded between two launches adds a cache flush and a gap)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    c0 = probe.mark()
     wall0 = time.perf_counter()
     start.record(stream)
+    for _ in range(args.steps):
+        w.step_fused()
+    stop.record(stream)
+    c1 = probe.mark()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    clock = probe.mhz(c0, c1)
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    # the same K steps again with events between the three launches of every
+    # step, on the launch stream: absorb, attention, merge + up-projection
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    c2 = probe.mark()
     for k in range(args.steps):
         ev[k][0].record(stream)
         w.absorb()
@@ -409,15 +654,14 @@ def main():
         ev[k][2].record(stream)
         w.combine_up()
         ev[k][3].record(stream)
-    stop.record(stream)
+    c3 = probe.mark()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(stop)
-    part_ms = lambda i: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
-    absorb_ms, attn_avg_ms, tail_ms = part_ms(0), part_ms(1), part_ms(2)
-    ms_per_step = total_ms / args.steps
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s), "
-        f"attention {attn_avg_ms * 1e3:.1f} us")
+    clock_parts = probe.mhz(c2, c3)
+    part = lambda i: np.array([e[i].elapsed_time(e[i + 1]) for e in ev])
+    absorb_ms, attn_ms, tail_ms = part(0), part(1), part(2)
+    attn_avg_ms = float(attn_ms.mean())
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s), clock {clock['mean_MHz']} MHz; "
+        f"with events between launches: attention {attn_avg_ms * 1e3:.1f} us")
 
     gbps = cache_bytes / (ms_per_step * 1e-3) / 1e9
     attn_gbps = cache_bytes / (attn_avg_ms * 1e-3) / 1e9
@@ -428,39 +672,21 @@ def main():
     attn_flop = float(np.sum(inp.seq_lens.astype(np.int64))) * 2 * inp.H * (inp.D_C + inp.D_R + inp.D_C)
     gemm_flop = 2.0 * inp.B * inp.H * inp.D_C * inp.D_N
     w_bytes = inp.H * inp.D_C * inp.D_N * 2
-    gemm = lambda ms, act_bytes: {"us": round(ms * 1e3, 2), "weight_GBps": round(w_bytes / (ms * 1e-3) / 1e9, 1),
-                                  "bytes_GBps": round((w_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1),
-                                  "mfma_util": round(gemm_flop / (ms * 1e-3) / BF16_PEAK_FLOPS, 5)}
+
+    def gemm(ms, act_bytes):
+        m, med = float(ms.mean()), float(np.median(ms))
+        return {"us": round(m * 1e3, 2), "us_median": round(med * 1e3, 2),
+                "weight_GBps": round(w_bytes / (m * 1e-3) / 1e9, 1),
+                "bytes_GBps": round((w_bytes + act_bytes) / (m * 1e-3) / 1e9, 1),
+                "mfma_util": round(gemm_flop / (m * 1e-3) / BF16_PEAK_FLOPS, 5)}
+
     part_bytes = w.plan.num_slots * inp.H * (inp.D_C * 2 + 4)  # BF16 partials + lse
     parts = {
         "absorb": gemm(absorb_ms, inp.B * inp.H * (inp.D_N + inp.D_C) * 2),
-        "attention": {"us": round(attn_avg_ms * 1e3, 2), "mfma_util": round(attn_flop / (attn_avg_ms * 1e-3) / BF16_PEAK_FLOPS, 4)},
+        "attention": {"us": round(attn_avg_ms * 1e3, 2), "us_median": round(float(np.median(attn_ms)) * 1e3, 2),
+                      "mfma_util": round(attn_flop / (attn_avg_ms * 1e-3) / BF16_PEAK_FLOPS, 4)},
         "combine_out_up": gemm(tail_ms, part_bytes + inp.B * inp.H * inp.D_V * 2),
     }
-    parts["cache_append"] = cache_append_part(torch, I, w)
-    ceiling = read_ceiling(torch)
-    long_layer = long_context_layer(torch, I, runner, num_cus) if args.long else None
-    fp8 = fp8g = None
-    if args.fp8_topk:
-        # one draw, both FP8 formats: one scale per token, and one per 128
-        # latent channels (the 656-byte item)
-        fp8_inp = I.make_inputs("v2_fp8_topk")
-        fp8 = fp8_topk_step(torch, I, runner, num_cus, fp8_inp)
-        g_inp = I.requantize(fp8_inp, I.DTYPE_FP8_G128)
-        del fp8_inp
-        fp8g = fp8_topk_step(torch, I, runner, num_cus, g_inp)
-    pre = prefill_leg(torch, I, runner) if args.prefill else None
-    idx = None
-    if args.indexer:
-        attn = runner.DeviceWorkload(g_inp, split=True, num_cus=num_cus) if args.fp8_topk else None
-        idx = indexer_step(torch, I, runner, attn=attn)
-        del attn
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on whole requests (about 15 s)")
-        cpu = cpu_baseline(inp)
-
     result = {
         "metric": "MLA decode latent-KV read GB/s (% HBM peak) + tokens/s, B=64 ctx=32K",
         "value": round(gbps, 2),
@@ -496,19 +722,47 @@ def main():
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic_from_profile(),
         },
-        "cpu_baseline": cpu,
+        "cpu_baseline": None,
         "parts": parts,
-        "read_ceiling": ceiling,
+        "parts_timing": "a second pass of the same K steps with HIP events between the launches (events add a "
+                        "gap and a cache flush, so these times are upper bounds)",
+        "clock_timed_region": clock,
+        "clock_parts_pass": clock_parts,
+        "settle": {"seconds": args.settle_s, "steps": settle_steps},
     }
-    if long_layer is not None:
-        result["v2_long_layer"] = long_layer
-    if fp8 is not None:
-        result["fp8_topk_step"] = fp8
-        result["fp8_g128_topk_step"] = fp8g
-    if idx is not None:
-        result["indexer_step"] = idx
-    if pre is not None:
-        result["prefill_4096"] = pre
+    if not args.main_only:
+        parts["cache_append"] = cache_append_part(torch, I, w)
+        del w
+        torch.cuda.empty_cache()
+        result["read_ceiling"] = read_ceiling(torch, probe)
+        log(f"read ceiling {result['read_ceiling']['GBps']} GB/s")
+        configs = {"tiny_fp32": tiny_leg(torch, I, runner)}
+        configs["v2_single"] = single_leg(torch, I, runner, num_cus)
+        log(f"v2_single {configs['v2_single']['step_us_median']} us/step")
+        configs["v2_long_token"] = long_context_token(torch, I, runner, DI, num_cus)
+        log(f"v2_long {configs['v2_long_token']['ms_per_token_median']} ms/token")
+        torch.cuda.empty_cache()
+        fp8, _ = fp8_topk_step(torch, I, runner, DI, num_cus, group128=False)
+        configs["v2_fp8_topk"] = fp8
+        torch.cuda.empty_cache()
+        fp8g, wg = fp8_topk_step(torch, I, runner, DI, num_cus, group128=True)
+        configs["v2_fp8g_topk"] = fp8g
+        log(f"fp8 top-k step {fp8['step_us']} / {fp8g['step_us']} us")
+        if args.indexer:
+            result["indexer_step"] = indexer_step(torch, I, runner, attn=wg)
+        del wg
+        torch.cuda.empty_cache()
+        if args.prefill:
+            result["prefill_4096"] = prefill_leg(torch, I, runner)
+        result["configs"] = configs
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on whole requests")
+        result["cpu_baseline"] = cpu_baseline(inp, full=args.cpu_full)
+        if not args.main_only:
+            other = cpu_baselines_other(I)
+            for k, v in other.items():
+                result["configs"].setdefault(k, {})["cpu_baseline"] = v
     print(json.dumps(result), flush=True)
 
 

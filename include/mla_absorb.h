@@ -55,7 +55,9 @@ typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = 1, /* null or misaligned pointer, bad size, too small workspace */
   MLA_ERR_UNSUPPORTED = 2, /* a dims / dtype combination the library has no kernel for */
-  MLA_ERR_LAUNCH = 3       /* the HIP runtime refused a launch */
+  MLA_ERR_LAUNCH = 3,      /* the HIP runtime refused a launch */
+  MLA_ERR_SCRATCH = 4      /* the call needs more than the library's static
+                              scratch holds */
 } mla_status;
 
 typedef enum {

@@ -19,7 +19,7 @@ import numpy as np
 LIB_PATH = os.environ.get("MLA_ABSORB_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "libmla_absorb.so")
 
-MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_LAUNCH = 0, 1, 2, 3
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_LAUNCH, MLA_ERR_SCRATCH = 0, 1, 2, 3, 4
 MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_FP8_E4M3_G128 = 0, 1, 2, 3
 PAGE_TOKENS = 64
 TILE_TOKENS = 32

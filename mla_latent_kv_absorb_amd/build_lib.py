@@ -17,8 +17,13 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_absorb.so")
+# measurement helpers used by the benchmark only (a streaming read and a
+# clock probe); not part of the decode library
+BENCH_LIB = os.path.join(HERE, "libmla_bench.so")
+BENCH_SOURCES = [("bench_kernels.hip", True)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+GXX = os.environ.get("CXX", "g++")
 ARCH = "gfx950"
 COMMON = [
     "-O3", "-std=c++17", "-fPIC",
@@ -38,15 +43,21 @@ SOURCES = [
     ("prefill.hip", True),
     ("mla_api.cpp", False),
     ("indexer_api.cpp", False),
+    ("host_checks.cpp", None),
 ]
 
 
-def _compile(src: str, device: bool) -> str:
+def _compile(src: str, device) -> str:
+    """device True: HIP source for gfx950; False: host C++ that includes the
+    HIP runtime headers; None: plain C++ without HIP (built with g++)."""
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON]
+    if device is None:
+        cmd = [GXX, "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror"]
+    else:
+        cmd = [HIPCC, *COMMON]
     if device:
         cmd += [*DEVICE, "-x", "hip"]
-    else:
+    elif device is False:
         cmd += ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,19 +66,26 @@ def _compile(src: str, device: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
-    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(*s), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link failed for {os.path.basename(lib)}:\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + BENCH_SOURCES
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(*s), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], BENCH_LIB)
     if verbose:
         print(f"built {LIB}")
+        print(f"built {BENCH_LIB}")
     return LIB
 
 

@@ -12,23 +12,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-struct F32Layout {
-  int q, qr, c, r, s, o, m, l, al, valid, total;  // offsets in floats
-  __host__ __device__ F32Layout(int H, int DC, int DR) {
-    q = 0;
-    qr = q + H * DC;
-    c = qr + H * DR;
-    r = c + kTile * DC;
-    s = r + kTile * DR;
-    o = s + H * kTile;
-    m = o + H * DC;
-    l = m + H;
-    al = l + H;
-    valid = al + H;
-    total = valid + kTile;
-  }
-};
-
 template <bool TOPK, bool DIRECT>
 __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
   extern __shared__ float sm[];
@@ -208,10 +191,6 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
 }
 
 }  // namespace
-
-size_t decode_f32_lds_bytes(int H, int D_C, int D_R) {
-  return (size_t)F32Layout(H, D_C, D_R).total * sizeof(float);
-}
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) {
   const bool topk = a.topk_idx != nullptr;

@@ -38,27 +38,36 @@ def workspace_bytes(H: int, D_C: int, slots: int) -> int:
 
 class DeviceWorkload:
     def __init__(self, inp: I.DecodeInputs, device="cuda", split=True, num_workers=None, num_cus=256,
-                 pool=None, table=None):
+                 pool=None, table=None, tensors=None):
+        """Upload ``inp`` (host arrays) to the device, or, with ``tensors``,
+        take device tensors already drawn there (pool, table, q_nope,
+        q_rope, w_uk, w_uv, topk_idx; ``inp`` then only gives dims and
+        lengths)."""
         import torch
         self.inp = inp
         self.device = device
         self.cfg = B.make_config(inp.H, inp.D_C, inp.D_R, inp.D_N, inp.D_V, inp.scale,
                                  _dtype_code(inp.cache_dtype), _dtype_code(inp.act_dtype))
-        if pool is None:
-            pool, table = I.build_paged_pool(inp)
-        self.pool = torch.from_numpy(pool).to(device)
-        self.table = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(device)
         self.seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(device)
-        self.topk = 0
-        self.topk_idx = None
-        if inp.topk_idx is not None:
-            self.topk_idx = torch.from_numpy(inp.topk_idx.astype(np.int32)).to(device)
-            self.topk = int(inp.topk_idx.shape[1])
         act = inp.act_dtype
-        self.q_nope = to_device_act(inp.q_nope, act, device)
-        self.q_rope = to_device_act(inp.q_rope, act, device)
-        self.w_uk = to_device_act(inp.w_uk, act, device)
-        self.w_uv = to_device_act(inp.w_uv, act, device)
+        if tensors is not None:
+            self.pool, self.table = tensors["pool"], tensors["table"]
+            self.q_nope, self.q_rope = tensors["q_nope"], tensors["q_rope"]
+            self.w_uk, self.w_uv = tensors["w_uk"], tensors["w_uv"]
+            self.topk_idx = tensors.get("topk_idx")
+        else:
+            if pool is None:
+                pool, table = I.build_paged_pool(inp)
+            self.pool = torch.from_numpy(pool).to(device)
+            self.table = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(device)
+            self.topk_idx = None
+            if inp.topk_idx is not None:
+                self.topk_idx = torch.from_numpy(inp.topk_idx.astype(np.int32)).to(device)
+            self.q_nope = to_device_act(inp.q_nope, act, device)
+            self.q_rope = to_device_act(inp.q_rope, act, device)
+            self.w_uk = to_device_act(inp.w_uk, act, device)
+            self.w_uv = to_device_act(inp.w_uv, act, device)
+        self.topk = 0 if self.topk_idx is None else int(self.topk_idx.shape[1])
         dt = torch.float32 if act == I.DTYPE_F32 else torch.bfloat16
         Bn, H = inp.B, inp.H
         self.q_lat = torch.empty((Bn, H, inp.D_C), dtype=dt, device=device)

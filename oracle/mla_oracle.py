@@ -42,7 +42,6 @@ __all__ = [
     "dequant_fp8_latent",
     "visible_positions",
     "decode_unabsorbed",
-    "decode_unabsorbed_batch",
     "prefill_unabsorbed",
     "absorb_query",
     "latent_decode",
@@ -179,15 +178,6 @@ def prefill_unabsorbed(c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, scale, q_start,
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
-
-
-def decode_unabsorbed_batch(inputs_per_request, scale, heads=None):
-    """Apply ``decode_unabsorbed`` to a list of per-request argument tuples
-    (c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, picked)."""
-    res = []
-    for (c, kr, qn, qr, wuk, wuv, picked) in inputs_per_request:
-        res.append(decode_unabsorbed(c, kr, qn, qr, wuk, wuv, scale, picked=picked, heads=heads))
-    return res
 
 
 # ---------------------------------------------------------------------------

@@ -210,3 +210,4 @@ def test_append_and_prefill_validation(B):
     assert lib.mla_prefill_attn(c, p, p, p, p, p, 100, 0, 0, p, null, null) == B.MLA_ERR_INVALID_ARG
     tiny = B.make_config(4, 16, 8, 8, 8, 0.25, B.MLA_F32, B.MLA_F32)
     assert lib.mla_prefill_attn(ctypes.byref(tiny), p, p, p, p, p, 100, 0, 10, p, null, null) == B.MLA_ERR_UNSUPPORTED
+

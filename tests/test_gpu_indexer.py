@@ -181,13 +181,14 @@ def _two_calls_then_fused(torch, w):
     return s2, i2, w.scores.cpu().numpy(), w.idx.cpu().numpy()
 
 
-@pytest.mark.parametrize("stride", ["wide", 5000])
+@pytest.mark.parametrize("stride", ["wide", 5000, 5001])
 def test_fused_indexer_topk_equals_two_calls(torch, R, stride):
     """mla_indexer_topk builds the pick's first histogram inside the score
     kernel: same float32 scores, same picks (bit-exact), on ragged rows that
     span several chunks, with some rows at or below k.  With score rows of
     5,000 entries the longer requests are cut to the row width in both
-    paths."""
+    paths; with 5,001 the rows after the first start off a 16-byte boundary,
+    so the pick reads them with scalar loads."""
     _log(f"indexer + pick in one call, ragged, stride {stride}")
     # request 1 has exactly k positions and request 3 fewer: every position
     # is picked and no histogram is built for them
@@ -201,7 +202,7 @@ def test_fused_indexer_topk_equals_two_calls(torch, R, stride):
     assert np.array_equal(i1, i2)
     check_pick_valid(i1[0], oracle_scores(inp, 0), int(inp.seq_lens[0]), inp.topk, "b=0")
     if stride != "wide":
-        # request 2 (9,500 positions) is picked among its first 5,000
+        # request 2 (9,500 positions) is picked among its first 5,000 (5,001)
         check_pick_valid(i1[2], oracle_scores(inp, 2)[:width], width, inp.topk, "b=2 cut to the row")
 
 

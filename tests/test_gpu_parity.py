@@ -1,7 +1,16 @@
 """GPU parity: the HIP path through the C ABI against the float64 oracle.
 
-Tolerances: max |err| <= 2e-2 * max|ref| for BF16 / FP8 caches; max |err| <=
-1e-4 (absolute) for the float32 configuration; index handling bit-exact.
+Tolerances: max |err| <= 2e-2 * max|ref| for BF16 / FP8 caches on out and
+o_lat, and max |err| <= 1e-2 (absolute) on the log-sum-exp; max |err| <= 1e-4
+(absolute) for the float32 configuration; index handling bit-exact.
+
+Why 1e-2 absolute on the log-sum-exp: lse is a softmax-weighted mean of the
+scores plus the log of the mass, so its error is about the score error.  The
+scores differ from the float64 ones by the BF16 rounding of q_lat (one
+rounding of a 512-term float32 sum) and, for FP8 caches, of the dequantised
+latent: about 2^-9 relative per term, a few 1e-3 on unit-variance scores.  A
+relative bound on lse would allow ~0.2 at 16K-131K contexts, a 20% error in
+the merge weights.
 """
 
 import math
@@ -15,6 +24,7 @@ from mla_latent_kv_absorb_amd import inputs as I
 pytestmark = pytest.mark.gpu
 
 REL_TOL = 2e-2
+LSE_ABS_TOL = 1e-2
 F32_TOL = 1e-4
 
 
@@ -61,13 +71,18 @@ def assert_close(got, ref, tol_rel=REL_TOL, abs_tol=None, what=""):
     return err
 
 
-def check_step(torch, R, inp, split=True, num_workers=None, requests=None, heads=None, f32=False):
+def check_step(torch, R, inp, split=True, num_workers=None, requests=None, heads=None, f32=False, checks=None,
+               lse_tol=LSE_ABS_TOL):
+    """Run the whole step on the GPU and compare out, o_lat and lse with the
+    oracle.  ``checks`` is a list of (requests, heads) pairs to compare (heads
+    None = all); by default (requests, heads) as given, every request and head
+    when both are None."""
     w = R.DeviceWorkload(inp, split=split, num_workers=num_workers)
     w.step()
     torch.cuda.synchronize()
     o_lat, out, lse = to_np(w.o_lat), to_np(w.out), to_np(w.lse)
-    reqs = range(inp.B) if requests is None else requests
-    hs = list(range(inp.H)) if heads is None else list(heads)
+    if checks is None:
+        checks = [(range(inp.B) if requests is None else requests, heads)]
     # the merge and up-projection in one launch as well (the benchmarked
     # step), on the same partials, where that call exists (BF16, V2 dims)
     fused = None
@@ -76,19 +91,21 @@ def check_step(torch, R, inp, split=True, num_workers=None, requests=None, heads
         w.combine_up()
         torch.cuda.synchronize()
         fused = to_np(w.out)
-    for b in reqs:
-        r_out, r_lse, r_olat = oracle_request(inp, b, heads=hs)
-        tag = f"b={b}"
-        if fused is not None:
-            assert_close(fused[b][hs], r_out, what="fused out " + tag)
-        if f32:
-            assert_close(out[b][hs], r_out, abs_tol=F32_TOL, what="out " + tag)
-            assert_close(o_lat[b][hs], r_olat, abs_tol=F32_TOL, what="o_lat " + tag)
-            assert_close(lse[b][hs], r_lse, abs_tol=F32_TOL, what="lse " + tag)
-        else:
-            assert_close(out[b][hs], r_out, what="out " + tag)
-            assert_close(o_lat[b][hs], r_olat, what="o_lat " + tag)
-            assert_close(lse[b][hs], r_lse, what="lse " + tag)
+    for reqs, hsel in checks:
+        hs = list(range(inp.H)) if hsel is None else list(hsel)
+        for b in reqs:
+            r_out, r_lse, r_olat = oracle_request(inp, b, heads=hs)
+            tag = f"b={b}"
+            if fused is not None:
+                assert_close(fused[b][hs], r_out, what="fused out " + tag)
+            if f32:
+                assert_close(out[b][hs], r_out, abs_tol=F32_TOL, what="out " + tag)
+                assert_close(o_lat[b][hs], r_olat, abs_tol=F32_TOL, what="o_lat " + tag)
+                assert_close(lse[b][hs], r_lse, abs_tol=F32_TOL, what="lse " + tag)
+            else:
+                assert_close(out[b][hs], r_out, what="out " + tag)
+                assert_close(o_lat[b][hs], r_olat, what="o_lat " + tag)
+                assert_close(lse[b][hs], r_lse, abs_tol=lse_tol, what="lse " + tag)
     return w
 
 
@@ -390,7 +407,9 @@ def test_fp8_group_scales_differ_per_group(torch, R):
     inp = I.make_inputs("v2_fp8g_topk", seed=24, batch=3, ctx=(200, 700), topk=0)
     rng = np.random.default_rng(24)
     inp.c_scales[:] = inp.c_scales * np.exp2(rng.integers(-2, 3, size=inp.c_scales.shape)).astype(np.float32)
-    check_step(torch, R, inp, split=True)
+    # latents up to 4x larger make scores (and their rounding error) up to 4x
+    # larger: the lse bound scales with them
+    check_step(torch, R, inp, split=True, lse_tol=4 * LSE_ABS_TOL)
 
 
 def test_out_of_range_indices_are_skipped(torch, R):
@@ -408,26 +427,163 @@ def test_out_of_range_indices_are_skipped(torch, R):
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads (sampled against the oracle)
+# Index lists longer than one list chunk (2,048 entries) and FP8 dense segments
+# longer than one page-id chunk (4,000 tiles): the kernel refills its LDS row
+# list and carries the online-softmax state across the refill.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cache", [I.DTYPE_BF16, I.DTYPE_FP8, I.DTYPE_FP8_G128])
+def test_topk_list_over_several_chunks(torch, R, cache):
+    """4,100 picked positions (three list chunks: 2,048 + 2,048 + 4) in one
+    request, 3,000 and padding in the other, in direct mode, on one worker
+    and with the planner's split."""
+    name = {I.DTYPE_BF16: "v2_batched", I.DTYPE_FP8: "v2_fp8_topk", I.DTYPE_FP8_G128: "v2_fp8g_topk"}[cache]
+    _log(f"topk 4100 over chunks, {cache}")
+    inp = I.make_inputs(name, seed=41, batch=2, ctx=(9000, 9000), topk=4100)
+    inp.topk_idx[1, 3000:] = -1
+    for mode in ("direct", 1, "auto"):
+        _log(f"  mode {mode}")
+        if mode == "direct":
+            check_step(torch, R, inp, split=False)
+        else:
+            check_step(torch, R, inp, split=True, num_workers=None if mode == "auto" else mode)
+
+
+@pytest.mark.parametrize("name", ["v2_fp8_topk", "v2_fp8g_topk"])
+def test_fp8_dense_over_one_page_chunk(torch, R, name):
+    """One dense FP8 request of 130,000 positions (4,063 tiles: one full chunk
+    of 4,000 tiles and a second one) in direct mode and on one worker."""
+    _log(f"{name} dense 130000 positions")
+    inp = I.make_inputs(name, seed=42, batch=1, ctx=(130000, 130000), topk=0)
+    for mode in ("direct", 1):
+        _log(f"  mode {mode}")
+        if mode == "direct":
+            check_step(torch, R, inp, split=False)
+        else:
+            check_step(torch, R, inp, split=True, num_workers=1)
+
+
+# ---------------------------------------------------------------------------
+# Index handling at the full list length, through the planner's split
+# ---------------------------------------------------------------------------
+LOW, HIGH, REQ, ONE = 0, 64, 128, 136  # latent dims of the count pattern
+
+
+def _count_pattern_case(cache, B=32, T=4096, k=2048, seed=8):
+    """Zero queries (every picked position gets probability 1).  Latent dim
+    p % 64 and dim 64 + p // 64 of position p hold 1 (a one-hot code of the
+    position), dims 128..132 hold the bits of the request index, dim 136 holds
+    1, every other dim 0.  All values are 0 or 1: exact in BF16 and in E4M3
+    (code 0x38) with unit scales."""
+    rng = np.random.default_rng(seed)
+    H, D_C, D_R = 128, 512, 64
+    pos = np.tile(np.arange(T), B)
+    rows = np.arange(B * T)
+    c = np.zeros((B * T, D_C), np.float32)
+    c[rows, LOW + pos % 64] = 1
+    c[rows, HIGH + pos // 64] = 1
+    req = np.repeat(np.arange(B), T)
+    for j in range(5):
+        c[:, REQ + j] = (req >> j) & 1
+    c[:, ONE] = 1
+    codes = scales = None
+    if cache in I.FP8_DTYPES:
+        codes = np.where(c > 0, 0x38, 0).astype(np.uint8)
+        scales = np.ones(B * T, np.float32) if cache == I.DTYPE_FP8 else np.ones((B * T, D_C // 128), np.float32)
+    idx = np.stack([np.sort(rng.choice(T, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    inp = custom_inputs(c, np.zeros((B * T, D_R)), np.zeros((B, H, 128)), np.zeros((B, H, D_R)),
+                        np.zeros((H, D_C, 128)), np.zeros((H, 128, D_C)), [T] * B, cache, I.DTYPE_BF16, 0.1,
+                        topk_idx=idx, codes=codes, scales=scales, perm_seed=seed)
+    return inp, idx
+
+
+# one picked position more or less moves the merged lse by ln(2049/2048) = 4.9e-4
+LSE_COUNT_TOL = 5e-5
+
+
+@pytest.mark.parametrize("cache", [I.DTYPE_BF16, I.DTYPE_FP8, I.DTYPE_FP8_G128])
+def test_topk_2048_counts_exact_through_split(torch, R, cache):
+    """32 requests x 2,048 picks over the planner's worker split (the launch
+    shape of the sparse workload).  Each partial (o_s, lse_s) of a worker
+    covers count_s picked positions of one request: exp(lse_s) = count_s and
+    o_s[d] = n_d / count_s, with n_d the number of its positions whose one-hot
+    code sets dim d.  The n_d are small (a few per dim), so the BF16 rounding
+    of o_s (at most 2^-8 relative) moves n_d = o_s[d] * count_s by far less
+    than 1/2 and both integers are recovered exactly; the request bits say
+    which request the partial belongs to.  Summed over the partials of a
+    request, the counts must equal the histograms of position % 64 and
+    position / 64 of its index list: a missing, repeated or wrong index
+    changes one of these integers.  The merged lse must be ln 2,048 for every
+    request and head."""
+    _log(f"topk 2048 exact counts through the split, {cache}")
+    inp, idx = _count_pattern_case(cache)
+    w = R.DeviceWorkload(inp, split=True)
+    assert w.plan.num_workers > inp.B, "the split must spread requests over several workers"
+    w.workspace.fill_(0xFF)                     # unwritten partials read as NaN
+    w.attend(q_lat=torch.zeros_like(w.q_lat))
+    torch.cuda.synchronize()
+    part_o, part_l = (x.cpu().numpy().astype(np.float64) for x in w.partials())
+    counts = np.zeros(inp.B, np.int64)
+    hist = np.zeros((inp.B, 128), np.int64)
+    used = 0
+    for s_ in range(part_o.shape[0]):
+        l = part_l[s_]
+        if not np.isfinite(l[0]):
+            continue
+        used += 1
+        assert np.all(l == l[0]), f"slot {s_}: heads disagree"
+        assert np.all(part_o[s_] == part_o[s_][0]), f"slot {s_}: heads disagree"
+        o = part_o[s_][0]
+        n = float(np.exp(l[0]))
+        cnt = int(round(n))
+        assert cnt >= 1 and abs(n - cnt) < 1e-3, f"slot {s_}: exp(lse) = {n}"
+        assert o[ONE] == 1.0, f"slot {s_}: weights do not sum to one ({o[ONE]})"
+        reqbits = o[REQ:REQ + 5]
+        assert np.all((reqbits == 0) | (reqbits == 1)), f"slot {s_}: positions of several requests"
+        b = int(np.sum(reqbits.astype(np.int64) << np.arange(5)))
+        nd = o[:128] * cnt
+        assert np.all(np.abs(nd - np.round(nd)) < 0.25), f"slot {s_}: counts not integral"
+        counts[b] += cnt
+        hist[b] += np.round(nd).astype(np.int64)
+    assert used >= inp.B
+    for b in range(inp.B):
+        sel = idx[b]
+        assert counts[b] == sel.size, f"request {b}: {counts[b]} positions weighted, {sel.size} picked"
+        expect = np.concatenate([np.bincount(sel % 64, minlength=64), np.bincount(sel // 64, minlength=64)])
+        assert np.array_equal(hist[b], expect), f"request {b}: position histograms differ"
+    w.combine()
+    torch.cuda.synchronize()
+    lse = w.lse.cpu().numpy().astype(np.float64)
+    err = np.max(np.abs(lse - math.log(2048)))
+    assert err <= LSE_COUNT_TOL, f"merged lse off by {err}"
+    o_lat = w.o_lat.float().cpu().numpy()
+    assert np.all(o_lat[:, :, ONE] == 1.0)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
 def test_v2_single_full(torch, R):
     _log("v2_single full")
     check_step(torch, R, I.make_inputs("v2_single"), split=True)
 
 
-def test_v2_batched_full_size_sampled(torch, R):
+def test_v2_batched_full_size(torch, R):
+    """All 128 heads of eight requests (the first and last two, and four
+    from the middle, each spread over several workers), and four heads, one
+    per wave, of every request."""
     _log("v2_batched full size")
     inp = I.make_inputs("v2_batched")
-    check_step(torch, R, inp, split=True, requests=[0, 31, 63], heads=[0, 77, 127])
+    check_step(torch, R, inp, split=True,
+               checks=[([0, 1, 17, 31, 32, 47, 62, 63], None), (range(inp.B), [0, 40, 77, 127])])
 
 
 @pytest.mark.parametrize("layer", [0, 29, 59])
-def test_v2_long_layer_sampled(torch, R, layer):
+def test_v2_long_layer_full(torch, R, layer):
     """Long context (1 request x 131,072 positions): the first, middle and
-    last of the 60 independently drawn layers, on sampled heads."""
+    last of the 60 independently drawn layers, every head."""
     _log(f"v2_long layer {layer}")
     inp = I.make_inputs("v2_long", layer=layer)
-    check_step(torch, R, inp, split=True, requests=[0], heads=[0, 64, 127])
+    check_step(torch, R, inp, split=True)
 
 
 @pytest.fixture(scope="module")
@@ -435,12 +591,38 @@ def fp8_full():
     return I.make_inputs("v2_fp8_topk")
 
 
-def test_fp8_topk_full_size_sampled(torch, R, fp8_full):
+def test_fp8_topk_full_size(torch, R, fp8_full):
+    """32 requests x 65,536 positions, 2,048 picked each, one scale per
+    position: every request and head."""
     _log("v2_fp8_topk full size")
-    check_step(torch, R, fp8_full, split=True, requests=[0, 31], heads=[0, 127])
+    check_step(torch, R, fp8_full, split=True)
 
 
-def test_fp8_group_scales_topk_full_size_sampled(torch, R, fp8_full):
+def test_fp8_group_scales_topk_full_size(torch, R, fp8_full):
     _log("v2_fp8g_topk full size (same draw, per-128-channel scales)")
     inp = I.requantize(fp8_full, I.DTYPE_FP8_G128)
-    check_step(torch, R, inp, split=True, requests=[0, 17, 31], heads=[0, 64, 127])
+    check_step(torch, R, inp, split=True)
+
+
+@pytest.mark.parametrize("cache", [I.DTYPE_FP8, I.DTYPE_FP8_G128])
+def test_fp8_topk_full_size_count(torch, R, fp8_full, cache):
+    """With zero queries every picked position has probability 1, so the
+    merged lse is ln 2,048 for every request and head, through the planner's
+    split of the full workload, and o_lat is the mean of the picked latents."""
+    _log(f"v2 fp8 top-k full size, zero queries, {cache}")
+    inp = fp8_full if cache == I.DTYPE_FP8 else I.requantize(fp8_full, I.DTYPE_FP8_G128)
+    w = R.DeviceWorkload(inp, split=True)
+    w.q_rope.zero_()
+    w.attend(q_lat=torch.zeros_like(w.q_lat))
+    w.combine()
+    torch.cuda.synchronize()
+    lse = w.lse.cpu().numpy().astype(np.float64)
+    err = np.max(np.abs(lse - math.log(2048)))
+    assert err <= LSE_COUNT_TOL, f"lse off by {err}"
+    o_lat = to_np(w.o_lat)
+    for b in (0, 15, 31):
+        lo, hi = inp.request(b)
+        c = oracle.dequant_fp8_latent(inp.c_codes[lo:hi], inp.c_scales[lo:hi])
+        ref, _ = oracle.latent_decode(np.zeros((inp.H, inp.D_C)), np.zeros((inp.H, inp.D_R)), c, inp.k_rope[lo:hi],
+                                      inp.scale, picked=inp.topk_idx[b])
+        assert_close(o_lat[b], ref, what=f"o_lat b={b}")
