@@ -57,7 +57,7 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 2, /* a dims / dtype combination the library has no kernel for */
   MLA_ERR_LAUNCH = 3,      /* the HIP runtime refused a launch */
   MLA_ERR_SCRATCH = 4      /* the call needs more than the library's static
-                              scratch holds */
+                              scratch holds (mla_decode_noalloc only) */
 } mla_status;
 
 typedef enum {
@@ -249,6 +249,42 @@ mla_status mla_out_up(const mla_config* cfg, const void* o_lat, const void* w_uv
 mla_status mla_combine_out_up(const mla_config* cfg, const void* workspace, size_t workspace_bytes,
                               const int32_t* seq_lens, int32_t topk, int32_t batch, const mla_plan* plan,
                               const void* w_uv, void* out, float* lse_out, void* stream);
+
+/* Bytes of the static device buffer mla_decode_noalloc keeps its split
+ * partials in (one buffer per GPU, held until the process ends). */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the split
+ * decode of mla_decode_attn (with `plan`) followed by its merge, in one call,
+ * with the split partials kept in a static device buffer the library owns
+ * instead of a caller workspace.  Nothing is allocated or freed by this call.
+ *   Arguments as mla_decode_attn (split mode) and mla_combine /
+ *   mla_combine_out_up.  Exactly one output form:
+ *     o_lat != NULL (w_uv and out NULL): the merged weighted latent, as
+ *       mla_combine writes it;
+ *     out != NULL with w_uv: the merged up-projection, as mla_combine_out_up
+ *       writes it (BF16, D_V = 128 only; o_lat is not written).
+ *   lse_out [batch][H] may be NULL.
+ * Capacity: the partials take (num_workers + batch - 1) * (H * D_C * e + H *
+ * 4) bytes, each section rounded up to 16, with e = 2 for BF16 activations and
+ * 4 for F32; calls needing more than MLA_NOALLOC_SCRATCH_BYTES return
+ * MLA_ERR_SCRATCH and enqueue nothing (at V2 dims: 382 slots, e.g. 256
+ * workers and up to 127 requests).
+ * Sharing: every call on a GPU uses that GPU's one buffer.  Calls that may
+ * overlap on one GPU (different streams, or host threads without ordering)
+ * race on it and must not be issued; calls in order on one stream are safe.
+ * The buffer keeps the last call's contents; nothing in it needs clearing,
+ * because the merge reads only partials written by the same call.
+ * The first call on a device looks up that device's buffer address (with the
+ * device current); later calls reuse it.
+ * Errors: as mla_decode_attn and the merge calls, plus both or neither
+ * output given -> MLA_ERR_INVALID_ARG, capacity -> MLA_ERR_SCRATCH. */
+mla_status mla_decode_noalloc(const mla_config* cfg, const void* q_lat, const void* q_rope, const void* kv_pool,
+                              int64_t num_pages, const int32_t* block_table, int32_t block_table_stride,
+                              const int32_t* seq_lens, const int32_t* topk_idx, int32_t topk, int32_t batch,
+                              const mla_plan* plan, void* o_lat, const void* w_uv, void* out, float* lse_out,
+                              void* stream);
 
 /* Host-side check of the device-metadata contract on host copies: lengths
  * >= 1, enough block-table columns, page ids in [0, num_pages) for every page

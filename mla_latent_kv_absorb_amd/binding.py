@@ -20,6 +20,7 @@ LIB_PATH = os.environ.get("MLA_ABSORB_LIB") or os.path.join(os.path.dirname(os.p
                                                            "libmla_absorb.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_LAUNCH, MLA_ERR_SCRATCH = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 48 << 20
 MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_FP8_E4M3_G128 = 0, 1, 2, 3
 PAGE_TOKENS = 64
 TILE_TOKENS = 32
@@ -30,7 +31,7 @@ EXPORTED = (
     "mla_check_decode_inputs_host", "mla_cache_append",
     "mla_prepare_w_uk_t", "mla_prefill_expand", "mla_prefill_attn",
     "mla_indexer_page_layout", "mla_indexer_scores", "mla_topk_workspace_bytes", "mla_topk_select",
-    "mla_indexer_topk",
+    "mla_indexer_topk", "mla_decode_noalloc",
 )
 INDEXER_HEADS, INDEXER_DIM = 64, 128
 
@@ -83,6 +84,7 @@ def _load():
         "mla_topk_workspace_bytes": ([I32, I64], SZ),
         "mla_topk_select": ([P, I64, P, I32, I32, P, P, SZ, P], I32),
         "mla_indexer_topk": ([I32, I32, P, P, P, I64, P, I32, P, I32, P, I64, I32, P, P, SZ, P], I32),
+        "mla_decode_noalloc": ([cfgp, P, P, P, I64, P, I32, P, P, I32, I32, planp, P, P, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -243,6 +245,38 @@ def mla_combine_out_up(cfg: MlaConfig, workspace, seq_lens, plan: MlaPlan, w_uv,
                                  _dev(w_uv, "w_uv", dt, (H, DV, DC)), _dev(out, "out", dt, (B, H, DV)), lp,
                                  _stream(stream))
     _check("mla_combine_out_up", st)
+
+
+def mla_decode_noalloc(cfg: MlaConfig, q_lat, q_rope, kv_pool, block_table, seq_lens, plan: MlaPlan, topk_idx=None,
+                       o_lat=None, w_uv=None, out=None, lse_out=None, stream=None):
+    """Split attention and merge in one call, partials in the library's
+    static scratch: o_lat given -> merged weighted latent; out and w_uv given
+    -> merged up-projection."""
+    torch = _torch()
+    B = q_lat.shape[0]
+    dt = _act(cfg)
+    H, DC, DR, DV = cfg.num_heads, cfg.d_latent, cfg.d_rope, cfg.d_v
+    page_bytes, _, _ = page_layout(cfg)
+    if kv_pool.dtype != torch.uint8 or kv_pool.dim() != 2 or kv_pool.shape[1] != page_bytes:
+        raise ValueError(f"kv_pool must be uint8 [num_pages, {page_bytes}]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [batch, stride]")
+    topk, tp = 0, None
+    if topk_idx is not None:
+        if topk_idx.dim() != 2 or topk_idx.shape[0] != B:
+            raise ValueError("topk_idx must be int32 [batch, k]")
+        topk = int(topk_idx.shape[1])
+        tp = _dev(topk_idx, "topk_idx", torch.int32)
+    ol = _dev(o_lat, "o_lat", dt, (B, H, DC)) if o_lat is not None else None
+    wp = _dev(w_uv, "w_uv", dt, (H, DV, DC)) if w_uv is not None else None
+    op = _dev(out, "out", dt, (B, H, DV)) if out is not None else None
+    lp = _dev(lse_out, "lse_out", torch.float32, (B, H)) if lse_out is not None else None
+    st = _lib.mla_decode_noalloc(
+        ctypes.byref(cfg), _dev(q_lat, "q_lat", dt, (B, H, DC)), _dev(q_rope, "q_rope", dt, (B, H, DR)),
+        _dev(kv_pool, "kv_pool"), int(kv_pool.shape[0]), _dev(block_table, "block_table", torch.int32),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, (B,)), tp, topk, B, ctypes.byref(plan),
+        ol, wp, op, lp, _stream(stream))
+    _check("mla_decode_noalloc", st)
 
 
 def mla_check_decode_inputs_host(cfg: MlaConfig, seq_lens, block_table, num_pages: int, topk_idx=None):

@@ -41,6 +41,7 @@ SOURCES = [
     ("indexer.hip", True),
     ("cache_append.hip", True),
     ("prefill.hip", True),
+    ("noalloc.hip", True),
     ("mla_api.cpp", False),
     ("indexer_api.cpp", False),
     ("host_checks.cpp", None),

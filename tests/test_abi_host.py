@@ -211,3 +211,34 @@ def test_append_and_prefill_validation(B):
     tiny = B.make_config(4, 16, 8, 8, 8, 0.25, B.MLA_F32, B.MLA_F32)
     assert lib.mla_prefill_attn(ctypes.byref(tiny), p, p, p, p, p, 100, 0, 10, p, null, null) == B.MLA_ERR_UNSUPPORTED
 
+
+def test_noalloc_checks_before_touching_its_scratch(B):
+    """mla_decode_noalloc refuses bad arguments, both or neither output form,
+    and a split whose partials would not fit its static scratch, before it
+    looks up or touches the scratch (nothing is launched here)."""
+    lib = B.raw_lib()
+    cfg = v2(B)
+    c = ctypes.byref(cfg)
+    q = ctypes.c_void_p(0x1000)
+    null = None
+    plan = B.MlaPlan(256, 256 + 126, 0)
+    ok_args = lambda batch, o_lat, w_uv, out: [c, q, q, q, 10, q, 4, q, null, 0, batch, ctypes.byref(plan),
+                                               o_lat, w_uv, out, null, null]
+    # neither output, both outputs
+    assert lib.mla_decode_noalloc(*ok_args(127, null, null, null)) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_noalloc(*ok_args(127, q, q, q)) == B.MLA_ERR_INVALID_ARG
+    # up-projection form without weights
+    assert lib.mla_decode_noalloc(*ok_args(127, null, null, q)) == B.MLA_ERR_INVALID_ARG
+    # 256 workers + 200 requests - 1 = 455 BF16 partial slots of 131,584 B: over 48 MiB
+    assert lib.mla_decode_noalloc(*ok_args(200, q, null, null)) == B.MLA_ERR_SCRATCH
+    assert lib.mla_decode_noalloc(*ok_args(200, null, q, q)) == B.MLA_ERR_SCRATCH
+    # the usual checks of the attention call (misaligned query, no plan)
+    args = ok_args(127, q, null, null)
+    args[1] = ctypes.c_void_p(0x1008)
+    assert lib.mla_decode_noalloc(*args) == B.MLA_ERR_INVALID_ARG
+    args = ok_args(127, q, null, null)
+    args[11] = None
+    assert lib.mla_decode_noalloc(*args) == B.MLA_ERR_INVALID_ARG
+    # the largest batch that fits with 256 workers: 382 slots
+    assert (382 * (128 * 512 * 2) + 382 * 128 * 4) <= B.NOALLOC_SCRATCH_BYTES < (383 * (128 * 512 * 2) + 383 * 128 * 4)
+    assert B.status_string(B.MLA_ERR_SCRATCH) != "unknown status"
