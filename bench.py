@@ -161,6 +161,48 @@ def cpu_baselines_other(I):
     return res
 
 
+class TimingEvents:
+    """HIP timing events created with hipEventDisableSystemFence: recording
+    one enqueues a timestamp without the system-scope cache writeback and
+    invalidate that a default event adds, so events between launches do not
+    slow the launches around them.  Uses the HIP runtime torch has loaded."""
+
+    FLAG = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, torch):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.torch = torch
+        self.events = []
+
+    def new(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.FLAG) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        f = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
 class ClockProbe:
     """Mean shader clock over a region of the stream: each probe launch records
     s_memtime (shader clock counter) and s_memrealtime (100 MHz) per XCD;
@@ -223,6 +265,39 @@ class ClockProbe:
             raise RuntimeError(f"stream read failed ({st})")
 
 
+def _run_ms(torch, fn, reps):
+    """Average time of fn() over reps back-to-back calls, HIP events only at
+    the two ends (an event between launches adds a gap and a cache flush)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def _graph_ms(torch, calls, reps):
+    """Average time per call of a list of launches captured once in a HIP
+    graph and replayed reps times (HIP events at the two ends): for legs whose
+    launches are shorter than their launch from Python.  None of the captured
+    calls records a memset."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for c in calls:
+                c()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    ms = _run_ms(torch, g.replay, reps)
+    del g
+    return ms / len(calls)
+
+
 def _median_ms(torch, fn, reps):
     ms = []
     for _ in range(reps):
@@ -264,21 +339,18 @@ def tiny_leg(torch, I, runner, reps=200):
     w = runner.DeviceWorkload(inp, split=False)
     w.step()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        w.step()
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / reps
+    us = _graph_ms(torch, [w.step] * 20, reps // 20) * 1e3
     return {"step_us": round(us, 2), "cache_bytes_per_step": int(I.cache_bytes_read(inp)),
-            "note": "absorb, attention (direct mode), merge, up-projection; launch-latency bound"}
+            "note": "absorb, attention (direct mode), up-projection, timed as HIP graph replays; "
+                    "launch-latency bound"}
 
 
 def single_leg(torch, I, runner, num_cus, copies=64, reps=4):
     """The single 4,096-token request: its 4.7 MB of cache would sit in the
     last-level cache, so the step cycles over `copies` copies of the pool at
-    different addresses (302 MB in all) and every launch reads HBM."""
+    different addresses (302 MB in all) and every launch reads HBM.  The
+    steps are shorter than their launch from Python, so they are timed as HIP
+    graph replays."""
     inp = I.make_inputs("v2_single")
     w = runner.DeviceWorkload(inp, split=True, num_cus=num_cus)
     n = w.pool.shape[0]
@@ -289,24 +361,17 @@ def single_leg(torch, I, runner, num_cus, copies=64, reps=4):
         w.table = t
         w.step_fused()
     torch.cuda.synchronize()
-    ev = []
-    for _ in range(reps):
-        for t in tables:
+
+    def on_copy(t, fn):
+        def call():
             w.table = t
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            e[0].record()
-            w.absorb()
-            e[1].record()
-            w.attend()
-            e[2].record()
-            w.combine_up()
-            e[3].record()
-            ev.append(e)
-    torch.cuda.synchronize()
+            fn()
+        return call
+
     cache_bytes = I.cache_bytes_read(inp)
-    step_us = float(np.median([e[0].elapsed_time(e[3]) for e in ev])) * 1e3
-    attn_us = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
-    return {"step_us_median": round(step_us, 2), "attn_us_median": round(attn_us, 2),
+    step_us = _graph_ms(torch, [on_copy(t, w.step_fused) for t in tables], reps) * 1e3
+    attn_us = _graph_ms(torch, [on_copy(t, w.attend) for t in tables], reps) * 1e3
+    return {"step_us": round(step_us, 2), "attn_us": round(attn_us, 2),
             "cache_GBps": round(cache_bytes / (step_us * 1e-6) / 1e9, 1),
             "attn_GBps": round(cache_bytes / (attn_us * 1e-6) / 1e9, 1),
             "tokens_per_s": round(1e6 / step_us, 1), "cache_bytes_per_step": int(cache_bytes),
@@ -318,8 +383,8 @@ def long_context_token(torch, I, runner, DI, num_cus, layers=60, tokens=10):
     (1 request x 131,072 positions each, 9.06 GB of cache in all), each layer
     absorb -> attention -> merge + up-projection.  The layers are drawn on the
     device (seed 4000 + layer).  The 180 launches of a token are captured in
-    one HIP graph and the graph is replayed; one eager token with events
-    between launches gives the per-layer attention time."""
+    one HIP graph and the graph is replayed; the 60 attention launches alone,
+    back to back, give the per-layer attention time."""
     ws = []
     for layer in range(layers):
         t = DI.draw_bf16_layer(torch, 4000 + layer, [131072])
@@ -328,18 +393,7 @@ def long_context_token(torch, I, runner, DI, num_cus, layers=60, tokens=10):
     for w in ws:
         w.step_fused()
     torch.cuda.synchronize()
-    ev = []
-    for w in ws:
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        e[0].record()
-        w.absorb()
-        e[1].record()
-        w.attend()
-        e[2].record()
-        w.combine_up()
-        ev.append(e)
-    torch.cuda.synchronize()
-    attn_us = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    attn_us = _run_ms(torch, lambda: [w.attend() for w in ws], 3) * 1e3 / layers
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -356,7 +410,7 @@ def long_context_token(torch, I, runner, DI, num_cus, layers=60, tokens=10):
     return {"ms_per_token_median": round(tok_ms, 3), "tokens_per_s": round(1e3 / tok_ms, 1),
             "cache_GBps": round(cache_bytes / (tok_ms * 1e-3) / 1e9, 1),
             "cache_bytes_per_token": int(cache_bytes), "layers": layers,
-            "attn_us_per_layer_median": round(attn_us, 2),
+            "attn_us_per_layer": round(attn_us, 2),
             "attn_GBps": round(cache_bytes / layers / (attn_us * 1e-6) / 1e9, 1),
             "eager_ms_per_token": round(eager_ms, 3), "tokens_timed": tokens,
             "timing": "HIP graph of the 60 layers' 180 launches, replayed; layers drawn on the device"}
@@ -368,7 +422,9 @@ def fp8_topk_step(torch, I, runner, DI, num_cus, group128, lists=16, reps=6):
     or one per 128 latent channels).  One step reads 42 MB out of a 1.35 GB
     pool, which would otherwise stay in the last-level cache, so the steps
     cycle over `lists` independently drawn index-list sets (675 MB of distinct
-    rows).  Reports the step and attention times (medians), the cache rate and
+    rows).  Steps and single launches are timed as HIP graph replays (they
+    are shorter than their launch from Python).  Reports the step and
+    attention times, the cache rate and
     both roofline fractions (HBM, and BF16 matrix cores: the FP8 latent is
     widened to BF16 for the MFMAs).  Returns (result, workload)."""
     t = DI.draw_fp8_topk(torch, 5, group128=group128)
@@ -384,28 +440,19 @@ def fp8_topk_step(torch, I, runner, DI, num_cus, group128, lists=16, reps=6):
         w.topk_idx = s_
         w.step_fused()
     torch.cuda.synchronize()
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    att = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps * lists)]
-    step_ev[0].record()
-    for r in range(reps):
-        for i, s_ in enumerate(sets):
-            e = att[r * lists + i]
-            w.topk_idx = s_
-            e[0].record()
-            w.absorb()
-            e[1].record()
-            w.attend()
-            e[2].record()
-            w.combine_up()
-            e[3].record()
-    step_ev[1].record()
-    torch.cuda.synchronize()
-    step_us = step_ev[0].elapsed_time(step_ev[1]) * 1e3 / (reps * lists)
-    attn_us = float(np.median([e[1].elapsed_time(e[2]) for e in att])) * 1e3
-    tail_us = float(np.median([e[2].elapsed_time(e[3]) for e in att])) * 1e3
-    absorb_us = float(np.median([e[0].elapsed_time(e[1]) for e in att])) * 1e3
-    res = {"step_us": round(step_us, 2), "attn_us_median": round(attn_us, 2),
-           "absorb_us_median": round(absorb_us, 2), "combine_out_up_us_median": round(tail_us, 2),
+
+    def on_set(t, fn):
+        def call():
+            w.topk_idx = t
+            fn()
+        return call
+
+    step_us = _graph_ms(torch, [on_set(t, w.step_fused) for t in sets], reps) * 1e3
+    attn_us = _graph_ms(torch, [on_set(t, w.attend) for t in sets], reps) * 1e3
+    absorb_us = _graph_ms(torch, [w.absorb] * lists, reps) * 1e3
+    tail_us = _graph_ms(torch, [w.combine_up] * lists, reps) * 1e3
+    res = {"step_us": round(step_us, 2), "attn_us": round(attn_us, 2),
+           "absorb_us": round(absorb_us, 2), "combine_out_up_us": round(tail_us, 2),
            "cache_bytes_per_step": int(cache_bytes),
            "attn_cache_GBps": round(cache_bytes / (attn_us * 1e-6) / 1e9, 1),
            "attn_hbm_frac": round(cache_bytes / (attn_us * 1e-6) / (HBM_PEAK_GBPS * 1e9), 4),
@@ -600,6 +647,14 @@ def main():
     num_cus = torch.cuda.get_device_properties(0).multi_processor_count
     w = runner.DeviceWorkload(inp, split=True, num_cus=num_cus)
     probe = ClockProbe(torch)
+    # The first launch of a kernel loads its code object, which stalls the
+    # host for tens of milliseconds; the GPU idles meanwhile and its clock
+    # drops, and the steps that follow run up to twice as long until it has
+    # recovered.  So every kernel the timed region and its probes use is
+    # launched once here, before the settle.
+    probe.mark()
+    probe.stream_read(torch.zeros(16 * 256 * 8, dtype=torch.uint8, device="cuda"), 1)
+    w.step_fused()
     torch.cuda.synchronize()
     log(f"resident on GPU after {time.time() - t0:.1f} s; workers {w.plan.num_workers}, "
         f"workspace {w.plan.workspace_bytes / 1e6:.1f} MB")
@@ -642,26 +697,38 @@ def main():
     clock = probe.mhz(c0, c1)
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
-    # the same K steps again with events between the three launches of every
-    # step, on the launch stream: absorb, attention, merge + up-projection
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # The same K steps again with timing events between the three launches
+    # of every step, on the launch stream (absorb, attention, merge +
+    # up-projection).  The events are recorded without the system-scope fence
+    # a default event adds (its cache writeback and invalidate slowed the
+    # launches after it by 10-20%); the whole pass is timed as well, to show
+    # the events leave the step time as it was.
+    te = TimingEvents(torch)
+    ev = [[te.new() for _ in range(4)] for _ in range(args.steps)]
+    p0, p1 = te.new(), te.new()
+    torch.cuda.synchronize()
     c2 = probe.mark()
+    te.record(p0, stream)
     for k in range(args.steps):
-        ev[k][0].record(stream)
+        te.record(ev[k][0], stream)
         w.absorb()
-        ev[k][1].record(stream)
+        te.record(ev[k][1], stream)
         w.attend()
-        ev[k][2].record(stream)
+        te.record(ev[k][2], stream)
         w.combine_up()
-        ev[k][3].record(stream)
+        te.record(ev[k][3], stream)
+    te.record(p1, stream)
     c3 = probe.mark()
     torch.cuda.synchronize()
     clock_parts = probe.mhz(c2, c3)
-    part = lambda i: np.array([e[i].elapsed_time(e[i + 1]) for e in ev])
+    instrumented_ms_per_step = te.ms(p0, p1) / args.steps
+    part = lambda i: np.array([te.ms(e[i], e[i + 1]) for e in ev])
     absorb_ms, attn_ms, tail_ms = part(0), part(1), part(2)
-    attn_avg_ms = float(attn_ms.mean())
+    te.close()
+    absorb_avg_ms, attn_avg_ms, tail_avg_ms = float(absorb_ms.mean()), float(attn_ms.mean()), float(tail_ms.mean())
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s), clock {clock['mean_MHz']} MHz; "
-        f"with events between launches: attention {attn_avg_ms * 1e3:.1f} us")
+        f"with timing events: {instrumented_ms_per_step * 1e3:.1f} us/step, attention {attn_avg_ms * 1e3:.1f} us, "
+        f"absorb {absorb_avg_ms * 1e3:.1f} us, merge + up-projection {tail_avg_ms * 1e3:.1f} us")
 
     gbps = cache_bytes / (ms_per_step * 1e-3) / 1e9
     attn_gbps = cache_bytes / (attn_avg_ms * 1e-3) / 1e9
@@ -673,19 +740,19 @@ def main():
     gemm_flop = 2.0 * inp.B * inp.H * inp.D_C * inp.D_N
     w_bytes = inp.H * inp.D_C * inp.D_N * 2
 
-    def gemm(ms, act_bytes):
-        m, med = float(ms.mean()), float(np.median(ms))
-        return {"us": round(m * 1e3, 2), "us_median": round(med * 1e3, 2),
+    def gemm(m, act_bytes):
+        return {"us": round(m * 1e3, 2),
                 "weight_GBps": round(w_bytes / (m * 1e-3) / 1e9, 1),
                 "bytes_GBps": round((w_bytes + act_bytes) / (m * 1e-3) / 1e9, 1),
                 "mfma_util": round(gemm_flop / (m * 1e-3) / BF16_PEAK_FLOPS, 5)}
 
     part_bytes = w.plan.num_slots * inp.H * (inp.D_C * 2 + 4)  # BF16 partials + lse
     parts = {
-        "absorb": gemm(absorb_ms, inp.B * inp.H * (inp.D_N + inp.D_C) * 2),
+        "absorb": gemm(absorb_avg_ms, inp.B * inp.H * (inp.D_N + inp.D_C) * 2),
         "attention": {"us": round(attn_avg_ms * 1e3, 2), "us_median": round(float(np.median(attn_ms)) * 1e3, 2),
                       "mfma_util": round(attn_flop / (attn_avg_ms * 1e-3) / BF16_PEAK_FLOPS, 4)},
-        "combine_out_up": gemm(tail_ms, part_bytes + inp.B * inp.H * inp.D_V * 2),
+        "combine_out_up": gemm(tail_avg_ms, part_bytes + inp.B * inp.H * inp.D_V * 2),
+        "step_us_with_timing_events": round(instrumented_ms_per_step * 1e3, 2),
     }
     result = {
         "metric": "MLA decode latent-KV read GB/s (% HBM peak) + tokens/s, B=64 ctx=32K",
@@ -724,8 +791,8 @@ def main():
         },
         "cpu_baseline": None,
         "parts": parts,
-        "parts_timing": "a second pass of the same K steps with HIP events between the launches (events add a "
-                        "gap and a cache flush, so these times are upper bounds)",
+        "parts_timing": "a second pass of the K steps with HIP timing events (no system-scope fence) between "
+                        "the launches on the launch stream: average launch duration",
         "clock_timed_region": clock,
         "clock_parts_pass": clock_parts,
         "settle": {"seconds": args.settle_s, "steps": settle_steps},
@@ -738,7 +805,7 @@ def main():
         log(f"read ceiling {result['read_ceiling']['GBps']} GB/s")
         configs = {"tiny_fp32": tiny_leg(torch, I, runner)}
         configs["v2_single"] = single_leg(torch, I, runner, num_cus)
-        log(f"v2_single {configs['v2_single']['step_us_median']} us/step")
+        log(f"v2_single {configs['v2_single']['step_us']} us/step")
         configs["v2_long_token"] = long_context_token(torch, I, runner, DI, num_cus)
         log(f"v2_long {configs['v2_long_token']['ms_per_token_median']} ms/token")
         torch.cuda.empty_cache()

@@ -74,21 +74,28 @@ __device__ __forceinline__ float wave_partner(float v) {
   return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
 }
 
-// Lane (l % 32, hi = l / 32) of a weighted-latent accumulator set O[16]
-// (U^T blocks of 32 columns, one head per lane) holds columns
-// 32 mb + 8 g + 4 hi + e of its head in O[mb][4 g + e].  Write the head's 512
-// columns, times inv, as BF16 to row[0..511] with 16-byte stores: the two
-// lanes of a head swap half of each pair of groups so that each lane owns 8
-// consecutive columns per store (32 stores per lane instead of 64).
-__device__ __forceinline__ void store_row_bf16(__bf16* row, const f32x16 (&O)[16], float inv) {
-  const int hi = __lane_id() >> 5;
+// Normalised accumulator (times inv) of a wave's 32 heads (w: the wave) as
+// BF16 rows [32][512] at dst, staged through LDS so that every global store
+// writes one contiguous 1 KiB row instead of 32-byte pieces of 32 rows.  The
+// staging area is the first 4 x 32 rows of 1,040 bytes of the work-group's
+// LDS (the tile ring): every tile load must have landed and every wave must
+// be done reading the ring, which the barrier here provides; the caller's
+// next use of the ring synchronises again.
+__device__ __forceinline__ void store_rows_staged(LDS char* L, __bf16* dst, const f32x16 (&O)[16], float inv, int w) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  const int lane = __lane_id();
+  const int hi = lane >> 5, row = lane & 31;
+  constexpr int kPitch = kCRow + 16;  // padded rows: the row-wise writes spread over the banks
+  LDS char* mine = L + w * 32 * kPitch;
+  LDS char* rowL = mine + row * kPitch;
+  // lane (row, hi) holds columns 32 mb + 8 g + 4 hi + e; the two lanes of a
+  // row swap half of each group pair so each writes 16 contiguous bytes
 #pragma unroll
   for (int mb = 0; mb < 16; ++mb)
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int g0 = 2 * k, g1 = 2 * k + 1;
-      // hi = 0 keeps group g0 (columns 8 g0 + 0..3) and sends g1 (8 g1 + 0..3);
-      // hi = 1 keeps group g1 (8 g1 + 4..7) and sends g0 (8 g0 + 4..7).
       uint32_t keep[2], send[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -101,12 +108,14 @@ __device__ __forceinline__ void store_row_bf16(__bf16* row, const f32x16 (&O)[16
       uint32_t recv[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) recv[e] = __float_as_uint(wave_partner(__uint_as_float(send[e])));
-      // hi = 0: columns 8 g0 + [own 0..3 | partner's 4..7]
-      // hi = 1: columns 8 g1 + [partner's 0..3 | own 4..7]
       const i32x4 v = hi ? i32x4{(int)recv[0], (int)recv[1], (int)keep[0], (int)keep[1]}
                          : i32x4{(int)keep[0], (int)keep[1], (int)recv[0], (int)recv[1]};
-      *(i32x4*)(row + 32 * mb + 8 * (hi ? g1 : g0)) = v;
+      *(LDS i32x4*)(rowL + 2 * (32 * mb + 8 * (hi ? g1 : g0))) = v;
     }
+  // each wave reads back only its own rows: no barrier needed
+#pragma unroll
+  for (int r = 0; r < 32; ++r)
+    *(i32x4*)(dst + r * kLatent + 8 * lane) = *(const LDS i32x4*)(mine + r * kPitch + 16 * lane);
 }
 
 // x * alpha for an accumulator value, kept in its accumulator register.  The

@@ -94,7 +94,7 @@ struct MergePlan {
   // the same, given W and the units below request b
   __device__ __forceinline__ void init(const CombineArgs& a, int32_t b, int h, int64_t W_, int64_t below) {
     W = W_;
-    const int64_t start = below + kLeadTiles;  // first tile of request b
+    const int64_t start = below + lead_of(a.topk);  // first tile of request b
     const int32_t nt_b = a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[b]);
     P = a.num_workers;
     H = a.H;
@@ -324,7 +324,8 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
     int64_t off = 0;
     for (int32_t base = 0; base < a.batch; base += 64) {
       const int32_t r = base + lane;
-      const int64_t sp = r < a.batch ? span_of(a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[r])) : 0;
+      const int64_t sp =
+          r < a.batch ? span_of(a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[r]), a.topk) : 0;
       int64_t incl = sp;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {

@@ -9,6 +9,7 @@
 // softmax never stalls the matrix cores:
 //
 //   iteration j:  wait for tile j, barrier, start the load of tile j + 2
+//                 (if the segment has it)
 //                 scores of tile j                        (36 MFMAs)
 //                 weighted latent of tile j - 1           (32 MFMAs)
 //                   with the softmax of tile j interleaved between them
@@ -29,9 +30,9 @@
 // XOR swizzle of the LDS rows is folded into them), and M0 as the LDS
 // destination.  Page ids come from the block table through scalar loads one
 // tile ahead.  Positions past the context end or on an invalid page are still
-// loaded from a valid page (so every wave always issues the same number of
-// loads and the vmcnt accounting holds), then zeroed in LDS and masked out
-// of the softmax.
+// loaded from a valid page (so every wave issues the same loads per tile),
+// then zeroed in LDS and masked out of the softmax.  No tile is loaded past a
+// segment's end: the last two iterations wait for everything in flight.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
   // of request b0's span (a span is the request's lead, then its tiles) ----
   int32_t b0, v0;
   int64_t n;
-  const int64_t worker = blockIdx.x;
+  const int64_t worker = DIRECT ? (int64_t)blockIdx.x : xcd_worker(blockIdx.x, gridDim.x);
   auto ntiles = [&](int32_t b) -> int32_t {
     const int32_t T = sload(a.seq_lens + b);
     return T > 0 ? tiles_of(T) : 0;
@@ -245,45 +246,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     }
   };
 
-  // Normalised accumulator (times inv) of this wave's 32 heads as BF16 rows
-  // [32][512] at dst.  Every stand-in load must have landed and every wave
-  // must have finished reading the stages before they are reused here; the
-  // next segment drains and synchronises again before loading into them.
-  auto store_rows_staged = [&](__bf16* dst, float inv) __attribute__((always_inline)) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    constexpr int kPitch = kCRow + 16;  // padded rows: the row-wise writes spread over the banks
-    LDS char* mine = L + w * 32 * kPitch;
-    LDS char* rowL = mine + row * kPitch;
-    // lane (row, hi) holds columns 32 mb + 8 g + 4 hi + e; the two lanes of a
-    // row swap half of each group pair so each writes 16 contiguous bytes
-#pragma unroll
-    for (int mb = 0; mb < 16; ++mb)
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int g0 = 2 * k, g1 = 2 * k + 1;
-        uint32_t keep[2], send[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const bf16x2 k0 = {(__bf16)(O[mb][4 * g0 + 2 * e] * inv), (__bf16)(O[mb][4 * g0 + 2 * e + 1] * inv)};
-          const bf16x2 k1 = {(__bf16)(O[mb][4 * g1 + 2 * e] * inv), (__bf16)(O[mb][4 * g1 + 2 * e + 1] * inv)};
-          const uint32_t u0 = __builtin_bit_cast(uint32_t, k0), u1 = __builtin_bit_cast(uint32_t, k1);
-          keep[e] = hi ? u1 : u0;
-          send[e] = hi ? u0 : u1;
-        }
-        uint32_t recv[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) recv[e] = __float_as_uint(wave_partner(__uint_as_float(send[e])));
-        const i32x4 v = hi ? i32x4{(int)recv[0], (int)recv[1], (int)keep[0], (int)keep[1]}
-                           : i32x4{(int)keep[0], (int)keep[1], (int)recv[0], (int)recv[1]};
-        *(LDS i32x4*)(rowL + 2 * (32 * mb + 8 * (hi ? g1 : g0))) = v;
-      }
-    // each wave reads back only its own rows: no barrier needed
-#pragma unroll
-    for (int r = 0; r < 32; ++r)
-      *(i32x4*)(dst + r * kLatent + 8 * lane) = *(const LDS i32x4*)(mine + r * kPitch + 16 * lane);
-  };
-
   int32_t cb = b0;
   int64_t cv = v0;   // offset of the next unit inside request cb's span
   int64_t done = 0;  // units consumed
@@ -308,14 +270,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     // earlier stores and loads count on vmcnt too, so drain first.
     wait_vmcnt<0>();
     __syncthreads();
-    // Page ids are fetched one tile ahead of the load that needs them.  Every
-    // iteration loads one tile (past the segment end a stand-in from page 0
-    // that nothing reads), so each wait is the same vmcnt count.  The first
-    // two tiles are loaded before the queries, so the two latencies overlap.
+    // Page ids are fetched one tile ahead of the load that needs them.  No
+    // tile is loaded past the segment end, so nothing is left in flight when
+    // the segment's result is written.  The first two tiles are loaded before
+    // the queries, so the two latencies overlap.
     int32_t pg_a = ld.page_of(ct >> 1);                                     // tile ct
     int32_t pg_b = seg > 1 ? ld.page_of((ct + 1) >> 1) : -1;               // tile ct + 1
     ld.issue(0, ct, pg_a);
-    ld.issue(1, ct + 1, pg_b);
+    if (seg > 1) ld.issue(1, ct + 1, pg_b);
     // page of tile ct + 2: loaded now, checked when its load is issued
     int32_t pg_next_p = seg > 2 ? (ct + 2) >> 1 : INT32_MAX;
     int32_t pg_next_raw = ld.raw(seg > 2 ? pg_next_p : 0);
@@ -361,14 +323,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
 
     for (int32_t j = 0; j < seg; ++j) {
       const int32_t t = ct + j;
-      // tile j landed (tile j + 1 may still be in flight)
-      wait_vmcnt<kDmaPerWave>();
+      // tile j landed (tile j + 1, if the segment has it, may still be in
+      // flight)
+      if (j + 1 < seg) wait_vmcnt<kDmaPerWave>();
+      else wait_vmcnt<0>();
       __syncthreads();
       // stage (j + 2) % 4 held tile j - 2, consumed in the previous
       // iteration; tile j + 2 is loaded into it during the scores below
       const int32_t pg_next = ld.checked(pg_next_p, pg_next_raw);
       const bool valid_j2 = pg_next >= 0;
       const TileLoader::Tile next_tile = ld.tile((j + 2) & 3, t + 2, pg_next);
+      const bool has_next = j + 2 < seg;
       pg_next_p = j + 3 < seg ? (t + 3) >> 1 : INT32_MAX;
       pg_next_raw = ld.raw(j + 3 < seg ? pg_next_p : 0);
       // rows of tile j that are visible
@@ -444,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
       };
       stream(std::true_type{}, j & 3, (j + 3) & 3, Pp0, Pp1, s,
              [&](int k) {
-               if ((k & 3) == 0 && (k >> 2) < kDmaPerWave) ld.issue_one(next_tile, k >> 2);
+               if (has_next && (k & 3) == 0 && (k >> 2) < kDmaPerWave) ld.issue_one(next_tile, k >> 2);
              },
              piece);
 
@@ -480,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
       const int64_t slot = worker + cb;
       __bf16* rows = DIRECT ? (__bf16*)a.o_lat + (int64_t)cb * kHeads * kLatent
                             : (__bf16*)a.part_o + slot * kHeads * kLatent;
-      store_rows_staged(rows + (int64_t)32 * w * kLatent, inv);
+      store_rows_staged(L, rows + (int64_t)32 * w * kLatent, O, inv, w);
       if (DIRECT) {
         if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
       } else {
@@ -492,7 +457,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     cv = 0;
     while (cb < a.batch && ntiles(cb) == 0) ++cb;
   }
-  wait_vmcnt<0>();
+  // Only stores can be in flight here (every tile load was waited for);
+  // the wave may end with them outstanding.
 }
 
 }  // namespace

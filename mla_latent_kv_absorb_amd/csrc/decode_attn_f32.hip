@@ -38,22 +38,26 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
   int32_t cb, ct = 0;
   int64_t cv, n;
   const int64_t worker = blockIdx.x;
+  const int32_t lead = lead_of(TOPK ? a.topk : 0);
   if (DIRECT) {
     cb = blockIdx.x;
-    cv = kLeadTiles;  // no lead: straight to tile 0
+    cv = lead;  // straight to tile 0
     n = ntiles(cb);
   } else {
     // n units of the split space from offset cv of request cb's span (the
     // request's lead, then its tiles)
     int64_t W = 0;
-    for (int32_t b = 0; b < a.batch; ++b) W += span_of(ntiles(b));
+    for (int32_t b = 0; b < a.batch; ++b) W += span_of(ntiles(b), TOPK ? a.topk : 0);
     const int64_t g0 = worker_lo(worker, W, a.num_workers);
     const int64_t g1 = worker_lo(worker + 1, W, a.num_workers);
     n = g1 - g0;
     if (n <= 0) return;
     int64_t acc = 0;
     int32_t b = 0;
-    while (acc + span_of(ntiles(b)) <= g0) { acc += span_of(ntiles(b)); ++b; }
+    while (acc + span_of(ntiles(b), TOPK ? a.topk : 0) <= g0) {
+      acc += span_of(ntiles(b), TOPK ? a.topk : 0);
+      ++b;
+    }
     cb = b;
     cv = g0 - acc;
   }
@@ -72,13 +76,13 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
   int64_t i = 0;
   while (i < n) {
     if (cb >= a.batch) break;  // unreachable when the tile accounting is consistent
-    if (cv < kLeadTiles) {  // the lead of request cb carries no work
-      const int64_t skip = kLeadTiles - cv < n - i ? kLeadTiles - cv : n - i;
+    if (cv < lead) {  // the lead of request cb carries no work
+      const int64_t skip = lead - cv < n - i ? lead - cv : n - i;
       i += skip;
       cv += skip;
       if (i >= n) break;
     }
-    ct = (int32_t)(cv - kLeadTiles);
+    ct = (int32_t)(cv - lead);
     const int64_t left = ntiles(cb) - ct;
     const int64_t seg = left < n - i ? left : n - i;
     if (seg <= 0) break;

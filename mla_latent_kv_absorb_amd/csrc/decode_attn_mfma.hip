@@ -26,9 +26,12 @@
 //
 // FP8 cache: the latent arrives as E4M3 with one float32 scale per position,
 // or one per 128 latent channels of a position ("DeepSeek's KV Cache", section
-// "Calculating V3.2's KV cache").  A conversion pass dequantises the tile into
-// BF16 in LDS: the exact E4M3 value times its scale, rounded once to BF16.
-// The scores and the weighted latent then run exactly as for a BF16 cache.
+// "Calculating V3.2's KV cache").  A conversion pass turns the tile into BF16
+// in LDS.  With one scale per position the BF16 values are the codes' exact
+// values, and the scale is applied in float32: the latent part of each score
+// is multiplied by it, and so is each probability that weights the row.  With
+// group scales the value times its scale is rounded once to BF16, and the
+// scores and the weighted latent then run exactly as for a BF16 cache.
 //
 // Sparse selection ("DeepSeek's KV Cache", Figure 10): with an index list the
 // tile rows are the listed positions, gathered one row per load; entries that
@@ -228,10 +231,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   // of request b0's span (a span is the request's lead, then its tiles) ----
   int32_t b0, v0;
   int64_t n;
-  int64_t worker = blockIdx.x;
+  const int64_t worker = DIRECT ? (int64_t)blockIdx.x : xcd_worker(blockIdx.x, gridDim.x);
+  const int32_t lead = lead_of(TOPK ? a.topk : 0);
   if (DIRECT) {
     b0 = blockIdx.x;
-    v0 = kLeadTiles;  // no lead: straight to tile 0
+    v0 = lead;  // straight to tile 0
     n = ld.ntiles(b0);
   } else {
     const int64_t W = spans_below(a.seq_lens, a.batch, TOPK ? a.topk : 0);
@@ -273,13 +277,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   while (i < n) {
     // ---- one segment: tiles [ct, ct + seg_len) of request cb ----
     if (cb >= a.batch) break;  // unreachable when the tile accounting is consistent
-    if (cv < kLeadTiles) {  // the lead of request cb carries no work
-      const int64_t skip = kLeadTiles - cv < n - i ? kLeadTiles - cv : n - i;
+    if (cv < lead) {  // the lead of request cb carries no work
+      const int64_t skip = lead - cv < n - i ? lead - cv : n - i;
       i += skip;
       cv += skip;
       if (i >= n) break;
     }
-    const int32_t ct = (int32_t)(cv - kLeadTiles);
+    const int32_t ct = (int32_t)(cv - lead);
     const int32_t nt_cb = ld.ntiles(cb);
     const int64_t left_in_req = nt_cb - ct;
     const int32_t seg_len = (int32_t)(left_in_req < n - i ? left_in_req : n - i);
@@ -342,9 +346,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
           for (int k = 0; k < 8; ++k) {
             const int r = 8 * w + k;
             const i32x2 raw = *(const LDS i32x2*)(src + k * kC8Row);
-            // lane l covers channels 8l .. 8l + 7: group l / 16 of 128 channels
-            const float sc = GS ? scl[C::SCALES * r + (lane >> 4)] : scl[r];
-            // E4M3 pairs -> exact float32 pairs, times the scale, one rounding to BF16
+            // E4M3 pairs -> exact float32 pairs.  One scale per position is
+            // applied later, in float32, to the scores and probabilities, so
+            // the BF16 values are the codes' exact values; with group scales
+            // (lane l covers channels 8l .. 8l + 7: group l / 16 of 128) the
+            // value times its scale is rounded once to BF16.
             const f32x2 v[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(raw[0], false),
                                 __builtin_amdgcn_cvt_pk_f32_fp8(raw[0], true),
                                 __builtin_amdgcn_cvt_pk_f32_fp8(raw[1], false),
@@ -352,7 +358,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
             i32x4 outv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const bf16x2 b = {(__bf16)(v[e][0] * sc), (__bf16)(v[e][1] * sc)};
+              bf16x2 b;
+              if (GS) {
+                const float sc = scl[C::SCALES * r + (lane >> 4)];
+                b = bf16x2{(__bf16)(v[e][0] * sc), (__bf16)(v[e][1] * sc)};
+              } else {
+                b = bf16x2{(__bf16)v[e][0], (__bf16)v[e][1]};
+              }
               outv[e] = __builtin_bit_cast(int, b);
             }
             if (!((mask >> r) & 1)) outv = i32x4{0, 0, 0, 0};
@@ -378,6 +390,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         // Operands are read SD blocks ahead into a register ring; scheduling
         // fences keep the order "MFMA k, then the read for k + SD" so the LDS
         // latency hides behind the MFMAs.
+        // FP8 with one scale per position: the latent part of the score is
+        // computed from the codes' exact values and multiplied by the row's
+        // scale in float32 before the rotary part is added; the scales of
+        // this lane's 16 positions (rows 8 (r / 4) + 4 hi + r % 4) are kept
+        // for the probabilities too.  Masked rows get scale 0 (their latent
+        // rows are zero, and their scale may be anything).
+        constexpr bool FOLD = FP8 && !GS;
+        float rsc[16];
+        if (FOLD) {
+          const LDS float* scl = (const LDS float*)(L + st * C::STAGE + C::C_STAGE + C::R_STAGE);
+          const uint32_t mlane = mask >> (4 * hi);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const f32x4 v = *(const LDS f32x4*)(scl + 8 * k + 4 * hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rsc[4 * k + e] = ((mlane >> (8 * k + e)) & 1u) ? v[e] : 0.f;
+          }
+        }
         f32x16 sacc = f32x16{};
         {
           constexpr int SD = 4;
@@ -391,6 +421,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int k = 0; k < 36; ++k) {
+            if (FOLD && k == 32) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) sacc[r] *= rsc[r];
+            }
             const bf16x8 bq = k < 32 ? q[k] : qr[k - 32];
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[k % SD], bq, sacc, 0, 0, 0);
             if (k + SD < 36) ring[k % SD] = s_operand(k + SD);
@@ -435,7 +469,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         for (int r = 0; r < 16; ++r) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, neg_m));
           lsum += p;
-          P[r >> 3][r & 7] = (__bf16)p;
+          // the weighted latent sums p times the dequantised row: the row's
+          // scale goes into the probability operand
+          P[r >> 3][r & 7] = (__bf16)(FOLD ? p * rsc[r] : p);
         }
         l_run += lsum;
 
@@ -473,23 +509,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       const float l_tot = l_run + wave_partner(l_run);
       const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
       const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      // BF16 rows of this wave's 32 heads (the final o_lat, or the partial:
+      // partials of the MFMA kernels are BF16), staged through LDS so that
+      // every global store writes one contiguous 1 KiB row
+      const int64_t slot = worker + cb;
+      __bf16* rows = DIRECT ? (__bf16*)a.o_lat + (int64_t)cb * kHeads * kLatent
+                            : (__bf16*)a.part_o + slot * kHeads * kLatent;
+      store_rows_staged(L, rows + (int64_t)32 * w * kLatent, O, inv, w);
       if (DIRECT) {
-        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-        __bf16* o = (__bf16*)a.o_lat + ((int64_t)cb * kHeads + head) * kLatent + 4 * hi;
-#pragma unroll
-        for (int mb = 0; mb < 16; ++mb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            bf16x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(O[mb][4 * g + e] * inv);
-            *(bf16x4*)(o + 32 * mb + 8 * g) = v;
-          }
         if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
       } else {
-        // partials of the MFMA kernels are BF16
-        const int64_t slot = worker + cb;
-        store_row_bf16((__bf16*)a.part_o + (slot * kHeads + head) * kLatent, O, inv);
         if (hi == 0) a.part_lse[slot * kHeads + head] = lse;
       }
     }
@@ -498,7 +527,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     cv = 0;
     while (cb < a.batch && ld.ntiles(cb) == 0) ++cb;
   }
-  wait_vmcnt<0>();
+  // Only stores can be in flight here (every tile load was waited for);
+  // the wave may end with them outstanding.
 }
 
 }  // namespace

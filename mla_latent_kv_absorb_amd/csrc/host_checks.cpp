@@ -367,6 +367,10 @@ mla_status mla_decode_plan(const mla_config* cfg, int32_t batch, const int32_t* 
   int64_t P = (W + kMinTilesPerWorker - 1) / kMinTilesPerWorker;
   if (P > num_cus) P = num_cus;
   if (P > kMaxWorkers) P = kMaxWorkers;
+  // Index lists give every request the same tile count and no lead: with a
+  // multiple of the batch as worker count every worker covers tiles of one
+  // request only, so it starts one segment and writes one partial.
+  if (topk > 0 && P >= batch) P -= P % batch;
   if (P < 1) P = 1;
   plan->num_workers = (int32_t)P;
   plan->num_slots = (int32_t)(P + batch - 1);

@@ -98,9 +98,10 @@ constexpr size_t decode_f32_lds_bytes(int H, int D_C, int D_R) {
 
 // ---------------------------------------------------------------------------
 // Split partition shared by the attention kernels and the combine kernel.
-// Every request with at least one tile occupies span_of(nt) = kLeadTiles + nt
-// units of a concatenated space (requests in order, W units in total): a
-// lead of kLeadTiles units that carry no work, then its nt tiles.  Worker p
+// Every request with at least one tile occupies span_of(nt) = lead + nt units
+// of a concatenated space (requests in order, W units in total): a lead of
+// kLeadTiles units that carry no work (dense requests only), then its nt
+// tiles.  Worker p
 // takes units [lo(p), lo(p+1)) with lo(p) = floor(p*W/P) and processes the
 // tiles among them.  The lead stands for the fixed cost of starting a request
 // (query loads, pipeline fill, one more partial to write): a worker whose
@@ -110,11 +111,15 @@ constexpr size_t decode_f32_lds_bytes(int H, int D_C, int D_R) {
 // and b never both stay the same from one piece to the next.
 // ---------------------------------------------------------------------------
 constexpr int32_t kLeadTiles = 12;
+// With index lists every request has the same number of tiles and there is no
+// lead: a plan whose worker count is a multiple of the batch then gives every
+// worker tiles of one request only (one segment, one partial).
+constexpr int32_t lead_of(int32_t topk) { return topk > 0 ? 0 : kLeadTiles; }
 constexpr int64_t worker_lo(int64_t p, int64_t W, int64_t P) { return (p * W) / P; }
 // Worker whose range contains unit x (0 <= x < W).
 constexpr int64_t worker_of(int64_t x, int64_t W, int64_t P) { return ((x + 1) * P - 1) / W; }
 constexpr int32_t tiles_of(int32_t len) { return (len + kTile - 1) / kTile; }
 // Units of the split space taken by a request with nt tiles.
-constexpr int64_t span_of(int32_t nt) { return nt > 0 ? (int64_t)nt + kLeadTiles : 0; }
+constexpr int64_t span_of(int32_t nt, int32_t topk) { return nt > 0 ? (int64_t)nt + lead_of(topk) : 0; }
 
 }  // namespace mla

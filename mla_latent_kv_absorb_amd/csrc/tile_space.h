@@ -26,25 +26,35 @@ __device__ inline int64_t wave_sum_i64(int64_t v) {
   return uniform_i64(v);
 }
 
+// Worker index of work-group b of P.  Work-groups are dispatched round-robin
+// over the 8 XCDs (work-group b runs on XCD b % 8), each with its own L2.
+// Consecutive workers share requests (their queries and page-table rows), so
+// they are given to work-groups of one XCD: worker (b % 8) * (P / 8) + b / 8.
+__device__ inline int64_t xcd_worker(uint32_t b, uint32_t P) {
+  constexpr uint32_t kXcds = 8;
+  if (P % kXcds != 0) return b;
+  return (int64_t)(b % kXcds) * (P / kXcds) + b / kXcds;
+}
+
 // Units of the split space (span_of) taken by requests [0, upto).
 __device__ inline int64_t spans_below(const int32_t* seq_lens, int32_t upto, int32_t topk) {
-  if (topk > 0) return (int64_t)upto * span_of(tiles_of(topk));
+  if (topk > 0) return (int64_t)upto * span_of(tiles_of(topk), topk);
   const int lane = __lane_id();
   int64_t sum = 0;
   for (int32_t base = 0; base < upto; base += 64) {
     const int32_t r = base + lane;
-    sum += r < upto ? span_of(tiles_dense(seq_lens[r])) : 0;
+    sum += r < upto ? span_of(tiles_dense(seq_lens[r]), 0) : 0;
   }
   return wave_sum_i64(sum);
 }
 
 // Request whose span holds unit g of the split space (0 <= g < total) and
-// the unit's offset inside that span (below kLeadTiles: the lead; else tile
-// offset - kLeadTiles).
+// the unit's offset inside that span (below the lead: the lead; else tile
+// offset + lead).
 __device__ inline void locate_span(const int32_t* seq_lens, int32_t batch, int32_t topk, int64_t g,
                                    int32_t* b, int32_t* t) {
   if (topk > 0) {
-    const int64_t sp = span_of(tiles_of(topk));
+    const int64_t sp = span_of(tiles_of(topk), topk);
     *b = (int32_t)(g / sp);
     *t = (int32_t)(g % sp);
     return;
@@ -53,7 +63,7 @@ __device__ inline void locate_span(const int32_t* seq_lens, int32_t batch, int32
   int64_t off = 0;
   for (int32_t base = 0; base < batch; base += 64) {
     const int32_t r = base + lane;
-    const int64_t sp = r < batch ? span_of(tiles_dense(seq_lens[r])) : 0;
+    const int64_t sp = r < batch ? span_of(tiles_dense(seq_lens[r]), 0) : 0;
     int64_t incl = sp;  // inclusive scan over the lanes
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {

@@ -92,7 +92,8 @@ static void test_plan() {
   const int32_t one[1] = {100};
   EXPECT(mla_decode_plan(&c, 1, one, 0, 0, 256, &p) == MLA_OK && p.num_workers == 2);
   EXPECT(mla_decode_plan(&c, 32, nullptr, 0, 2048, 256, &p) == MLA_OK && p.num_workers == 256);
-  EXPECT(mla_decode_plan(&c, 32, nullptr, 0, 2048, 100, &p) == MLA_OK && p.num_workers == 100);
+  EXPECT(mla_decode_plan(&c, 32, nullptr, 0, 2048, 100, &p) == MLA_OK && p.num_workers == 96);
+  EXPECT(mla_decode_plan(&c, 3, nullptr, 0, 300, 256, &p) == MLA_OK && p.num_workers == 15);
   EXPECT(mla_decode_plan(&c, 1, nullptr, 0, 0, 256, &p) == MLA_ERR_INVALID_ARG);  // no lengths at all
   EXPECT(mla_decode_plan(&c, 0, lens, 0, 0, 256, &p) == MLA_ERR_INVALID_ARG);
   EXPECT(mla_decode_plan(&c, 3, lens, 0, 0, 256, nullptr) == MLA_ERR_INVALID_ARG);

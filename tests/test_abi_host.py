@@ -76,7 +76,11 @@ def test_plan_sizes_workspace(B):
     assert single.num_workers == 64
     topk = B.mla_decode_plan(cfg, 32, None, 0, 2048, 256)
     assert topk.num_workers == 256
-    assert B.mla_decode_plan(cfg, 32, None, 0, 2048, 100).num_workers == 100
+    # index lists: a multiple of the batch, so every worker serves one request
+    assert B.mla_decode_plan(cfg, 32, None, 0, 2048, 100).num_workers == 96
+    assert B.mla_decode_plan(cfg, 3, None, 0, 300, 256).num_workers == 15   # 30 tiles, two each
+    assert B.mla_decode_plan(cfg, 40, None, 0, 64, 256).num_workers == 40   # 80 tiles
+    assert B.mla_decode_plan(cfg, 300, None, 0, 64, 256).num_workers == 256  # fewer workers than requests
 
 
 def test_invalid_arguments_rejected_before_launch(B):

@@ -399,10 +399,10 @@ def test_fp8_group_scales_differ_per_group(torch, R):
     """Group scales that differ by up to 2^4 across the four groups of a
     position (and across positions): the per-group dequantisation, not a
     per-position one, is what matches the oracle (one scale for all groups
-    would be off by the whole latent).  The spread is kept where the scores
-    stay near unit size, the regime the BF16 tolerance is derived for; a
-    2^10 spread gives scores of ~9 sigma, where BF16 rounding of the latent
-    alone moves the peaked softmax past it."""
+    would be off by the whole latent).  The spread is kept at 2^-2 .. 2^2:
+    at 2^-5 .. 2^5 the BF16 rounding of the absorbed query alone takes the
+    output past the 2e-2 bound, whatever the dequantisation
+    (test_precision_model.py models it)."""
     _log("fp8 group scales spread")
     inp = I.make_inputs("v2_fp8g_topk", seed=24, batch=3, ctx=(200, 700), topk=0)
     rng = np.random.default_rng(24)
@@ -410,6 +410,34 @@ def test_fp8_group_scales_differ_per_group(torch, R):
     # latents up to 4x larger make scores (and their rounding error) up to 4x
     # larger: the lse bound scales with them
     check_step(torch, R, inp, split=True, lse_tol=4 * LSE_ABS_TOL)
+
+
+def test_fp8_per_position_scales_applied_in_float32(torch, R):
+    """Per-position scales spread over 2^-5 .. 2^5, with q_lat given as BF16
+    values that the oracle uses too (so the query's own rounding is out of the
+    comparison).  The kernel widens the E4M3 codes exactly and multiplies the
+    latent scores and the probabilities by each position's scale in float32,
+    which keeps o_lat within 4e-3 of the oracle here; rounding code x scale
+    to BF16 first gives 2.3-3.5e-2 on these rows (test_precision_model.py
+    models both), so the 1e-2 bound tells the two apart."""
+    _log("fp8 per-position scales, wide spread")
+    inp = I.make_inputs("v2_fp8_topk", seed=24, batch=3, ctx=(200, 700), topk=0)
+    rng = np.random.default_rng(24)
+    inp.c_scales[:] = inp.c_scales * np.exp2(rng.integers(-5, 6, size=inp.c_scales.shape)).astype(np.float32)
+    q_lat = I.round_to_bf16(oracle.absorb_query(inp.q_nope, inp.w_uk).astype(np.float32))
+    for split in (False, True):
+        w = R.DeviceWorkload(inp, split=split)
+        w.attend(q_lat=R.to_device_act(q_lat, I.DTYPE_BF16, "cuda"))
+        w.combine()
+        torch.cuda.synchronize()
+        o_lat, lse = to_np(w.o_lat), to_np(w.lse)
+        for b in range(inp.B):
+            lo, hi = inp.request(b)
+            c = oracle.dequant_fp8_latent(inp.c_codes[lo:hi], inp.c_scales[lo:hi])
+            ref_o, ref_l = oracle.latent_decode(q_lat[b], inp.q_rope[b], c, inp.k_rope[lo:hi], inp.scale)
+            err = assert_close(o_lat[b], ref_o, tol_rel=1e-2, what=f"o_lat b={b} split={split}")
+            _log(f"  b={b} split={split}: o_lat max|err|/max|ref| = {err / np.max(np.abs(ref_o)):.2e}")
+            assert_close(lse[b], ref_l, abs_tol=LSE_ABS_TOL, what=f"lse b={b} split={split}")
 
 
 def test_out_of_range_indices_are_skipped(torch, R):
