@@ -161,48 +161,6 @@ def cpu_baselines_other(I):
     return res
 
 
-class TimingEvents:
-    """HIP timing events created with hipEventDisableSystemFence: recording
-    one enqueues a timestamp without the system-scope cache writeback and
-    invalidate that a default event adds, so events between launches do not
-    slow the launches around them.  Uses the HIP runtime torch has loaded."""
-
-    FLAG = 0x20000000  # hipEventDisableSystemFence
-
-    def __init__(self, torch):
-        import ctypes
-        self.ct = ctypes
-        self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
-        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.torch = torch
-        self.events = []
-
-    def new(self):
-        e = self.ct.c_void_p()
-        if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.FLAG) != 0:
-            raise RuntimeError("hipEventCreateWithFlags failed")
-        self.events.append(e)
-        return e
-
-    def record(self, e, stream):
-        if self.hip.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream)) != 0:
-            raise RuntimeError("hipEventRecord failed")
-
-    def ms(self, a, b):
-        f = self.ct.c_float()
-        if self.hip.hipEventElapsedTime(self.ct.byref(f), a, b) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return f.value
-
-    def close(self):
-        for e in self.events:
-            self.hip.hipEventDestroy(e)
-        self.events = []
-
-
 class ClockProbe:
     """Mean shader clock over a region of the stream: each probe launch records
     s_memtime (shader clock counter) and s_memrealtime (100 MHz) per XCD;
@@ -220,6 +178,7 @@ class ClockProbe:
         self.lib.mlab_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
         self.lib.mlab_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_void_p]
+        self.lib.mlab_stamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.torch = torch
         self.bufs = []
 
@@ -256,6 +215,12 @@ class ClockProbe:
             per_xcd[str(x)] = round(float(np.median([v for xx, v in per_unit if xx == x])), 1)
         return {"mean_MHz": round(float(np.median(vals)), 1), "units": len(per_unit), "per_xcd_MHz": per_xcd,
                 "realtime_ticks": int(np.median(b[:, 1]) - np.median(a[:, 1]))}
+
+    def stamp(self, buf, i):
+        """Real-time stamp (100 MHz ticks) into buf[i] when the stream gets there."""
+        st = self.lib.mlab_stamp(buf.data_ptr() + 8 * i, self.torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"stamp failed ({st})")
 
     def stream_read(self, buf, groups):
         sink = self.torch.zeros(groups, dtype=self.torch.int32, device="cuda")
@@ -681,54 +646,64 @@ def main():
     log(f"settle {settle_steps} steps, warmup {args.warmup} done")
 
     stream = torch.cuda.current_stream()
-    # the timed region: K whole steps, HIP events only at its two ends (an
-    # event recorded between two launches adds a cache flush and a gap)
+    # The timed region: K whole steps, HIP events only at its two ends (an
+    # event recorded between two launches slows the launch after it).  The
+    # passes that time single launches are queued right behind it, each after
+    # a bridge of untimed steps, and the host does not wait in between: a
+    # GPU left idle for a few milliseconds drops its clock, and the launches
+    # after the gap run slow until it has recovered.
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     c0 = probe.mark()
-    wall0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
         w.step_fused()
     stop.record(stream)
     c1 = probe.mark()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    clock = probe.mhz(c0, c1)
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
-    # The same K steps again with timing events between the three launches
-    # of every step, on the launch stream (absorb, attention, merge +
-    # up-projection).  The events are recorded without the system-scope fence
-    # a default event adds (its cache writeback and invalidate slowed the
-    # launches after it by 10-20%); the whole pass is timed as well, to show
-    # the events leave the step time as it was.
-    te = TimingEvents(torch)
-    ev = [[te.new() for _ in range(4)] for _ in range(args.steps)]
-    p0, p1 = te.new(), te.new()
-    torch.cuda.synchronize()
+    # Per-launch times: the same K steps with a one-wave stamp kernel between
+    # the launches that writes the real-time counter (100 MHz).  A stamp is an
+    # ordinary launch on the stream, without the cache writeback and
+    # invalidate of an event.
+    stamps = torch.zeros((args.steps, 4), dtype=torch.int64, device="cuda")
+    for _ in range(20):
+        w.step_fused()
     c2 = probe.mark()
-    te.record(p0, stream)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
     for k in range(args.steps):
-        te.record(ev[k][0], stream)
+        probe.stamp(stamps[k], 0)
         w.absorb()
-        te.record(ev[k][1], stream)
+        probe.stamp(stamps[k], 1)
         w.attend()
-        te.record(ev[k][2], stream)
+        probe.stamp(stamps[k], 2)
         w.combine_up()
-        te.record(ev[k][3], stream)
-    te.record(p1, stream)
+        probe.stamp(stamps[k], 3)
+    p1.record(stream)
     c3 = probe.mark()
+    # and with HIP events around the attention launches, for comparison
+    for _ in range(20):
+        w.step_fused()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        w.absorb()
+        ev[k][0].record(stream)
+        w.attend()
+        ev[k][1].record(stream)
+        w.combine_up()
     torch.cuda.synchronize()
+    clock = probe.mhz(c0, c1)
+    ms_per_step = start.elapsed_time(stop) / args.steps
     clock_parts = probe.mhz(c2, c3)
-    instrumented_ms_per_step = te.ms(p0, p1) / args.steps
-    part = lambda i: np.array([te.ms(e[i], e[i + 1]) for e in ev])
+    stamped_ms_per_step = p0.elapsed_time(p1) / args.steps
+    ticks = stamps.cpu().numpy().astype(np.float64)
+    part = lambda i: (ticks[:, i + 1] - ticks[:, i]) / 1e5   # 100 MHz ticks -> ms
     absorb_ms, attn_ms, tail_ms = part(0), part(1), part(2)
-    te.close()
     absorb_avg_ms, attn_avg_ms, tail_avg_ms = float(absorb_ms.mean()), float(attn_ms.mean()), float(tail_ms.mean())
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s), clock {clock['mean_MHz']} MHz; "
-        f"with timing events: {instrumented_ms_per_step * 1e3:.1f} us/step, attention {attn_avg_ms * 1e3:.1f} us, "
-        f"absorb {absorb_avg_ms * 1e3:.1f} us, merge + up-projection {tail_avg_ms * 1e3:.1f} us")
+    attn_event_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, clock {clock['mean_MHz']} MHz; "
+        f"with stamps: {stamped_ms_per_step * 1e3:.1f} us/step, attention {attn_avg_ms * 1e3:.1f} us, "
+        f"absorb {absorb_avg_ms * 1e3:.1f} us, merge + up-projection {tail_avg_ms * 1e3:.1f} us; "
+        f"attention between HIP events {attn_event_ms * 1e3:.1f} us")
 
     gbps = cache_bytes / (ms_per_step * 1e-3) / 1e9
     attn_gbps = cache_bytes / (attn_avg_ms * 1e-3) / 1e9
@@ -752,7 +727,8 @@ def main():
         "attention": {"us": round(attn_avg_ms * 1e3, 2), "us_median": round(float(np.median(attn_ms)) * 1e3, 2),
                       "mfma_util": round(attn_flop / (attn_avg_ms * 1e-3) / BF16_PEAK_FLOPS, 4)},
         "combine_out_up": gemm(tail_avg_ms, part_bytes + inp.B * inp.H * inp.D_V * 2),
-        "step_us_with_timing_events": round(instrumented_ms_per_step * 1e3, 2),
+        "step_us_with_stamps": round(stamped_ms_per_step * 1e3, 2),
+        "attention_us_between_hip_events": round(attn_event_ms * 1e3, 2),
     }
     result = {
         "metric": "MLA decode latent-KV read GB/s (% HBM peak) + tokens/s, B=64 ctx=32K",
@@ -788,11 +764,14 @@ def main():
             "unit": "GB/s",
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic_from_profile(),
+            "timing": "average attention launch duration in a pass of the K steps with a one-wave stamp kernel "
+                      "(real-time counter) between launches; with HIP events between launches the launch takes "
+                      "attention_us_between_hip_events",
         },
         "cpu_baseline": None,
         "parts": parts,
-        "parts_timing": "a second pass of the K steps with HIP timing events (no system-scope fence) between "
-                        "the launches on the launch stream: average launch duration",
+        "parts_timing": "a second pass of the K steps with a one-wave kernel between the launches on the launch "
+                        "stream stamping the real-time counter (100 MHz): average launch duration",
         "clock_timed_region": clock,
         "clock_parts_pass": clock_parts,
         "settle": {"seconds": args.settle_s, "steps": settle_steps},

@@ -13,6 +13,9 @@
 //                     delta(realtime), from work-groups that ran on the same
 //                     compute unit both times (the counters of different
 //                     units are not aligned).
+//   mlab_stamp        one wave writes the real-time counter to a slot: launched
+//                     between two launches on a stream it marks the boundary
+//                     between them, for per-launch times without events.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -56,9 +59,25 @@ __global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t* __restrict__ 
   }
 }
 
+// One wave writes the real-time counter (100 MHz) to *slot.  Launched on the
+// stream between two launches it time-stamps the boundary between them
+// without the cache writeback and invalidate of an event.
+__global__ __launch_bounds__(64) void stamp_kernel(uint64_t* __restrict__ slot) {
+  const uint64_t r = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) *slot = r;
+}
+
 }  // namespace
 
 extern "C" {
+
+// *slot = the real-time counter when the stamp runs on `stream`.
+int mlab_stamp(uint64_t* slot, void* stream) {
+  if (!slot) return 1;
+  hipLaunchKernelGGL(stamp_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, slot);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
 
 // Read `bytes` bytes of `src` (16-byte aligned) once.  `bytes` must be a
 // multiple of 16 * 256 * 8 * num_groups; sink holds num_groups words (written

@@ -272,10 +272,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     __syncthreads();
     // Page ids are fetched one tile ahead of the load that needs them.  No
     // tile is loaded past the segment end, so nothing is left in flight when
-    // the segment's result is written.  The first two tiles are loaded before
-    // the queries, so the two latencies overlap.
-    int32_t pg_a = ld.page_of(ct >> 1);                                     // tile ct
-    int32_t pg_b = seg > 1 ? ld.page_of((ct + 1) >> 1) : -1;               // tile ct + 1
+    // the segment's result is written.  The page ids of the first two tiles
+    // go out first; while they are in flight the queries are requested (the
+    // latent queries into registers, the rotary queries straight into LDS),
+    // then the two tiles; all of it lands before the loop, in one round trip
+    // after the page ids.
+    const int32_t raw_a = ld.raw(ct >> 1);                                  // tile ct
+    const int32_t raw_b = ld.raw(seg > 1 ? (ct + 1) >> 1 : 0);             // tile ct + 1
+    {
+      const __bf16* ql = (const __bf16*)a.q_lat + ((int64_t)cb * kHeads + head) * kLatent + 8 * hi;
+#pragma unroll
+      for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8*)(ql + 16 * kb);
+      // rotary queries: rows 32 w + 8 p .. + 7 per load, lane l bringing the
+      // chunk that LDS position l % 8 of its row holds (rows swizzled like
+      // the rotary keys)
+      const __bf16* qp = (const __bf16*)a.q_rope + (int64_t)cb * kHeads * kRope;
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int hh = 32 * w + 8 * pass + (lane >> 3);
+        const int c = (lane & 7) ^ swz_r(hh);
+        dma16(qp + hh * kRope + 8 * c, ld.lds_base + kQrOff + (32 * w + 8 * pass) * kRRow);
+      }
+    }
+    const int32_t pg_a = ld.checked(ct >> 1, raw_a);
+    const int32_t pg_b = seg > 1 ? ld.checked((ct + 1) >> 1, raw_b) : -1;
     ld.issue(0, ct, pg_a);
     if (seg > 1) ld.issue(1, ct + 1, pg_b);
     // page of tile ct + 2: loaded now, checked when its load is issued
@@ -283,21 +303,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     int32_t pg_next_raw = ld.raw(seg > 2 ? pg_next_p : 0);
     // validity of the tiles in flight, by stage: tile ct + j has stage j % 4
     bool valid_j = pg_a >= 0, valid_j1 = pg_b >= 0;
-    {
-      const __bf16* ql = (const __bf16*)a.q_lat + ((int64_t)cb * kHeads + head) * kLatent + 8 * hi;
-#pragma unroll
-      for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8*)(ql + 16 * kb);
-#pragma unroll
-      for (int kb = 0; kb < 32; ++kb) asm volatile("" ::"v"(q[kb]));
-      // rotary queries into LDS: thread -> (head, 16-byte chunk), 4 passes
-      const __bf16* qp = (const __bf16*)a.q_rope + (int64_t)cb * kHeads * kRope;
-#pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        const int hh = (tid >> 3) + 32 * pass, c = tid & 7;
-        const bf16x8 v = *(const bf16x8*)(qp + hh * kRope + 8 * c);
-        *(LDS bf16x8*)(L + kQrOff + hh * kRRow + 16 * (c ^ swz_r(hh))) = v;
-      }
-    }
     {
       // The weighted latent of "tile -1" reads stage 3 with zero
       // probabilities; zero its latent rows so stale or uninitialised LDS
@@ -308,6 +313,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
       for (int v = 0; v < 8; ++v) *(LDS i32x4*)(dst + 16 * v) = i32x4{0, 0, 0, 0};
     }
     wait_vmcnt<0>();  // queries and the first two tiles
+    // take the latent queries here, so the waits for them sit before the
+    // tile loop (all satisfied) and not inside it
+#pragma unroll
+    for (int kb = 0; kb < 32; ++kb) asm volatile("" ::"v"(q[kb]));
 
 
 #pragma unroll

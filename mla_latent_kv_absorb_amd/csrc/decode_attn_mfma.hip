@@ -56,7 +56,11 @@ struct Cfg {
   static constexpr int LIST_OFF = CONV_OFF + CONV;             // page ids / row codes of a chunk
   static constexpr int LIST = 2048;                            // entries (int32)
   static constexpr int MASK_OFF = LIST_OFF + LIST * 4;
-  static constexpr int LDS_BYTES = MASK_OFF + NS * 4;
+  // FP8: the rotary queries of the segment's request live in LDS
+  // ([head][64] BF16, rows swizzled) instead of 16 registers per lane
+  static constexpr bool QR_LDS = FP8;
+  static constexpr int QR_OFF = MASK_OFF + 32;
+  static constexpr int LDS_BYTES = QR_LDS ? QR_OFF + kHeads * kRRow : MASK_OFF + NS * 4;
   static constexpr int DMA_PER_WAVE = FP8 ? 6 : 9;             // loads per wave per tile
 };
 
@@ -309,6 +313,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8*)(ql + 16 * kb);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) qr[kb] = *(const bf16x8*)(qp + 16 * kb);
+        if (C::QR_LDS) {
+          // chunk 2 kb + hi of this lane's head, swizzled like the rotary keys
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            *(LDS bf16x8*)(L + C::QR_OFF + head * kRRow + 16 * ((2 * kb + hi) ^ swz_r(head))) = qr[kb];
+        }
       }
       __syncthreads();  // the row list is complete
       // the first tiles go in flight while the queries are still loading
@@ -319,8 +329,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         // placed before the tile loop and not inside it
 #pragma unroll
         for (int kb = 0; kb < 32; ++kb) asm volatile("" ::"v"(q[kb]));
+        if (!C::QR_LDS) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) asm volatile("" ::"v"(qr[kb]));
+          for (int kb = 0; kb < 4; ++kb) asm volatile("" ::"v"(qr[kb]));
+        }
       }
 
       for (int32_t j = 0; j < clen; ++j) {
@@ -397,8 +409,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         // for the probabilities too.  Masked rows get scale 0 (their latent
         // rows are zero, and their scale may be anything).
         constexpr bool FOLD = FP8 && !GS;
-        float rsc[16];
-        if (FOLD) {
+        // the 16 scales of this lane's positions (read when needed, twice, so
+        // they hold no registers across the tile)
+        auto row_scales = [&](float (&rsc)[16]) __attribute__((always_inline)) {
           const LDS float* scl = (const LDS float*)(L + st * C::STAGE + C::C_STAGE + C::R_STAGE);
           const uint32_t mlane = mask >> (4 * hi);
 #pragma unroll
@@ -407,7 +420,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
             for (int e = 0; e < 4; ++e) rsc[4 * k + e] = ((mlane >> (8 * k + e)) & 1u) ? v[e] : 0.f;
           }
-        }
+        };
+        auto rq_operand = [&](int v) -> bf16x8 {
+          if (C::QR_LDS) return *(const LDS bf16x8*)(L + C::QR_OFF + head * kRRow + 16 * ((2 * v + hi) ^ swz_r(head)));
+          return qr[v];
+        };
         f32x16 sacc = f32x16{};
         {
           constexpr int SD = 4;
@@ -419,13 +436,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
           for (int k = 0; k < SD; ++k) ring[k] = s_operand(k);
           __builtin_amdgcn_sched_barrier(0);
+          bf16x8 rq[4];
 #pragma unroll
           for (int k = 0; k < 36; ++k) {
+            if (k == 28) {
+#pragma unroll
+              for (int v = 0; v < 4; ++v) rq[v] = rq_operand(v);
+            }
             if (FOLD && k == 32) {
+              float rsc[16];
+              row_scales(rsc);
 #pragma unroll
               for (int r = 0; r < 16; ++r) sacc[r] *= rsc[r];
             }
-            const bf16x8 bq = k < 32 ? q[k] : qr[k - 32];
+            const bf16x8 bq = k < 32 ? q[k] : rq[k - 32];
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[k % SD], bq, sacc, 0, 0, 0);
             if (k + SD < 36) ring[k % SD] = s_operand(k + SD);
             __builtin_amdgcn_sched_barrier(0);
@@ -465,6 +489,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
         float lsum = 0.f;
         bf16x8 P[2];
+        float rsc[16];
+        if (FOLD) row_scales(rsc);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, neg_m));
