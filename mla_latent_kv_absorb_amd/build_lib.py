@@ -35,6 +35,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 SOURCES = [
     ("decode_attn_mfma.hip", True),
     ("decode_attn_bf16.hip", True),
+    ("decode_attn_fp8.hip", True),
     ("decode_attn_f32.hip", True),
     ("combine.hip", True),
     ("head_gemm.hip", True),

@@ -2,6 +2,8 @@
 // kernel translation units only.
 #pragma once
 
+#include <type_traits>
+
 #include "mla_internal.h"
 #include "tile_space.h"
 
@@ -20,6 +22,15 @@ typedef __attribute__((ext_vector_type(2))) int i32x2;
 #define LDS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
+
+// f(integral_constant<int, i>) for i = B .. E - 1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 constexpr int kCRow = kLatent * 2;  // bytes of one BF16 latent row (1024)
 constexpr int kRRow = kRope * 2;    // bytes of one BF16 rotary row (128)
 constexpr int kC8Row = kLatent;     // bytes of one FP8 latent row (512)
@@ -47,6 +58,13 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
+}
+// The same with a 64-bit scalar base and a per-lane 32-bit offset.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma4s(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -135,11 +153,42 @@ __device__ __forceinline__ float scale_acc(float x, float alpha) {
   return x;
 }
 
+// Score MFMA with its accumulator in ordinary registers (the softmax reads the
+// scores with VALU instructions, and the accumulator registers hold the
+// weighted latent).  Back-to-back MFMAs that accumulate into the same
+// registers need no wait states; the reader of the final value waits.  The
+// operands must come from loads (the compiler waits for those), not from VALU
+// instructions.
+__device__ __forceinline__ f32x16 mfma_sv0(const bf16x8& a, const bf16x8& b) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_sv(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
 // Uniform metadata reads go through the constant address space so they become
 // scalar loads (lgkmcnt), never vector loads that would queue behind the
 // in-flight LDS-bound loads on vmcnt.
 __device__ __forceinline__ int32_t sload(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
+}
+
+// Row codes of the listed positions of tiles [tc0, tc0 + len) of request b
+// (all threads; the caller synchronises): page * 64 + slot per entry, -1 for
+// padding, positions out of range and invalid pages.
+__device__ __forceinline__ void fill_index_codes(const DecodeArgs& a, int32_t b, int32_t tc0, int32_t len, int32_t T,
+                                                 LDS int32_t* list, int tid) {
+  const int32_t n = len * kTile;
+  for (int k = tid; k < n; k += kThreads) {
+    const int32_t lp = tc0 * kTile + k;
+    const int32_t idx = lp < a.topk ? a.topk_idx[(int64_t)b * a.topk + lp] : -1;
+    bool v = idx >= 0 && idx < T && (idx >> 6) < a.bt_stride;
+    const int32_t page = v ? a.block_table[(int64_t)b * a.bt_stride + (idx >> 6)] : -1;
+    v = v && page >= 0 && page < a.num_pages;
+    list[k] = v ? page * 64 + (idx & 63) : -1;
+  }
 }
 
 // Per-lane LDS offsets of the MFMA operands inside one tile (relative to the

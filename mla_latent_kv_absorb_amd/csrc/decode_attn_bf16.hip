@@ -47,23 +47,6 @@ constexpr int kDmaPerWave = 9;                  // 8 latent rows + 1 rotary bloc
 constexpr int kQrOff = kNS * kStage;            // rotary queries of the request, [head][64] bf16
 constexpr int kLdsBytes = kQrOff + kHeads * kRRow;  // 160 KiB
 
-__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
-}
-
-// Score MFMA with its accumulator in ordinary registers (the softmax reads the
-// scores with VALU instructions, and the accumulator registers hold the
-// weighted latent).  Back-to-back MFMAs that accumulate into the same
-// registers need no wait states; the reader of the final value waits.
-__device__ __forceinline__ f32x16 mfma_sv0(const bf16x8& a, const bf16x8& b) {
-  f32x16 d;
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-  return d;
-}
-__device__ __forceinline__ void mfma_sv(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-
 struct TileLoader {
   const uint8_t* pool;
   int64_t page_bytes, rope_off, num_pages;

@@ -19,19 +19,18 @@
 // roles).
 //
 // Loads use global_load_lds_dwordx4 (HBM -> LDS without registers) through a
-// 4-stage ring (6 for FP8) with explicit vmcnt waits; the rows are stored with
+// 4-stage ring (5 for FP8) with explicit vmcnt waits; the rows are stored with
 // an XOR swizzle of their 16-byte chunks so the MFMA operand reads are free of
 // bank conflicts.  Page ids and index lists are read with scalar loads so
 // they never wait behind the LDS-bound vector loads.
 //
-// FP8 cache: the latent arrives as E4M3 with one float32 scale per position,
-// or one per 128 latent channels of a position ("DeepSeek's KV Cache", section
-// "Calculating V3.2's KV cache").  A conversion pass turns the tile into BF16
-// in LDS.  With one scale per position the BF16 values are the codes' exact
-// values, and the scale is applied in float32: the latent part of each score
-// is multiplied by it, and so is each probability that weights the row.  With
-// group scales the value times its scale is rounded once to BF16, and the
-// scores and the weighted latent then run exactly as for a BF16 cache.
+// This kernel serves BF16 caches with an index list and FP8 caches with one
+// float32 scale per 128 latent channels of a position ("DeepSeek's KV Cache",
+// section "Calculating V3.2's KV cache"); FP8 caches with one scale per
+// position have their own kernel (decode_attn_fp8.hip).  For the group-scaled
+// FP8 cache a conversion pass turns the tile into BF16 in LDS: each value
+// times its group's scale is rounded once to BF16, and the scores and the
+// weighted latent then run exactly as for a BF16 cache.
 //
 // Sparse selection ("DeepSeek's KV Cache", Figure 10): with an index list the
 // tile rows are the listed positions, gathered one row per load; entries that
@@ -108,15 +107,7 @@ struct Loader {
         list[k] = (page >= 0 && page < a.num_pages) ? page : -1;
       }
     } else {
-      const int32_t n = len * kTile;
-      for (int k = tid; k < n; k += 256) {
-        const int32_t lp = tc0 * kTile + k;
-        const int32_t idx = lp < a.topk ? a.topk_idx[(int64_t)b * a.topk + lp] : -1;
-        bool v = idx >= 0 && idx < T && (idx >> 6) < a.bt_stride;
-        const int32_t page = v ? a.block_table[(int64_t)b * a.bt_stride + (idx >> 6)] : -1;
-        v = v && page >= 0 && page < a.num_pages;
-        list[k] = v ? page * 64 + (idx & 63) : -1;
-      }
+      fill_index_codes(a, b, tc0, len, T, list, tid);
     }
   }
 
@@ -218,6 +209,7 @@ struct Loader {
 
 template <bool FP8, bool GS, bool TOPK, bool DIRECT>
 __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
+  static_assert(FP8 == GS, "FP8 caches served here carry group scales");
   using C = Cfg<FP8, GS>;
   constexpr int NS = C::NS;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
@@ -358,11 +350,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
           for (int k = 0; k < 8; ++k) {
             const int r = 8 * w + k;
             const i32x2 raw = *(const LDS i32x2*)(src + k * kC8Row);
-            // E4M3 pairs -> exact float32 pairs.  One scale per position is
-            // applied later, in float32, to the scores and probabilities, so
-            // the BF16 values are the codes' exact values; with group scales
-            // (lane l covers channels 8l .. 8l + 7: group l / 16 of 128) the
-            // value times its scale is rounded once to BF16.
+            // E4M3 pairs -> exact float32 pairs; each value times its group's
+            // scale (lane l covers channels 8l .. 8l + 7: group l / 16 of 128)
+            // is rounded once to BF16.
             const f32x2 v[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(raw[0], false),
                                 __builtin_amdgcn_cvt_pk_f32_fp8(raw[0], true),
                                 __builtin_amdgcn_cvt_pk_f32_fp8(raw[1], false),
@@ -370,13 +360,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
             i32x4 outv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              bf16x2 b;
-              if (GS) {
-                const float sc = scl[C::SCALES * r + (lane >> 4)];
-                b = bf16x2{(__bf16)(v[e][0] * sc), (__bf16)(v[e][1] * sc)};
-              } else {
-                b = bf16x2{(__bf16)v[e][0], (__bf16)v[e][1]};
-              }
+              const float sc = scl[C::SCALES * r + (lane >> 4)];
+              const bf16x2 b = bf16x2{(__bf16)(v[e][0] * sc), (__bf16)(v[e][1] * sc)};
               outv[e] = __builtin_bit_cast(int, b);
             }
             if (!((mask >> r) & 1)) outv = i32x4{0, 0, 0, 0};
@@ -402,25 +387,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         // Operands are read SD blocks ahead into a register ring; scheduling
         // fences keep the order "MFMA k, then the read for k + SD" so the LDS
         // latency hides behind the MFMAs.
-        // FP8 with one scale per position: the latent part of the score is
-        // computed from the codes' exact values and multiplied by the row's
-        // scale in float32 before the rotary part is added; the scales of
-        // this lane's 16 positions (rows 8 (r / 4) + 4 hi + r % 4) are kept
-        // for the probabilities too.  Masked rows get scale 0 (their latent
-        // rows are zero, and their scale may be anything).
-        constexpr bool FOLD = FP8 && !GS;
-        // the 16 scales of this lane's positions (read when needed, twice, so
-        // they hold no registers across the tile)
-        auto row_scales = [&](float (&rsc)[16]) __attribute__((always_inline)) {
-          const LDS float* scl = (const LDS float*)(L + st * C::STAGE + C::C_STAGE + C::R_STAGE);
-          const uint32_t mlane = mask >> (4 * hi);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const f32x4 v = *(const LDS f32x4*)(scl + 8 * k + 4 * hi);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rsc[4 * k + e] = ((mlane >> (8 * k + e)) & 1u) ? v[e] : 0.f;
-          }
-        };
         auto rq_operand = [&](int v) -> bf16x8 {
           if (C::QR_LDS) return *(const LDS bf16x8*)(L + C::QR_OFF + head * kRRow + 16 * ((2 * v + hi) ^ swz_r(head)));
           return qr[v];
@@ -442,12 +408,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
             if (k == 28) {
 #pragma unroll
               for (int v = 0; v < 4; ++v) rq[v] = rq_operand(v);
-            }
-            if (FOLD && k == 32) {
-              float rsc[16];
-              row_scales(rsc);
-#pragma unroll
-              for (int r = 0; r < 16; ++r) sacc[r] *= rsc[r];
             }
             const bf16x8 bq = k < 32 ? q[k] : rq[k - 32];
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[k % SD], bq, sacc, 0, 0, 0);
@@ -489,15 +449,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
         float lsum = 0.f;
         bf16x8 P[2];
-        float rsc[16];
-        if (FOLD) row_scales(rsc);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, neg_m));
           lsum += p;
-          // the weighted latent sums p times the dequantised row: the row's
-          // scale goes into the probability operand
-          P[r >> 3][r & 7] = (__bf16)(FOLD ? p * rsc[r] : p);
+          P[r >> 3][r & 7] = (__bf16)p;
         }
         l_run += lsum;
 
@@ -575,7 +531,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, CacheKind kind, hipStream_t s
     }                                                                                                    \
   } while (0)
   switch (kind) {
-    case CacheKind::kFp8Token: MLA_LAUNCH(true, false); break;
+    case CacheKind::kFp8Token: return launch_decode_fp8(a, s);
     case CacheKind::kFp8Group128: MLA_LAUNCH(true, true); break;
     default: MLA_LAUNCH(false, false); break;
   }

@@ -12,6 +12,7 @@ namespace mla {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, CacheKind kind, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);  // BF16 cache, dense
+hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t s);   // FP8 cache, one scale per position
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_combine_up(const CombineUpArgs& u, hipStream_t s);  // V2 dims, BF16
