@@ -49,7 +49,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_v2_batched_traffic.js
 # Sources that define the timed attention kernel (decode_bf16_kernel): the
 # traffic counters are used only while they match.
 KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_absorb_amd", "csrc", f)
-               for f in ("decode_attn_bf16.hip", "attn_common.h", "tile_space.h", "mla_internal.h")]
+               for f in ("decode_attn_bf16.hip", "attn_common.h", "tile_space.h", "mla_internal.h", "mla_args.h")]
 
 
 def log(msg):
@@ -392,6 +392,7 @@ def fp8_topk_step(torch, I, runner, DI, num_cus, group128, lists=16, reps=6):
     attention times, the cache rate and
     both roofline fractions (HBM, and BF16 matrix cores: the FP8 latent is
     widened to BF16 for the MFMAs).  Returns (result, workload)."""
+    log(f"fp8 top-k leg ({'group' if group128 else 'per-position'} scales): drawing inputs")
     t = DI.draw_fp8_topk(torch, 5, group128=group128)
     w = runner.DeviceWorkload(t["shell"], split=True, num_cus=num_cus, tensors=t)
     inp = w.inp
@@ -405,6 +406,7 @@ def fp8_topk_step(torch, I, runner, DI, num_cus, group128, lists=16, reps=6):
         w.topk_idx = s_
         w.step_fused()
     torch.cuda.synchronize()
+    log(f"fp8 top-k leg: {lists} index sets resident; timing")
 
     def on_set(t, fn):
         def call():
@@ -587,6 +589,11 @@ def main():
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--main-only", action="store_true",
                     help="time only the batched workload (no other configurations, no reference read)")
+    ap.add_argument("--configs", default="tiny_fp32,v2_single,v2_long_token,v2_fp8_topk,v2_fp8g_topk",
+                    help="comma-separated configuration legs to run after the batched workload (default: all)")
+    ap.add_argument("--fp8-lists", type=int, default=16,
+                    help="index-list sets the FP8 top-k legs cycle through (fewer for counter runs)")
+    ap.add_argument("--fp8-reps", type=int, default=6, help="graph replays per FP8 top-k timing")
     ap.add_argument("--prefill", action="store_true",
                     help="also time prefill of a 4,096-token prompt on the expanded path")
     ap.add_argument("--indexer", action="store_true",
@@ -782,18 +789,29 @@ def main():
         torch.cuda.empty_cache()
         result["read_ceiling"] = read_ceiling(torch, probe)
         log(f"read ceiling {result['read_ceiling']['GBps']} GB/s")
-        configs = {"tiny_fp32": tiny_leg(torch, I, runner)}
-        configs["v2_single"] = single_leg(torch, I, runner, num_cus)
-        log(f"v2_single {configs['v2_single']['step_us']} us/step")
-        configs["v2_long_token"] = long_context_token(torch, I, runner, DI, num_cus)
-        log(f"v2_long {configs['v2_long_token']['ms_per_token_median']} ms/token")
-        torch.cuda.empty_cache()
-        fp8, _ = fp8_topk_step(torch, I, runner, DI, num_cus, group128=False)
-        configs["v2_fp8_topk"] = fp8
-        torch.cuda.empty_cache()
-        fp8g, wg = fp8_topk_step(torch, I, runner, DI, num_cus, group128=True)
-        configs["v2_fp8g_topk"] = fp8g
-        log(f"fp8 top-k step {fp8['step_us']} / {fp8g['step_us']} us")
+        legs = set(args.configs.split(",")) if args.configs else set()
+        configs = {}
+        if "tiny_fp32" in legs:
+            configs["tiny_fp32"] = tiny_leg(torch, I, runner)
+        if "v2_single" in legs:
+            configs["v2_single"] = single_leg(torch, I, runner, num_cus)
+            log(f"v2_single {configs['v2_single']['step_us']} us/step")
+        if "v2_long_token" in legs:
+            configs["v2_long_token"] = long_context_token(torch, I, runner, DI, num_cus)
+            log(f"v2_long {configs['v2_long_token']['ms_per_token_median']} ms/token")
+            torch.cuda.empty_cache()
+        if "v2_fp8_topk" in legs:
+            fp8, _ = fp8_topk_step(torch, I, runner, DI, num_cus, group128=False, lists=args.fp8_lists,
+                                   reps=args.fp8_reps)
+            configs["v2_fp8_topk"] = fp8
+            log(f"fp8 top-k step {fp8['step_us']} us")
+            torch.cuda.empty_cache()
+        wg = None
+        if "v2_fp8g_topk" in legs or args.indexer:
+            fp8g, wg = fp8_topk_step(torch, I, runner, DI, num_cus, group128=True, lists=args.fp8_lists,
+                                     reps=args.fp8_reps)
+            configs["v2_fp8g_topk"] = fp8g
+            log(f"fp8 top-k step, group scales {fp8g['step_us']} us")
         if args.indexer:
             result["indexer_step"] = indexer_step(torch, I, runner, attn=wg)
         del wg
