@@ -72,6 +72,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// a ^ K (an LDS address and a swizzle constant), computed where it is used:
+// the compiler can then neither keep one register per K alive across a tile
+// loop nor merge two uses into one long-lived value
+template <int K>
+__device__ __forceinline__ uint32_t xor_here(uint32_t a) {
+  if constexpr (K == 0) {
+    return a;
+  } else {
+    uint32_t r;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(K), "v"(a));
+    return r;
+  }
+}
+
 // Maximum of two or three floats in one instruction.  fmaxf first quiets
 // each input (one more instruction per operand); scores are finite or -inf,
 // so nothing needs quieting.

@@ -1,38 +1,44 @@
 // Weight-absorbed MLA decode attention, BF16 latent cache, all positions
 // visible (no index list), gfx950.
 //
-// Same work split and arithmetic as the general attention kernel (4 waves per
-// work-group, each owning 32 of the 128 heads; scores S^T[pos][head] =
-// C . q_lat + K_rope . q_rope on MFMA 32x32x16; online softmax with one head
-// per lane; weighted latent U^T += C^T P^T on MFMA; "DeepSeek's KV Cache",
-// Figures 5 and 6, form (2)), but the tile loop is software-pipelined so the
-// softmax never stalls the matrix cores:
+// Scores as in the general attention kernel: each of the 4 waves owns 32 of
+// the 128 heads, S^T[pos][head] = C . q_lat + K_rope . q_rope on MFMA
+// 32x32x16 with the queries in registers, and an online softmax with one head
+// per lane ("DeepSeek's KV Cache", Figures 5 and 6, form (2)).  The weighted
+// latent is split the other way: wave w accumulates U^T[latent][head] for the
+// latent columns 128 w .. 128 w + 127 and all 128 heads, and takes the
+// probabilities of every head from LDS, where the owner of each head puts
+// them.  A wave then reads only its quarter of a tile with transposing reads
+// (each wave reading the whole tile transposed makes that phase wait on LDS),
+// plus 8 KiB of probabilities with plain 16-byte reads.
 //
 //   iteration j:  wait for tile j, barrier, start the load of tile j + 2
 //                 (if the segment has it)
 //                 scores of tile j                        (36 MFMAs)
+//                 rescale the accumulator if the running maximum of any head
+//                 jumped at tile j - 1 (factors from the heads' owners)
 //                 weighted latent of tile j - 1           (32 MFMAs)
-//                   with the softmax of tile j interleaved between them
-//                 rescale the accumulator if a running maximum jumped
+//                   with the softmax of tile j interleaved between them; its
+//                   probabilities and rescale factors go to LDS
 //
-// The softmax of tile j needs only the scores of tile j, and the weighted
-// latent of tile j - 1 needs only the probabilities of tile j - 1, so the two
-// are independent and the VALU work runs in the shadow of the MFMAs.  The 68
-// MFMAs of an iteration read their LDS operands through one register ring
-// that runs three MFMAs ahead across the switch from scores to weighted
-// latent, and the rotary query blocks are fetched the same distance ahead, so
-// no MFMA waits on a fresh LDS read.  The stage ring holds 4 tiles: j - 1
-// (being consumed), j (being scored), j + 1 and j + 2 (in flight).
+// One barrier per iteration orders everything: what an owner writes for tile
+// j (probabilities, rescale factors) is read in iteration j + 1, and the
+// buffers alternate between even and odd tiles.
+//
+// LDS: 4 latent stages (tiles j - 1 .. j + 2), 3 rotary stages (j .. j + 2:
+// the weighted latent needs no rotary rows), 2 probability buffers and 2
+// rescale-factor buffers.
 //
 // Loads: each wave moves 8 latent rows (1 KiB each) and 8 rotary rows of a
 // tile with global_load_lds_dwordx4 in its scalar-base form: one 64-bit page
-// address per tile, per-lane 32-bit offsets fixed for the whole launch (the
-// XOR swizzle of the LDS rows is folded into them), and M0 as the LDS
-// destination.  Page ids come from the block table through scalar loads one
-// tile ahead.  Positions past the context end or on an invalid page are still
-// loaded from a valid page (so every wave issues the same loads per tile),
-// then zeroed in LDS and masked out of the softmax.  No tile is loaded past a
-// segment's end: the last two iterations wait for everything in flight.
+// address per tile, per-lane 32-bit offsets (the XOR swizzle of the LDS rows
+// is folded into them), and M0 as the LDS destination.  Page ids come from the
+// block table through scalar loads one tile ahead.  Positions past the context
+// end or on an invalid page are still loaded from a valid page (so every wave
+// issues the same loads per tile), then zeroed in LDS and masked out of the
+// softmax.  The last two iterations of a segment load page 0 into the free
+// stages in place of the tiles past its end, so every iteration issues the
+// same instructions; the segment's stores wait for them.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -40,19 +46,38 @@
 namespace mla {
 namespace {
 
-constexpr int kNS = 4;                          // ring stages
-constexpr int kCStage = kTile * kCRow;          // 32 KiB latent rows
-constexpr int kStage = kCStage + kTile * kRRow;  // + 4 KiB rotary rows
-constexpr int kDmaPerWave = 9;                  // 8 latent rows + 1 rotary block per wave and tile
-constexpr int kQrOff = kNS * kStage;            // rotary queries of the request, [head][64] bf16
-constexpr int kLdsBytes = kQrOff + kHeads * kRRow;  // 160 KiB
+constexpr int kNS = 4;                           // latent stages
+constexpr int kNR = 3;                           // rotary stages
+constexpr int kLStage = kTile * kCRow;           // 32 KiB of latent rows
+constexpr int kRStage = kTile * kRRow;           // 4 KiB of rotary rows
+constexpr int kROff = kNS * kLStage;             // the rotary stages
+constexpr int kPOff = kROff + kNR * kRStage;     // probabilities, 2 x [head][32] bf16
+constexpr int kPBytes = kHeads * kTile * 2;      // 8 KiB
+constexpr int kAOff = kPOff + 2 * kPBytes;       // rescale factors, 2 x [128] float
+constexpr int kIOff = kAOff + 2 * kHeads * 4;    // 1 / row sum at a segment's end, [128] float
+constexpr int kLdsBytes = kIOff + kHeads * 4;    // 157.5 KiB
+constexpr int kDmaPerWave = 9;                   // 8 latent rows + 1 rotary block per wave and tile
+constexpr int kPitch = kCRow + 16;               // staging rows of the output (padded: spread over banks)
+constexpr int kD = 4;                            // score operands fetched ahead of their MFMA
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(kHeads * kPitch <= kPOff, "output staging must stay clear of the probability buffers");
+
+// Per-head values that every wave reads (rescale factors, 1 / row sums) are
+// stored with head 32 nb + r at float 4 r + nb: lane r reads its four heads
+// with one 16-byte read.
+__device__ __forceinline__ constexpr int head_slot(int head) { return 4 * (head & 31) + (head >> 5); }
+
+// Probability rows: chunk c (16 bytes) of head h is stored at chunk
+// c ^ pswz(h), so that 16 consecutive heads of one chunk column touch
+// distinct banks (64-bank and 32-bank LDS alike).
+__device__ __forceinline__ constexpr int pswz(int h) { return ((h >> 1) & 3) ^ ((h >> 3) & 1); }
 
 struct TileLoader {
   const uint8_t* pool;
   int64_t page_bytes, rope_off, num_pages;
   const int32_t* bt;  // block-table row of the current request
   int32_t bt_stride;
-  uint32_t lds_base;  // LDS address of stage 0
+  uint32_t lds_base;  // LDS address of the work-group's array
   int w;
   uint32_t lane16;    // 16 * lane
   uint32_t voff_r;    // per-lane byte offset inside this wave's 8 rotary rows
@@ -73,45 +98,103 @@ struct TileLoader {
   }
 
   // This wave's share of tile t (page id `page`, -1 = invalid or no tile)
-  // into stage st, as kDmaPerWave single loads that the caller spreads over
-  // its MFMAs (all loads of a work-group issued at once would queue in the
-  // address unit and stall the issuing waves).  An invalid page is replaced
-  // by page 0: its rows are zeroed after they land.
+  // into latent stage ls and rotary stage rs, as kDmaPerWave single loads that
+  // the caller spreads over its MFMAs (all loads of a work-group issued at
+  // once would queue in the address unit and stall the issuing waves).  An
+  // invalid page is replaced by page 0: its rows are zeroed after they land.
   struct Tile {
     const uint8_t* c_base;
     const uint8_t* r_base;
-    uint32_t sb;
+    uint32_t lsb, rsb;
   };
-  __device__ __forceinline__ Tile tile(int st, int32_t t, int32_t page) const {
+  __device__ __forceinline__ Tile tile(int ls, int rs, int32_t t, int32_t page) const {
     const int64_t pg = page >= 0 ? page : 0;
     const int slot0 = (t & 1) * kTile + 8 * w;
     return Tile{pool + pg * page_bytes + (int64_t)slot0 * kCRow,
-                pool + pg * page_bytes + rope_off + (int64_t)slot0 * kRRow, lds_base + st * kStage};
+                pool + pg * page_bytes + rope_off + (int64_t)slot0 * kRRow,
+                lds_base + ls * kLStage, lds_base + kROff + rs * kRStage};
   }
   __device__ __forceinline__ void issue_one(const Tile& tl, int k) const {
-    if (k < 8)  // latent row 8w + k: lane l fetches chunk l ^ swz(row), so LDS chunk l holds it
-      dma16s(lane16 ^ (16 * swz(8 * w + k)), tl.c_base + k * kCRow, tl.sb + (8 * w + k) * kCRow);
-    else
-      dma16s(voff_r, tl.r_base, tl.sb + kCStage + 8 * w * kRRow);
+    if (k < 8) {
+      // latent row 8w + k: lane l fetches chunk l ^ swz(row), so LDS chunk l
+      // holds it.  lane16 has no bit at or above 1 KiB, so one XOR both
+      // applies the swizzle and adds the row offset k KiB; it is formed here
+      // so no register per row stays live.
+      const uint32_t x = 16 * swz(8 * w + k) + k * kCRow;
+      uint32_t voff;
+      asm volatile("v_xor_b32 %0, %1, %2" : "=v"(voff) : "s"(x), "v"(lane16));
+      dma16s(voff, tl.c_base, tl.lsb + (8 * w + k) * kCRow);
+    } else {
+      dma16s(voff_r, tl.r_base, tl.rsb + 8 * w * kRRow);
+    }
   }
-  __device__ __forceinline__ void issue(int st, int32_t t, int32_t page) const {
-    const Tile tl = tile(st, t, page);
+  __device__ __forceinline__ void issue(const Tile& tl) const {
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) issue_one(tl, k);
   }
 };
 
+// Normalised accumulator of this wave's latent quarter for all 128 heads as
+// BF16 rows [128][512] at dst.  The rows are assembled in LDS (the latent and
+// rotary stages, free once every tile has landed and every wave is past its
+// last read, which the first barrier provides), then every wave writes 32
+// whole rows with 1 KiB stores.  The 1 / row sums come from the heads'
+// owners through kIOff, written before the call.
+__device__ __forceinline__ void store_rows_split(LDS char* L, __bf16* dst, const f32x16 (&O)[16], int w) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  const int lane = __lane_id();
+  const int hi = lane >> 5, row = lane & 31;
+  const f32x4 inv = *(const LDS f32x4*)(L + kIOff + 16 * row);
+  // lane (row, hi) of block (mbl, nb) holds head 32 nb + row, latent columns
+  // 32 (4 w + mbl) + 8 g + 4 hi + e; the two lanes of a head swap half of each
+  // group pair so each writes 16 contiguous bytes
+#pragma unroll
+  for (int mbl = 0; mbl < 4; ++mbl)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x16& o = O[4 * mbl + nb];
+      LDS char* rowL = L + (32 * nb + row) * kPitch + 2 * 32 * (4 * w + mbl);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int g0 = 2 * k, g1 = 2 * k + 1;
+        uint32_t keep[2], send[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bf16x2 k0 = {(__bf16)(o[4 * g0 + 2 * e] * inv[nb]), (__bf16)(o[4 * g0 + 2 * e + 1] * inv[nb])};
+          const bf16x2 k1 = {(__bf16)(o[4 * g1 + 2 * e] * inv[nb]), (__bf16)(o[4 * g1 + 2 * e + 1] * inv[nb])};
+          const uint32_t u0 = __builtin_bit_cast(uint32_t, k0), u1 = __builtin_bit_cast(uint32_t, k1);
+          keep[e] = hi ? u1 : u0;
+          send[e] = hi ? u0 : u1;
+        }
+        uint32_t recv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) recv[e] = __float_as_uint(wave_partner(__uint_as_float(send[e])));
+        const i32x4 v = hi ? i32x4{(int)recv[0], (int)recv[1], (int)keep[0], (int)keep[1]}
+                           : i32x4{(int)keep[0], (int)keep[1], (int)recv[0], (int)recv[1]};
+        *(LDS i32x4*)(rowL + 2 * 8 * (hi ? g1 : g0)) = v;
+      }
+    }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 32; ++r)
+    *(i32x4*)(dst + (32 * w + r) * kLatent + 8 * lane) = *(const LDS i32x4*)(L + (32 * w + r) * kPitch + 16 * lane);
+}
+
 template <bool DIRECT>
 __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  // the operand addresses below are a per-lane base XOR a swizzle constant:
+  // stage bases must not touch the swizzled bits
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   LDS char* L = (LDS char*)smem;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
   const int row = lane & 31;
-  const int head = 32 * w + row;
+  const int head = 32 * w + row;  // the head this lane scores
   const float scale_log2 = a.scale * kLog2e;
 
   // ---- this work-group's share: n units of the split space from offset v0
@@ -145,87 +228,144 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     return;
   }
 
-  const OperandOffsets off(lane);
   TileLoader ld;
   ld.pool = a.pool;
   ld.page_bytes = a.page_bytes;
   ld.rope_off = a.rope_off;
   ld.num_pages = a.num_pages;
   ld.bt_stride = a.bt_stride;
-  ld.lds_base = (uint32_t)(uintptr_t)smem;
+  ld.lds_base = lds0;
   ld.w = w;
   ld.init(lane);
 
-  f32x16 O[16];
-  bf16x8 q[32];
+  // ---- per-lane operand bases.  Each operand address is base ^ K + offset,
+  // with K a compile-time swizzle constant that only touches bits the base
+  // leaves to the swizzle (a 16-byte chunk index (2 v + hi) ^ s splits into
+  // (v ^ (s >> 1)) and (hi ^ (s & 1))). ----
+  uint32_t bs, br, bp, bt0, bt1;
+  {
+    const int sw = swz(row), sr = swz_r(row), ps = pswz(row);
+    // score latent K-block k: row `row`, chunk (2 (k & 7) + hi) ^ swz(row) of column group k >> 3
+    bs = row * kCRow + 16 * (hi ^ (sw & 1)) + 32 * (sw >> 1);
+    // score rotary K-block v: chunk (2 v + hi) ^ swz_r(row)
+    br = row * kRRow + 16 * (hi ^ (sr & 1)) + 32 * (sr >> 1);
+    // probabilities of head 32 nb + row, position chunk 2 kb2 + hi
+    bp = 64 * row + 16 * (hi ^ (ps & 1)) + 32 * (ps >> 1);
+    // transposed latent of this wave's column block 4 w + mbl, rows
+    // 16 kb2 + 8 h8 + tr_row: lane group (hh, ch), lane j16 in it
+    const int j16 = lane & 15, g16 = lane >> 4, hh = g16 >> 1, ch = g16 & 1;
+    const int tr_row = 4 * hh + (j16 >> 2);  // 0..7
+    const int lo = 2 * ch + ((j16 & 3) >> 1);
+    auto tb = [&](int r) {
+      const int sz = swz(r);
+      return (uint32_t)(r * kCRow + 8 * (j16 & 1) + 16 * (lo ^ (sz & 3)) + 64 * (sz >> 2) + 256 * w);
+    };
+    bt0 = tb(tr_row);
+    bt1 = tb(tr_row + 8);
+  }
 
-  // ---- the MFMA stream of one iteration ----
-  // Operand i < 36: score K-block i of the tile in stage `sst` (latent blocks,
-  // then rotary blocks); operand i >= 36: transposed latent block i - 36 of
-  // the tile in stage `pst` for the weighted latent.  One ring of loads runs
-  // three MFMAs ahead across both halves, so the matrix cores never wait for
-  // the first operand of a phase.
-  auto s_operand = [&](const LDS char* Ct, int k) -> bf16x8 {
-    if (k < 32) return *(const LDS bf16x8*)(Ct + off.s_off[k & 7] + 256 * (k >> 3));
-    return *(const LDS bf16x8*)(Ct + kCStage + off.r_off[k - 32]);
+  f32x16 O[16];  // O[4 mbl + nb]: U^T rows 32 (4 w + mbl) .., columns (heads) 32 nb ..
+  bf16x8 q[32];  // latent queries of this lane's head
+  bf16x8 qr[4];  // rotary queries of this lane's head
+
+  // score K-block k < 32 (latent) of the stage at sb, or rotary block k - 32 at rb
+  auto s_read = [&](uint32_t sb, uint32_t rb, auto kc) __attribute__((always_inline)) -> bf16x8 {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k < 32)
+      return *(const LDS bf16x8*)((LDS char*)(uintptr_t)xor_here<32 * (k & 7)>(sb) + 256 * (k >> 3));
+    else
+      return *(const LDS bf16x8*)(LDS char*)(uintptr_t)xor_here<32 * (k - 32)>(rb);
   };
-  // step j: column block mb = j % 16, position half kb2 = j / 16, so that
-  // consecutive MFMAs accumulate into different blocks
-  auto pv_operand = [&](const LDS char* Ct, int j) -> bf16x8 {
-    const int mb = j & 15, kb2 = j >> 4;
-    const LDS char* p1 = Ct + off.tr_off[0][mb & 3] + 256 * (mb >> 2) + 16 * kCRow * kb2;
-    const LDS char* p2 = Ct + off.tr_off[1][mb & 3] + 256 * (mb >> 2) + 16 * kCRow * kb2;
+  // transposed latent (A operand of the weighted latent): column block
+  // 4 w + mbl, positions 16 kb2 .. 16 kb2 + 15 (st = 4 kb2 + mbl)
+  auto a_read = [&](uint32_t t0, uint32_t t1, auto stc) __attribute__((always_inline)) -> bf16x8 {
+    constexpr int st = decltype(stc)::value, mbl = st & 3, kb2 = st >> 2;
+    const LDS char* p1 = (LDS char*)(uintptr_t)xor_here<64 * mbl>(t0) + 16 * kCRow * kb2;
+    const LDS char* p2 = (LDS char*)(uintptr_t)xor_here<64 * mbl>(t1) + 16 * kCRow * kb2;
     s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p1);
     s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p2);
     typedef __attribute__((ext_vector_type(8))) short s16x8;
     return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // rotary query block v of this lane's head (rows swizzled as the rotary keys)
-  auto rq_operand = [&](int v) -> bf16x8 {
-    return *(const LDS bf16x8*)(L + kQrOff + head * kRRow + 16 * ((2 * v + hi) ^ swz_r(head)));
+  // probabilities (B operand of the weighted latent): heads 32 nb .., position half kb2
+  auto b_read = [&](uint32_t pb, int nb, auto kbc) __attribute__((always_inline)) -> bf16x8 {
+    constexpr int kb2 = decltype(kbc)::value;
+    return *(const LDS bf16x8*)((LDS char*)(uintptr_t)xor_here<32 * kb2>(pb) + 2048 * nb);
   };
-  // HAS_S: scores of the tile in sst (36 MFMAs) before the weighted latent of
-  // the tile in pst (32 MFMAs); without it only the weighted latent.
+
+  // ---- the MFMA stream of one iteration ----
+  // HAS_S: the 36 score MFMAs of the tile at (sb, rb) first, then mid(), then
+  // the 32 weighted-latent MFMAs of the tile at (t0, t1) with the
+  // probabilities at pb.  Without HAS_S only mid() and the weighted latent.
   // after_s(k) runs after score MFMA k, piece(k) after weighted MFMA k + 1;
-  // the scores land in s before the first piece.
-  auto stream = [&](auto has_s, int sst, int pst, const bf16x8& P0, const bf16x8& P1, f32x16& s, auto&& after_s,
-                    auto&& piece) __attribute__((always_inline)) {
+  // the scores land in s before mid().
+  //
+  // Score operands are fetched kD MFMAs ahead.  The weighted latent goes
+  // column block by column block (st = 4 kb2 + mbl), each A operand serving
+  // four MFMAs (one per head block nb); A operands alternate between two
+  // registers, the four B operands of a position half sit in four.  The
+  // first A operand and the B operands of half 0 are fetched in the place of
+  // the last score operands.
+  auto stream = [&](auto has_s, uint32_t sb, uint32_t rb, uint32_t t0, uint32_t t1, uint32_t pb, f32x16& s,
+                    auto&& after_s, auto&& mid, auto&& piece) __attribute__((always_inline)) {
     constexpr bool HAS_S = decltype(has_s)::value;
-    constexpr int I0 = HAS_S ? 0 : 36;
-    constexpr int D = 3;
-    const LDS char* Cs = L + sst * kStage;
-    const LDS char* Cp = L + pst * kStage;
-    auto operand = [&](int i) -> bf16x8 { return i < 36 ? s_operand(Cs, i) : pv_operand(Cp, i - 36); };
-    bf16x8 ring[D];
-    bf16x8 rq[D];
-    f32x16 sacc;
-#pragma unroll
-    for (int i = I0; i < I0 + D; ++i) ring[i % D] = operand(i);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = I0; i < 36; ++i) {
-      const bf16x8 bq = i < 32 ? q[i & 31] : rq[(i + 3 * D - 32) % D];
-      if (i == 0) sacc = mfma_sv0(ring[i % D], bq);
-      else mfma_sv(sacc, ring[i % D], bq);
-      ring[i % D] = operand(i + D);
-      // rotary query blocks, D MFMAs ahead of their use
-      if (i >= 32 - D && i < 36 - D) rq[(i + D - 32) % D] = rq_operand(i + D - 32);
-      after_s(i);
+    bf16x8 A[2], B[4];
+    // weighted-latent operands fetched before its first MFMA, in order of need
+    auto pre = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i == 0) A[0] = a_read(t0, t1, std::integral_constant<int, 0>{});
+      else if constexpr (i <= 4) B[i - 1] = b_read(pb, i - 1, std::integral_constant<int, 0>{});
+      else A[1] = a_read(t0, t1, std::integral_constant<int, 1>{});
+    };
+    constexpr int kPre = 6;
+    if constexpr (HAS_S) {
+      bf16x8 ring[kD];
+      f32x16 sacc;
+      static_for<0, kD>([&](auto ic) { ring[decltype(ic)::value] = s_read(sb, rb, ic); });
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (HAS_S) {
+      static_for<0, 36>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const bf16x8 bq = i < 32 ? q[i & 31] : qr[(i - 32) & 3];
+        if constexpr (i == 0) sacc = mfma_sv0(ring[0], bq);
+        else mfma_sv(sacc, ring[i % kD], bq);
+        if constexpr (i + kD < 36) ring[i % kD] = s_read(sb, rb, std::integral_constant<int, i + kD>{});
+        else if constexpr (i + kD - 36 < kPre) pre(std::integral_constant<int, i + kD - 36>{});
+        after_s(i);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      static_for<kD, kPre>([&](auto ic) { pre(ic); });
       // the last score MFMA's result is read by VALU instructions: cover the
       // MFMA-write -> VALU-read distance (at most 19 wait states)
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(sacc));
       s = sacc;
+    } else {
+      static_for<0, kPre>([&](auto ic) { pre(ic); });
     }
-#pragma unroll
-    for (int i = 36; i < 68; ++i) {
-      const int j = i - 36;
-      O[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % D], (j >> 4) ? P1 : P0, O[j & 15], 0, 0, 0);
-      if (i + D < 68) ring[i % D] = operand(i + D);
-      if (i > 36) piece(i - 37);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, 32>([&](auto jc) {
+      constexpr int j = decltype(jc)::value, kb2 = j >> 4, mbl = (j >> 2) & 3, nb = j & 3;
+      constexpr int st = 4 * kb2 + mbl;
+      O[4 * mbl + nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[st & 1], B[nb], O[4 * mbl + nb], 0, 0, 0);
+      // B operand (nb, 1) replaces (nb, 0) after its last use, then A operand
+      // st + 2 replaces st after its last use (the B operand is needed first)
+      if constexpr (j >= 12 && j < 16) B[nb] = b_read(pb, nb, std::integral_constant<int, 1>{});
+      if constexpr (nb == 3 && st + 2 < 8) A[st & 1] = a_read(t0, t1, std::integral_constant<int, st + 2>{});
+      if constexpr (j > 0) piece(j - 1);
       __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // rescale factors of tile tt (written by the owners in its iteration)
+  auto alpha_of = [&](int32_t tt) __attribute__((always_inline)) -> f32x4 { return *(const LDS f32x4*)(L + kAOff + (tt & 1) * 512 + 16 * row); };
+  // rescale the accumulator by the factors of the previous tile, if any is not 1
+  auto rescale = [&](const f32x4& al) __attribute__((always_inline)) {
+    const bool mine = al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f;
+    if (__builtin_amdgcn_ballot_w64(mine) != 0) {
+#pragma unroll
+      for (int b = 0; b < 16; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[b][r] = scale_acc(O[b][r], al[b & 3]);
     }
   };
 
@@ -253,88 +393,83 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     // earlier stores and loads count on vmcnt too, so drain first.
     wait_vmcnt<0>();
     __syncthreads();
-    // Page ids are fetched one tile ahead of the load that needs them.  No
-    // tile is loaded past the segment end, so nothing is left in flight when
-    // the segment's result is written.  The page ids of the first two tiles
-    // go out first; while they are in flight the queries are requested (the
-    // latent queries into registers, the rotary queries straight into LDS),
-    // then the two tiles; all of it lands before the loop, in one round trip
-    // after the page ids.
+    // Page ids are fetched one tile ahead of the load that needs them.  The
+    // page ids of the first two tiles go out first; while they are in flight
+    // the queries are requested into registers, then the two tiles; all of it
+    // lands before the loop, in one round trip after the page ids.
     const int32_t raw_a = ld.raw(ct >> 1);                                  // tile ct
     const int32_t raw_b = ld.raw(seg > 1 ? (ct + 1) >> 1 : 0);             // tile ct + 1
     {
       const __bf16* ql = (const __bf16*)a.q_lat + ((int64_t)cb * kHeads + head) * kLatent + 8 * hi;
 #pragma unroll
       for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8*)(ql + 16 * kb);
-      // rotary queries: rows 32 w + 8 p .. + 7 per load, lane l bringing the
-      // chunk that LDS position l % 8 of its row holds (rows swizzled like
-      // the rotary keys)
-      const __bf16* qp = (const __bf16*)a.q_rope + (int64_t)cb * kHeads * kRope;
+      const __bf16* qp = (const __bf16*)a.q_rope + ((int64_t)cb * kHeads + head) * kRope + 8 * hi;
 #pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        const int hh = 32 * w + 8 * pass + (lane >> 3);
-        const int c = (lane & 7) ^ swz_r(hh);
-        dma16(qp + hh * kRope + 8 * c, ld.lds_base + kQrOff + (32 * w + 8 * pass) * kRRow);
-      }
+      for (int v = 0; v < 4; ++v) qr[v] = *(const bf16x8*)(qp + 16 * v);
     }
     const int32_t pg_a = ld.checked(ct >> 1, raw_a);
     const int32_t pg_b = seg > 1 ? ld.checked((ct + 1) >> 1, raw_b) : -1;
-    ld.issue(0, ct, pg_a);
-    if (seg > 1) ld.issue(1, ct + 1, pg_b);
+    ld.issue(ld.tile(0, 0, ct, pg_a));
+    if (seg > 1) ld.issue(ld.tile(1, 1, ct + 1, pg_b));
     // page of tile ct + 2: loaded now, checked when its load is issued
     int32_t pg_next_p = seg > 2 ? (ct + 2) >> 1 : INT32_MAX;
     int32_t pg_next_raw = ld.raw(seg > 2 ? pg_next_p : 0);
-    // validity of the tiles in flight, by stage: tile ct + j has stage j % 4
+    // validity of the tiles in flight: tile ct + j has latent stage j % 4
+    // and rotary stage j % 3
     bool valid_j = pg_a >= 0, valid_j1 = pg_b >= 0;
     {
-      // The weighted latent of "tile -1" reads stage 3 with zero
-      // probabilities; zero its latent rows so stale or uninitialised LDS
+      // The weighted latent of "tile -1" reads latent stage 3 with the
+      // probabilities of buffer 1: zero both, so stale or uninitialised LDS
       // cannot turn 0 x NaN into NaN.  Ordered before the first read by the
       // barrier of iteration 0.
-      LDS char* dst = L + 3 * kStage + (tid >> 3) * kCRow + 128 * (tid & 7);
+      LDS char* dst = L + 3 * kLStage + (tid >> 3) * kCRow + 128 * (tid & 7);
 #pragma unroll
       for (int v = 0; v < 8; ++v) *(LDS i32x4*)(dst + 16 * v) = i32x4{0, 0, 0, 0};
+      LDS char* pz = L + kPOff + kPBytes + 32 * tid;
+      *(LDS i32x4*)pz = i32x4{0, 0, 0, 0};
+      *(LDS i32x4*)(pz + 16) = i32x4{0, 0, 0, 0};
     }
     wait_vmcnt<0>();  // queries and the first two tiles
-    // take the latent queries here, so the waits for them sit before the
-    // tile loop (all satisfied) and not inside it
+    // take the queries here, so the waits for them sit before the tile loop
+    // (all satisfied) and not inside it
 #pragma unroll
     for (int kb = 0; kb < 32; ++kb) asm volatile("" ::"v"(q[kb]));
-
+#pragma unroll
+    for (int v = 0; v < 4; ++v) asm volatile("" ::"v"(qr[v]));
 
 #pragma unroll
-    for (int mb = 0; mb < 16; ++mb) O[mb] = f32x16{};
+    for (int b = 0; b < 16; ++b) O[b] = f32x16{};
     float m_run = -INFINITY;  // running maximum of this lane's head (log2 units)
     float l_run = 0.f;        // this lane's share of the running sum
-    bf16x8 Pp0, Pp1;          // probabilities of the previous tile
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      Pp0[r] = (__bf16)0.f;
-      Pp1[r] = (__bf16)0.f;
-    }
+    int rs = 0;               // rotary stage of tile j
 
     for (int32_t j = 0; j < seg; ++j) {
       const int32_t t = ct + j;
-      // tile j landed (tile j + 1, if the segment has it, may still be in
-      // flight)
-      if (j + 1 < seg) wait_vmcnt<kDmaPerWave>();
-      else wait_vmcnt<0>();
+      // tile j landed (the loads of tile j + 1 may still be in flight)
+      wait_vmcnt<kDmaPerWave>();
       __syncthreads();
-      // stage (j + 2) % 4 held tile j - 2, consumed in the previous
-      // iteration; tile j + 2 is loaded into it during the scores below
+      // stages (j + 2) % 4 and (j + 2) % 3 held tiles j - 2 and j - 1,
+      // whose last reads were in the previous iteration; tile j + 2 is
+      // loaded into them during the scores below
+      const int rs2 = rs == 0 ? 2 : rs - 1;
       const int32_t pg_next = ld.checked(pg_next_p, pg_next_raw);
       const bool valid_j2 = pg_next >= 0;
-      const TileLoader::Tile next_tile = ld.tile((j + 2) & 3, t + 2, pg_next);
-      const bool has_next = j + 2 < seg;
+      // Past the segment's end the same loads bring page 0 into the free
+      // stages: every iteration issues the same instructions, with no branch
+      // (the end of the segment waits for them before its stores).
+      const TileLoader::Tile next_tile = ld.tile((j + 2) & 3, rs2, t + 2, pg_next);
       pg_next_p = j + 3 < seg ? (t + 3) >> 1 : INT32_MAX;
       pg_next_raw = ld.raw(j + 3 < seg ? pg_next_p : 0);
+      // rescale factors of tile j - 1 (none before tile 0)
+      const f32x4 al_prev = alpha_of(j + 1);
       // rows of tile j that are visible
       const int32_t nvis = valid_j ? (T - t * kTile < kTile ? T - t * kTile : kTile) : 0;
       const bool full = nvis == kTile;
       if (!full) {
-        // zero the invisible rows (they hold page-0 or past-the-end data,
-        // which a zero probability must not turn into NaN)
-        LDS char* Ct = L + (j & 3) * kStage;
+        // zero the invisible latent rows (they hold page-0 or past-the-end
+        // data, which a zero probability must not turn into NaN); their
+        // scores are masked below, so the rotary rows may stay
+        LDS char* Ct = L + (j & 3) * kLStage;
         const int r = tid >> 3, qq = tid & 7;
         if (r >= nvis) {
           LDS char* dst = Ct + r * kCRow + 128 * qq;
@@ -348,10 +483,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
 
       // ---- softmax of tile j, in pieces, inside the weighted latent of tile j - 1 ----
       f32x16 s;  // scores, then probabilities, of tile j
-      float mt = -INFINITY, m_use = m_run, neg_m = 0.f, lsum = 0.f;
+      float mt = -INFINITY, m_use = m_run, neg_m = 0.f, lsum = 0.f, alpha = 1.f;
       bool need = false;
       bf16x8 Pc0, Pc1;
-      auto piece = [&](int k) {
+      const uint32_t pw = lds0 + kPOff + (j & 1) * kPBytes + bp + 2048 * w;  // this lane's probability row
+      auto piece = [&](int k) __attribute__((always_inline)) {
         // Each step ends with an empty asm that takes its result: code motion
         // cannot then sink the VALU work past the MFMAs that hide it.
         if (k == 0) {
@@ -380,12 +516,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
           m_use = need ? m_new : m_run;
           neg_m = (m_use == -INFINITY) ? 0.f : -m_use;
           asm volatile("" : "+v"(neg_m), "+v"(m_use));
-        } else if (k >= 4 && k < 20) {
-          const int r = k - 4;
+        } else if (k == 4) {
+          // factor that takes sums relative to m_run to m_use; every wave
+          // applies it to its columns of this head before the next tile's
+          // weighted latent
+          alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
+          *(LDS float*)(L + kAOff + (j & 1) * 512 + 4 * head_slot(head)) = alpha;
+        } else if (k >= 5 && k < 21) {
+          const int r = k - 5;
           s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, neg_m));
           asm volatile("" : "+v"(s[r]));
-        } else if (k >= 20 && k < 28) {
-          const int r = 2 * (k - 20);
+        } else if (k >= 21 && k < 29) {
+          const int r = 2 * (k - 21);
           lsum += s[r] + s[r + 1];
           if (r < 8) {
             Pc0[r] = (__bf16)s[r];
@@ -395,34 +537,38 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
             Pc1[r - 7] = (__bf16)s[r + 1];
           }
           asm volatile("" : "+v"(lsum));
-          if (k == 23) asm volatile("" : "+v"(Pc0));
-          if (k == 27) asm volatile("" : "+v"(Pc1));
+          if (k == 24) asm volatile("" : "+v"(Pc0));
+          if (k == 28) asm volatile("" : "+v"(Pc1));
+        } else if (k == 29) {
+          *(LDS bf16x8*)(LDS char*)(uintptr_t)pw = Pc0;
+        } else if (k == 30) {
+          *(LDS bf16x8*)(LDS char*)(uintptr_t)xor_here<32>(pw) = Pc1;
         }
       };
-      stream(std::true_type{}, j & 3, (j + 3) & 3, Pp0, Pp1, s,
+      stream(std::true_type{}, lds0 + (j & 3) * kLStage + bs, lds0 + kROff + rs * kRStage + br,
+             lds0 + ((j + 3) & 3) * kLStage + bt0, lds0 + ((j + 3) & 3) * kLStage + bt1,
+             lds0 + kPOff + ((j + 1) & 1) * kPBytes + bp, s,
              [&](int k) {
-               if (has_next && (k & 3) == 0 && (k >> 2) < kDmaPerWave) ld.issue_one(next_tile, k >> 2);
+               if ((k & 3) == 0 && (k >> 2) < kDmaPerWave) ld.issue_one(next_tile, k >> 2);
+             },
+             [&]() {
+               if (j > 0) rescale(al_prev);
              },
              piece);
 
-      // rescale what the accumulator holds (tiles up to j - 1) to the new reference
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
-        l_run *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < 16; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
-      }
       m_run = m_use;
-      l_run += lsum;
-      Pp0 = Pc0;
-      Pp1 = Pc1;
+      l_run = l_run * alpha + lsum;
+      rs = rs == 2 ? 0 : rs + 1;
     }
     {
-      // weighted latent of the last tile
+      // weighted latent of the last tile, after its rescale; the barrier
+      // makes every owner's probabilities and factors of that tile visible
+      __syncthreads();
+      const f32x4 al_last = alpha_of(seg - 1);
       f32x16 s_unused;
-      stream(std::false_type{}, 0, (seg + 3) & 3, Pp0, Pp1, s_unused, [](int) {}, [](int) {});
+      stream(std::false_type{}, 0u, 0u, lds0 + ((seg + 3) & 3) * kLStage + bt0,
+             lds0 + ((seg + 3) & 3) * kLStage + bt1, lds0 + kPOff + ((seg + 1) & 1) * kPBytes + bp, s_unused,
+             [](int) {}, [&]() { rescale(al_last); }, [](int) {});
     }
     done += seg;
 
@@ -431,13 +577,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
       const float l_tot = l_run + wave_partner(l_run);
       const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
       const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-      // BF16 rows of this wave's 32 heads (the final o_lat, or the partial:
-      // partials of the MFMA kernels are BF16), staged through LDS so that
-      // every global store writes one contiguous 1 KiB row
+      *(LDS float*)(L + kIOff + 4 * head_slot(head)) = inv;
+      // BF16 rows of all 128 heads (the final o_lat, or the partial:
+      // partials of the MFMA kernels are BF16)
       const int64_t slot = worker + cb;
       __bf16* rows = DIRECT ? (__bf16*)a.o_lat + (int64_t)cb * kHeads * kLatent
                             : (__bf16*)a.part_o + slot * kHeads * kLatent;
-      store_rows_staged(L, rows + (int64_t)32 * w * kLatent, O, inv, w);
+      store_rows_split(L, rows, O, w);
       if (DIRECT) {
         if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
       } else {

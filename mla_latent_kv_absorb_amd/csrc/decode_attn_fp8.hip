@@ -105,19 +105,6 @@ struct Fp8Offsets {
   }
 };
 
-// a ^ K, computed where it is used: the compiler cannot keep one register per
-// K alive across the tile loop
-template <int K>
-__device__ __forceinline__ uint32_t xor_here(uint32_t a) {
-  if constexpr (K == 0) {
-    return a;
-  } else {
-    uint32_t r;
-    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(K), "v"(a));
-    return r;
-  }
-}
-
 template <bool TOPK>
 struct Fp8Loader {
   using C = Fp8Cfg<TOPK>;

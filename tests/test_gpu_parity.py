@@ -205,15 +205,21 @@ def test_v2_page_order_is_bit_identical(torch, R, v2_ragged):
         assert torch.equal(x, y)
 
 
-def test_v2_repeat_runs_bit_identical(torch, R, v2_ragged):
-    _log("determinism")
-    w = R.DeviceWorkload(v2_ragged, split=True)
+@pytest.mark.parametrize("case", ["ragged", "many_segments", "many_segments_direct"])
+def test_v2_repeat_runs_bit_identical(torch, R, v2_ragged, case):
+    """Every work-group exchanges probabilities and rescale factors between
+    its waves through LDS: a missing barrier shows up as results that change
+    from run to run.  Many segments per work-group and long ones, split and
+    direct."""
+    _log(f"determinism {case}")
+    inp = v2_ragged if case == "ragged" else I.make_inputs("v2_batched", seed=71, batch=12, ctx=(3000, 9000))
+    w = R.DeviceWorkload(inp, split=case != "many_segments_direct")
     w.step()
-    a = (w.o_lat.clone(), w.out.clone())
-    for _ in range(3):
+    a = (w.o_lat.clone(), w.out.clone(), w.lse.clone())
+    for _ in range(4):
         w.step()
-    torch.cuda.synchronize()
-    assert torch.equal(a[0], w.o_lat) and torch.equal(a[1], w.out)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], w.o_lat) and torch.equal(a[1], w.out) and torch.equal(a[2], w.lse)
 
 
 def test_v2_absorb_and_up_projection_alone(torch, R, v2_ragged):
