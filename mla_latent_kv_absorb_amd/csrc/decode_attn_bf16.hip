@@ -268,11 +268,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
   bf16x8 q[32];  // latent queries of this lane's head
   bf16x8 qr[4];  // rotary queries of this lane's head
 
-  // score K-block k < 32 (latent) of the stage at sb, or rotary block k - 32 at rb
-  auto s_read = [&](uint32_t sb, uint32_t rb, auto kc) __attribute__((always_inline)) -> bf16x8 {
+  // score K-block k < 32 (latent) of a tile whose eight latent read
+  // addresses are sa (sa[v]: the lane's base ^ 32 v; the column group k / 8
+  // goes in the offset field), or rotary block k - 32 at rb
+  auto s_read = [&](const uint32_t (&sa)[8], uint32_t rb, auto kc) __attribute__((always_inline)) -> bf16x8 {
     constexpr int k = decltype(kc)::value;
     if constexpr (k < 32)
-      return *(const LDS bf16x8*)((LDS char*)(uintptr_t)xor_here<32 * (k & 7)>(sb) + 256 * (k >> 3));
+      return *(const LDS bf16x8*)((LDS char*)(uintptr_t)sa[k & 7] + 256 * (k >> 3));
     else
       return *(const LDS bf16x8*)(LDS char*)(uintptr_t)xor_here<32 * (k - 32)>(rb);
   };
@@ -310,25 +312,40 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
                     auto&& after_s, auto&& mid, auto&& piece) __attribute__((always_inline)) {
     constexpr bool HAS_S = decltype(has_s)::value;
     bf16x8 A[2], B[4];
+    uint32_t ta0[4], ta1[4];  // transposed-read addresses of column block mbl (half 0; half 1 at +16 KiB)
+    uint32_t pb1 = 0;         // probability read address of position half 1
+    auto ar = [&](auto stc) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int st = decltype(stc)::value, mbl = st & 3, kb2 = st >> 2;
+      if constexpr (kb2 == 0) {
+        ta0[mbl] = xor_here<64 * mbl>(t0);
+        ta1[mbl] = xor_here<64 * mbl>(t1);
+      }
+      s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)((LDS char*)(uintptr_t)ta0[mbl] + 16 * kCRow * kb2));
+      s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)((LDS char*)(uintptr_t)ta1[mbl] + 16 * kCRow * kb2));
+      typedef __attribute__((ext_vector_type(8))) short s16x8;
+      return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     // weighted-latent operands fetched before its first MFMA, in order of need
     auto pre = [&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if constexpr (i == 0) A[0] = a_read(t0, t1, std::integral_constant<int, 0>{});
+      if constexpr (i == 0) A[0] = ar(std::integral_constant<int, 0>{});
       else if constexpr (i <= 4) B[i - 1] = b_read(pb, i - 1, std::integral_constant<int, 0>{});
-      else A[1] = a_read(t0, t1, std::integral_constant<int, 1>{});
+      else A[1] = ar(std::integral_constant<int, 1>{});
     };
     constexpr int kPre = 6;
     if constexpr (HAS_S) {
       bf16x8 ring[kD];
       f32x16 sacc;
-      static_for<0, kD>([&](auto ic) { ring[decltype(ic)::value] = s_read(sb, rb, ic); });
+      uint32_t sa[8];
+      static_for<0, 8>([&](auto vc) { sa[decltype(vc)::value] = xor_here<32 * decltype(vc)::value>(sb); });
+      static_for<0, kD>([&](auto ic) { ring[decltype(ic)::value] = s_read(sa, rb, ic); });
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, 36>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         const bf16x8 bq = i < 32 ? q[i & 31] : qr[(i - 32) & 3];
         if constexpr (i == 0) sacc = mfma_sv0(ring[0], bq);
         else mfma_sv(sacc, ring[i % kD], bq);
-        if constexpr (i + kD < 36) ring[i % kD] = s_read(sb, rb, std::integral_constant<int, i + kD>{});
+        if constexpr (i + kD < 36) ring[i % kD] = s_read(sa, rb, std::integral_constant<int, i + kD>{});
         else if constexpr (i + kD - 36 < kPre) pre(std::integral_constant<int, i + kD - 36>{});
         after_s(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -349,8 +366,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
       O[4 * mbl + nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[st & 1], B[nb], O[4 * mbl + nb], 0, 0, 0);
       // B operand (nb, 1) replaces (nb, 0) after its last use, then A operand
       // st + 2 replaces st after its last use (the B operand is needed first)
-      if constexpr (j >= 12 && j < 16) B[nb] = b_read(pb, nb, std::integral_constant<int, 1>{});
-      if constexpr (nb == 3 && st + 2 < 8) A[st & 1] = a_read(t0, t1, std::integral_constant<int, st + 2>{});
+      if constexpr (j == 12) pb1 = xor_here<32>(pb);
+      if constexpr (j >= 12 && j < 16) B[nb] = *(const LDS bf16x8*)((LDS char*)(uintptr_t)pb1 + 2048 * nb);
+      if constexpr (nb == 3 && st + 2 < 8) A[st & 1] = ar(std::integral_constant<int, st + 2>{});
       if constexpr (j > 0) piece(j - 1);
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -509,10 +527,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
           asm volatile("" : "+v"(mt));
         } else if (k == 3) {
           // Lazy rescale: keep the reference maximum unless the tile's
-          // maximum exceeds it by more than 8 (log2 units), so probabilities
-          // stay <= 256 and the accumulator is rescaled rarely.
+          // maximum exceeds it by more than 16 (log2 units): probabilities
+          // stay <= 2^16, far inside the range of BF16 and of the float32
+          // sums, and the accumulator (all 128 heads in every wave) is
+          // rescaled rarely.
           const float m_new = max_raw(m_run, mt);
-          need = m_new > m_run + 8.0f;
+          need = m_new > m_run + 16.0f;
           m_use = need ? m_new : m_run;
           neg_m = (m_use == -INFINITY) ? 0.f : -m_use;
           asm volatile("" : "+v"(neg_m), "+v"(m_use));
@@ -552,7 +572,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
                if ((k & 3) == 0 && (k >> 2) < kDmaPerWave) ld.issue_one(next_tile, k >> 2);
              },
              [&]() {
-               if (j > 0) rescale(al_prev);
+               // (through tile 0 the accumulator holds only the zero
+               // weighted latent of "tile -1": nothing to rescale)
+               if (j > 1) rescale(al_prev);
              },
              piece);
 
@@ -568,7 +590,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
       f32x16 s_unused;
       stream(std::false_type{}, 0u, 0u, lds0 + ((seg + 3) & 3) * kLStage + bt0,
              lds0 + ((seg + 3) & 3) * kLStage + bt1, lds0 + kPOff + ((seg + 1) & 1) * kPBytes + bp, s_unused,
-             [](int) {}, [&]() { rescale(al_last); }, [](int) {});
+             [](int) {}, [&]() {
+               if (seg > 1) rescale(al_last);
+             },
+             [](int) {});
     }
     done += seg;
 
