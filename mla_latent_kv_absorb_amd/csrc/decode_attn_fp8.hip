@@ -547,9 +547,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
             asm volatile("" : "+v"(mt));
           } else if (k == 3) {
             // Lazy rescale: keep the reference maximum unless the tile's
-            // maximum exceeds it by more than 8 (log2 units).
+            // maximum exceeds it by more than 16 (log2 units): probabilities
+            // stay <= 2^16 (times a row scale), far inside the range of BF16
+            // and of the float32 sums.
             const float m_new = max_raw(m_run, mt);
-            need = m_new > m_run + 8.0f;
+            need = m_new > m_run + 16.0f;
             m_use = need ? m_new : m_run;
             neg_m = (m_use == -INFINITY) ? 0.f : -m_use;
             asm volatile("" : "+v"(neg_m), "+v"(m_use));
@@ -590,14 +592,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
           if (lane == 0) L[C::MASK_OFF + 4 * nst + w] = (char)dnext.bits;
         }
 
-        // rescale what the accumulator holds (tiles up to j - 1) to the new reference
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        // rescale what the accumulator holds (tiles up to j - 1) to the new
+        // reference; a head whose maximum is still -inf has only zeros there
+        // (all its probabilities so far were 0), so the first tile of a
+        // segment never needs the accumulator pass
+        {
           const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
           l_run *= alpha;
+          if (__builtin_amdgcn_ballot_w64(need && m_run != -INFINITY) != 0) {
 #pragma unroll
-          for (int mb = 0; mb < 16; ++mb)
+            for (int mb = 0; mb < 16; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
+              for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
+          }
         }
         m_run = m_use;
         l_run += lsum;

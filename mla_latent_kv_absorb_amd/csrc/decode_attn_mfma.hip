@@ -435,16 +435,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         mloc = fmaxf(mloc, wave_partner(mloc)) * scale_log2;
         const float m_new = fmaxf(m_run, mloc);
         // Rescale lazily: keep the old reference maximum unless the new one
-        // exceeds it by more than 8 (log2 units), so probabilities stay <= 256.
-        const bool need = m_new > m_run + 8.0f;
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        // exceeds it by more than 16 (log2 units), so probabilities stay
+        // <= 2^16, far inside the range of BF16 and of the float32 sums.  A
+        // head whose maximum is still -inf has only zeros in the accumulator
+        // (all its probabilities so far were 0): the first tile of a segment
+        // never needs the accumulator pass.
+        const bool need = m_new > m_run + 16.0f;
+        {
           const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+          const bool held = m_run != -INFINITY;
           m_run = need ? m_new : m_run;
           l_run *= alpha;
+          if (__builtin_amdgcn_ballot_w64(need && held) != 0) {
 #pragma unroll
-          for (int mb = 0; mb < 16; ++mb)
+            for (int mb = 0; mb < 16; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
+              for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
+          }
         }
         const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
         float lsum = 0.f;
