@@ -57,6 +57,7 @@ constexpr int kAOff = kPOff + 2 * kPBytes;       // rescale factors, 2 x [128] f
 constexpr int kIOff = kAOff + 2 * kHeads * 4;    // 1 / row sum at a segment's end, [128] float
 constexpr int kLdsBytes = kIOff + kHeads * 4;    // 157.5 KiB
 constexpr int kDmaPerWave = 9;                   // 8 latent rows + 1 rotary block per wave and tile
+constexpr int kQOff = 2 * kLStage;               // query staging at a segment's start (stages 2, 3)
 constexpr int kPitch = kCRow + 16;               // staging rows of the output (padded: spread over banks)
 constexpr int kD = 4;                            // score operands fetched ahead of their MFMA
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
@@ -387,6 +388,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     }
   };
 
+  // Latent queries reach the registers through LDS, in two halves (latent
+  // dims 0..255, then 256..511): a load straight into the operand layout
+  // would touch 32 rows of 32 bytes per instruction, while each load here
+  // moves two whole half rows.  Wave w stages its own 32 heads' half rows
+  // ([head][512 bytes], chunks swizzled like the latent rows) at kQOff +
+  // 16 KiB w, inside latent stages 2 and 3, which the first two tiles
+  // leave free; only wave w reads them back, so no barrier is needed.
+  // lanes 0..31 fetch head 32 w + 2 i, lanes 32..63 head 32 w + 2 i + 1,
+  // lane chunk c the row's chunk c ^ swz(head); swz(2 i + 1) is swz(2 i)
+  // with bit 2 set, so the per-lane offset is qd ^ 16 swz(2 i)
+  const uint32_t qd = ((uint32_t)hi << 10) | ((16 * (lane & 31)) ^ (64 * hi));
+  auto q_half = [&](int r, int32_t b) __attribute__((always_inline)) {
+    const uint8_t* base = (const uint8_t*)a.q_lat + ((int64_t)b * kHeads + 32 * w) * kCRow + 512 * r;
+    static_for<0, 16>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      dma16s(xor_here<16 * swz(2 * i)>(qd), base + 2 * i * kCRow, lds0 + kQOff + (32 * w + 2 * i) * 512);
+    });
+  };
+  const uint32_t qb = lds0 + kQOff + (32 * w + row) * 512 + (bs - row * kCRow);
+  auto q_take = [&](auto rc) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    uint32_t qa[8];
+    static_for<0, 8>([&](auto vc) { qa[decltype(vc)::value] = xor_here<32 * decltype(vc)::value>(qb); });
+    static_for<0, 16>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      q[16 * r + k] = *(const LDS bf16x8*)((LDS char*)(uintptr_t)qa[k & 7] + 256 * (k >> 3));
+    });
+  };
+
   int32_t cb = b0;
   int64_t cv = v0;   // offset of the next unit inside request cb's span
   int64_t done = 0;  // units consumed
@@ -412,15 +442,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     wait_vmcnt<0>();
     __syncthreads();
     // Page ids are fetched one tile ahead of the load that needs them.  The
-    // page ids of the first two tiles go out first; while they are in flight
-    // the queries are requested into registers, then the two tiles; all of it
-    // lands before the loop, in one round trip after the page ids.
+    // page ids of the first two tiles go out first, then the first half of
+    // the latent queries (see q_half) and the rotary queries; the two tiles
+    // follow as soon as their page ids are in.
     const int32_t raw_a = ld.raw(ct >> 1);                                  // tile ct
     const int32_t raw_b = ld.raw(seg > 1 ? (ct + 1) >> 1 : 0);             // tile ct + 1
+    q_half(0, cb);
     {
-      const __bf16* ql = (const __bf16*)a.q_lat + ((int64_t)cb * kHeads + head) * kLatent + 8 * hi;
-#pragma unroll
-      for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8*)(ql + 16 * kb);
       const __bf16* qp = (const __bf16*)a.q_rope + ((int64_t)cb * kHeads + head) * kRope + 8 * hi;
 #pragma unroll
       for (int v = 0; v < 4; ++v) qr[v] = *(const bf16x8*)(qp + 16 * v);
@@ -429,6 +457,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     const int32_t pg_b = seg > 1 ? ld.checked((ct + 1) >> 1, raw_b) : -1;
     ld.issue(ld.tile(0, 0, ct, pg_a));
     if (seg > 1) ld.issue(ld.tile(1, 1, ct + 1, pg_b));
+    // the first query half has landed once at most the rotary queries and
+    // the tile loads are in flight; its reads must be done before the second
+    // half overwrites the area
+    if (seg > 1) wait_vmcnt<4 + 2 * kDmaPerWave>();
+    else wait_vmcnt<4 + kDmaPerWave>();
+    q_take(std::integral_constant<int, 0>{});
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    q_half(1, cb);
     // page of tile ct + 2: loaded now, checked when its load is issued
     int32_t pg_next_p = seg > 2 ? (ct + 2) >> 1 : INT32_MAX;
     int32_t pg_next_raw = ld.raw(seg > 2 ? pg_next_p : 0);
@@ -437,23 +473,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     bool valid_j = pg_a >= 0, valid_j1 = pg_b >= 0;
     {
       // The weighted latent of "tile -1" reads latent stage 3 with the
-      // probabilities of buffer 1: zero both, so stale or uninitialised LDS
-      // cannot turn 0 x NaN into NaN.  Ordered before the first read by the
-      // barrier of iteration 0.
-      LDS char* dst = L + 3 * kLStage + (tid >> 3) * kCRow + 128 * (tid & 7);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) *(LDS i32x4*)(dst + 16 * v) = i32x4{0, 0, 0, 0};
+      // probabilities of buffer 1: zero both (stage 3 below, once the query
+      // rows staged there are read), so stale or uninitialised LDS cannot
+      // turn 0 x NaN into NaN.  Ordered before the first read by the barrier
+      // of iteration 0.
       LDS char* pz = L + kPOff + kPBytes + 32 * tid;
       *(LDS i32x4*)pz = i32x4{0, 0, 0, 0};
       *(LDS i32x4*)(pz + 16) = i32x4{0, 0, 0, 0};
     }
     wait_vmcnt<0>();  // queries and the first two tiles
+    q_take(std::integral_constant<int, 1>{});
     // take the queries here, so the waits for them sit before the tile loop
     // (all satisfied) and not inside it
 #pragma unroll
     for (int kb = 0; kb < 32; ++kb) asm volatile("" ::"v"(q[kb]));
 #pragma unroll
     for (int v = 0; v < 4; ++v) asm volatile("" ::"v"(qr[v]));
+    if (w >= 2) {
+      // latent stage 3 held the query rows of waves 2 and 3: each zeroes its
+      // own half, after its reads (one wave's LDS operations run in order)
+      LDS char* z = L + 3 * kLStage + (w - 2) * (kLStage / 2) + 16 * lane;
+#pragma unroll
+      for (int v = 0; v < kLStage / 2 / 1024; ++v) *(LDS i32x4*)(z + 1024 * v) = i32x4{0, 0, 0, 0};
+    }
 
 #pragma unroll
     for (int b = 0; b < 16; ++b) O[b] = f32x16{};
