@@ -150,6 +150,73 @@ __device__ __forceinline__ void store_rows_staged(LDS char* L, __bf16* dst, cons
     *(i32x4*)(dst + r * kLatent + 8 * lane) = *(const LDS i32x4*)(mine + r * kPitch + 16 * lane);
 }
 
+// ---- split-column weighted latent (wave w accumulates latent columns
+// 128 w .. 128 w + 127 for all 128 heads; the heads' owners share their
+// probabilities, rescale factors and row sums through LDS) ----
+
+// Per-head values that every wave reads (rescale factors, 1 / row sums) are
+// stored with head 32 nb + r at float 4 r + nb: lane r reads its four heads
+// with one 16-byte read.
+__device__ __forceinline__ constexpr int head_slot(int head) { return 4 * (head & 31) + (head >> 5); }
+
+// Probability rows: chunk c (16 bytes) of head h is stored at chunk
+// c ^ pswz(h), so that 16 consecutive heads of one chunk column touch
+// distinct banks (64-bank and 32-bank LDS alike).
+__device__ __forceinline__ constexpr int pswz(int h) { return ((h >> 1) & 3) ^ ((h >> 3) & 1); }
+
+constexpr int kSplitPitch = kCRow + 16;                 // output staging rows (padded: spread over banks)
+constexpr int kSplitStage = kHeads * kSplitPitch;       // bytes of the output staging
+
+// Normalised accumulator of this wave's latent quarter for all 128 heads as
+// BF16 rows [128][512] at dst.  The rows are assembled in LDS (the latent and
+// rotary stages, free once every tile has landed and every wave is past its
+// last read, which the first barrier provides), then every wave writes 32
+// whole rows with 1 KiB stores.  The 1 / row sums come from the heads'
+// owners through the float array at inv_off ([128], head_slot order),
+// written before the call; the rows are assembled in the first kSplitStage
+// bytes of the work-group's LDS.
+__device__ __forceinline__ void store_rows_split(LDS char* L, int inv_off, __bf16* dst, const f32x16 (&O)[16],
+                                                 int w) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  const int lane = __lane_id();
+  const int hi = lane >> 5, row = lane & 31;
+  const f32x4 inv = *(const LDS f32x4*)(L + inv_off + 16 * row);
+  // lane (row, hi) of block (mbl, nb) holds head 32 nb + row, latent columns
+  // 32 (4 w + mbl) + 8 g + 4 hi + e; the two lanes of a head swap half of each
+  // group pair so each writes 16 contiguous bytes
+#pragma unroll
+  for (int mbl = 0; mbl < 4; ++mbl)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x16& o = O[4 * mbl + nb];
+      LDS char* rowL = L + (32 * nb + row) * kSplitPitch + 2 * 32 * (4 * w + mbl);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int g0 = 2 * k, g1 = 2 * k + 1;
+        uint32_t keep[2], send[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bf16x2 k0 = {(__bf16)(o[4 * g0 + 2 * e] * inv[nb]), (__bf16)(o[4 * g0 + 2 * e + 1] * inv[nb])};
+          const bf16x2 k1 = {(__bf16)(o[4 * g1 + 2 * e] * inv[nb]), (__bf16)(o[4 * g1 + 2 * e + 1] * inv[nb])};
+          const uint32_t u0 = __builtin_bit_cast(uint32_t, k0), u1 = __builtin_bit_cast(uint32_t, k1);
+          keep[e] = hi ? u1 : u0;
+          send[e] = hi ? u0 : u1;
+        }
+        uint32_t recv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) recv[e] = __float_as_uint(wave_partner(__uint_as_float(send[e])));
+        const i32x4 v = hi ? i32x4{(int)recv[0], (int)recv[1], (int)keep[0], (int)keep[1]}
+                           : i32x4{(int)keep[0], (int)keep[1], (int)recv[0], (int)recv[1]};
+        *(LDS i32x4*)(rowL + 2 * 8 * (hi ? g1 : g0)) = v;
+      }
+    }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 32; ++r)
+    *(i32x4*)(dst + (32 * w + r) * kLatent + 8 * lane) = *(const LDS i32x4*)(L + (32 * w + r) * kSplitPitch + 16 * lane);
+}
+
 // x * alpha for an accumulator value, kept in its accumulator register.  The
 // online-softmax rescale runs only when a head's running maximum grows by a
 // large step; writing it this way keeps the register allocator from moving

@@ -58,20 +58,9 @@ constexpr int kIOff = kAOff + 2 * kHeads * 4;    // 1 / row sum at a segment's e
 constexpr int kLdsBytes = kIOff + kHeads * 4;    // 157.5 KiB
 constexpr int kDmaPerWave = 9;                   // 8 latent rows + 1 rotary block per wave and tile
 constexpr int kQOff = 2 * kLStage;               // query staging at a segment's start (stages 2, 3)
-constexpr int kPitch = kCRow + 16;               // staging rows of the output (padded: spread over banks)
 constexpr int kD = 4;                            // score operands fetched ahead of their MFMA
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(kHeads * kPitch <= kPOff, "output staging must stay clear of the probability buffers");
-
-// Per-head values that every wave reads (rescale factors, 1 / row sums) are
-// stored with head 32 nb + r at float 4 r + nb: lane r reads its four heads
-// with one 16-byte read.
-__device__ __forceinline__ constexpr int head_slot(int head) { return 4 * (head & 31) + (head >> 5); }
-
-// Probability rows: chunk c (16 bytes) of head h is stored at chunk
-// c ^ pswz(h), so that 16 consecutive heads of one chunk column touch
-// distinct banks (64-bank and 32-bank LDS alike).
-__device__ __forceinline__ constexpr int pswz(int h) { return ((h >> 1) & 3) ^ ((h >> 3) & 1); }
+static_assert(kSplitStage <= kPOff, "output staging must stay clear of the probability buffers");
 
 struct TileLoader {
   const uint8_t* pool;
@@ -134,53 +123,6 @@ struct TileLoader {
     for (int k = 0; k < kDmaPerWave; ++k) issue_one(tl, k);
   }
 };
-
-// Normalised accumulator of this wave's latent quarter for all 128 heads as
-// BF16 rows [128][512] at dst.  The rows are assembled in LDS (the latent and
-// rotary stages, free once every tile has landed and every wave is past its
-// last read, which the first barrier provides), then every wave writes 32
-// whole rows with 1 KiB stores.  The 1 / row sums come from the heads'
-// owners through kIOff, written before the call.
-__device__ __forceinline__ void store_rows_split(LDS char* L, __bf16* dst, const f32x16 (&O)[16], int w) {
-  wait_vmcnt<0>();
-  __syncthreads();
-  const int lane = __lane_id();
-  const int hi = lane >> 5, row = lane & 31;
-  const f32x4 inv = *(const LDS f32x4*)(L + kIOff + 16 * row);
-  // lane (row, hi) of block (mbl, nb) holds head 32 nb + row, latent columns
-  // 32 (4 w + mbl) + 8 g + 4 hi + e; the two lanes of a head swap half of each
-  // group pair so each writes 16 contiguous bytes
-#pragma unroll
-  for (int mbl = 0; mbl < 4; ++mbl)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const f32x16& o = O[4 * mbl + nb];
-      LDS char* rowL = L + (32 * nb + row) * kPitch + 2 * 32 * (4 * w + mbl);
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int g0 = 2 * k, g1 = 2 * k + 1;
-        uint32_t keep[2], send[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const bf16x2 k0 = {(__bf16)(o[4 * g0 + 2 * e] * inv[nb]), (__bf16)(o[4 * g0 + 2 * e + 1] * inv[nb])};
-          const bf16x2 k1 = {(__bf16)(o[4 * g1 + 2 * e] * inv[nb]), (__bf16)(o[4 * g1 + 2 * e + 1] * inv[nb])};
-          const uint32_t u0 = __builtin_bit_cast(uint32_t, k0), u1 = __builtin_bit_cast(uint32_t, k1);
-          keep[e] = hi ? u1 : u0;
-          send[e] = hi ? u0 : u1;
-        }
-        uint32_t recv[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) recv[e] = __float_as_uint(wave_partner(__uint_as_float(send[e])));
-        const i32x4 v = hi ? i32x4{(int)recv[0], (int)recv[1], (int)keep[0], (int)keep[1]}
-                           : i32x4{(int)keep[0], (int)keep[1], (int)recv[0], (int)recv[1]};
-        *(LDS i32x4*)(rowL + 2 * 8 * (hi ? g1 : g0)) = v;
-      }
-    }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 32; ++r)
-    *(i32x4*)(dst + (32 * w + r) * kLatent + 8 * lane) = *(const LDS i32x4*)(L + (32 * w + r) * kPitch + 16 * lane);
-}
 
 template <bool DIRECT>
 __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) {
@@ -650,7 +592,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
       const int64_t slot = worker + cb;
       __bf16* rows = DIRECT ? (__bf16*)a.o_lat + (int64_t)cb * kHeads * kLatent
                             : (__bf16*)a.part_o + slot * kHeads * kLatent;
-      store_rows_split(L, rows, O, w);
+      store_rows_split(L, kIOff, rows, O, w);
       if (DIRECT) {
         if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
       } else {

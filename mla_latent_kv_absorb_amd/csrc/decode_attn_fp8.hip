@@ -4,19 +4,22 @@
 // cache item, Figure 10 for the selection).
 //
 // Same work split and arithmetic as the BF16 kernel (4 waves per work-group,
-// each owning 32 of the 128 heads; scores S^T[pos][head] = C . q_lat +
-// K_rope . q_rope on MFMA 32x32x16; online softmax with one head per lane;
-// weighted latent U^T += C^T P^T on MFMA; Figures 5 and 6, form (2)), and the
-// same software pipeline: iteration j issues the scores of tile j and the
-// weighted latent of tile j - 1 as one MFMA stream, with the softmax of tile j
-// woven between the MFMAs.
+// each scoring 32 of the 128 heads: S^T[pos][head] = C . q_lat + K_rope .
+// q_rope on MFMA 32x32x16, online softmax with one head per lane; weighted
+// latent U^T += C^T P^T on MFMA, wave w taking latent columns 128 w .. + 127
+// for all 128 heads, with the probabilities and rescale factors of every
+// head passed through LDS; Figures 5 and 6, form (2)), and the same software
+// pipeline: iteration j issues the scores of tile j and the weighted latent
+// of tile j - 1 as one MFMA stream, with the softmax of tile j woven between
+// the MFMAs.
 //
 // The latent rows stay FP8 in LDS and go from the load ring straight into the
 // matrix cores: every MFMA operand is read as FP8 bytes -- 16-byte row reads
 // for the scores (two K-blocks per read), 8-byte transposing reads
 // (ds_read_b64_tr_b8: eight positions of one latent column) for the weighted
-// latent -- and widened to BF16 in registers (v_cvt_scalef32_pk_bf16_fp8 at
-// scale 1, exact: every E4M3 value is a BF16 value).  There is no conversion
+// latent, of this wave's column quarter only -- and widened to BF16 in
+// registers (v_cvt_scalef32_pk_bf16_fp8 at scale 1, exact: every E4M3 value
+// is a BF16 value).  There is no conversion
 // pass, no conversion buffer and no barrier for one.  The position's scale is
 // applied in float32: the latent part of each score is multiplied by it before
 // the rotary part is added, and each probability that weights the row is
@@ -39,7 +42,7 @@ __device__ __forceinline__ constexpr int fswz(int r) { return ((r & 3) << 1) | (
 
 template <bool TOPK>
 struct Fp8Cfg {
-  static constexpr int NS = 6;                        // ring stages
+  static constexpr int NS = 5;                        // ring stages
   static constexpr int C_STAGE = kTile * kC8Row;      // 16 KiB FP8 latent rows
   static constexpr int R_STAGE = kTile * kRRow;       // 4 KiB BF16 rotary rows
   static constexpr int SC_STAGE = kTile * 4;          // 128 B scales
@@ -47,12 +50,20 @@ struct Fp8Cfg {
   // stage address plus a swizzled offset, formed by XOR on bits 5-7
   static constexpr int STAGE = (C_STAGE + R_STAGE + SC_STAGE + 255) / 256 * 256;
   static constexpr int MASK_OFF = NS * STAGE;         // one byte per wave and stage: visible rows
-  // the output rows are staged through the first 133,120 bytes at a segment's end
-  static constexpr int RING_END = MASK_OFF + 32 > 133120 ? MASK_OFF + 32 : 133120;
-  static constexpr int QR_OFF = RING_END;             // rotary queries, [head][64] BF16, rows swizzled
+  static constexpr int QR_OFF = MASK_OFF + 32;        // rotary queries, [head][64] BF16, rows swizzled
   static constexpr int LIST_OFF = QR_OFF + kHeads * kRRow;
   static constexpr int LIST = TOPK ? 2048 : 0;        // row codes (page * 64 + slot) of a chunk
-  static constexpr int LDS_BYTES = LIST_OFF + LIST * 4;
+  // probabilities (times the row scales) of the tiles, 2 x [head][32] BF16
+  static constexpr int P_OFF = (LIST_OFF + LIST * 4 + 255) / 256 * 256;
+  static constexpr int P_BYTES = kHeads * kTile * 2;
+  static constexpr int A_OFF = P_OFF + 2 * P_BYTES;   // rescale factors, 2 x [128] float
+  static constexpr int I_OFF = A_OFF + 2 * kHeads * 4;  // 1 / row sum at a segment's end, [128] float
+  static constexpr int LDS_BYTES = I_OFF + kHeads * 4;
+  // the output rows are staged through the first kSplitStage bytes at a
+  // segment's end, over the ring, the rotary queries, the list and the
+  // probabilities (all free by then), never over the row sums
+  static_assert(kSplitStage <= I_OFF, "output staging must stay clear of the row sums");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static constexpr int DPW = 6;                       // loads per wave and tile: 4 latent, rotary, scales
   static constexpr int CHUNK = TOPK ? LIST / kTile : 1 << 30;  // tiles between two pipeline drains
 };
@@ -244,6 +255,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
   }
 
   const Fp8Offsets off(lane);
+  // probabilities of head 32 nb + row, position chunk 2 kb2 + hi:
+  // (bp ^ 32 kb2) + 2048 nb inside a probability buffer
+  const int ps = pswz(row);
+  const uint32_t bp = 64 * row + 16 * (hi ^ (ps & 1)) + 32 * (ps >> 1);
+  // transposing reads of this wave's column block 4 w + mbl: (tq ^ 32 mbl)
+  // + 16 rows * kb2 (off.t_base names block mb as t_base ^ 32 (mb % 8) plus
+  // 256 (mb / 8); t_base has no bit 8)
+  const uint32_t tq = ((uint32_t)off.t_base ^ (128u * (uint32_t)(w & 1))) | (256u * (uint32_t)(w >> 1));
   Fp8Loader<TOPK> ld;
   ld.pool = a.pool;
   ld.page_bytes = a.page_bytes;
@@ -280,28 +299,47 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
 
   // ---- the MFMA stream of one iteration ----
   // HAS_S: the 32 latent score MFMAs of the tile in stage sst, then the 32
-  // weighted-latent MFMAs of the tile in stage pst, with the rest of the
-  // tile-sst work between them: after weighted MFMA 2 the latent scores are
-  // multiplied by the row scales, after MFMAs 3, 4, 6 and 7 the 4 rotary
-  // score MFMAs continue the same accumulator chain, and from MFMA 10 on the
-  // softmax runs (piece(s) after weighted MFMA 10 + s).  Without HAS_S only the weighted
-  // latent.  after_s(k) runs after latent score MFMA k.
-  auto stream = [&](auto has_s, int sst, int pst, const bf16x8& P0, const bf16x8& P1, f32x16& S,
-                    const float (&rsc)[16], auto&& after_s, auto&& piece) __attribute__((always_inline)) {
+  // weighted-latent MFMAs of the tile in stage pst with the probabilities at
+  // pb, with the rest of the tile-sst work between them: after weighted MFMA
+  // 2 the latent scores are multiplied by the row scales, after MFMAs 3, 4, 6
+  // and 7 the 4 rotary score MFMAs continue the same accumulator chain, and
+  // from MFMA 10 on the softmax runs (piece(s) after weighted MFMA 10 + s).
+  // Without HAS_S only the weighted latent.  after_s(k) runs after latent
+  // score MFMA k, mid() before the first weighted MFMA.
+  //
+  // The weighted latent goes column block by column block (st = 4 kb2 +
+  // mbl, block 4 w + mbl of this wave's quarter), each A operand serving four
+  // MFMAs (one per head block nb): its raw FP8 read goes out two blocks
+  // ahead and is widened one block ahead, in two alternating registers; the
+  // four B operands of a position half sit in four.
+  auto stream = [&](auto has_s, int sst, int pst, uint32_t pb, f32x16& S, float (&rsc)[16], auto&& after_s,
+                    auto&& mid, auto&& piece) __attribute__((always_inline)) {
     constexpr bool HAS_S = decltype(has_s)::value;
-    constexpr int DS = 3, DP = 4;  // operand reads in flight: score pairs, weighted-latent blocks
+    constexpr int DS = 3;  // score operand pairs in flight
     const uint32_t sb = ld.lds0 + sst * C::STAGE + off.s_base;
-    const uint32_t pb = ld.lds0 + pst * C::STAGE + off.t_base;
+    const uint32_t pq = ld.lds0 + pst * C::STAGE + tq;
     auto pair_raw = [&](auto pc) -> i32x4 {
       constexpr int p = decltype(pc)::value;
       return *(const LDS i32x4*)((LDS char*)(uintptr_t)xor_here<32 * (p & 7)>(sb) + 256 * (p >> 3));
     };
-    auto pv_raw = [&](auto jc) -> i32x2 {
-      constexpr int jj = decltype(jc)::value, mb = jj & 15, kb2 = jj >> 4;
+    auto a_raw = [&](auto stc) __attribute__((always_inline)) -> i32x2 {
+      constexpr int st = decltype(stc)::value, mbl = st & 3, kb2 = st >> 2;
       return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (LDS i32x2*)((LDS char*)(uintptr_t)xor_here<32 * (mb & 7)>(pb) + 256 * (mb >> 3) + 16 * kC8Row * kb2));
+          (LDS i32x2*)((LDS char*)(uintptr_t)xor_here<32 * mbl>(pq) + 16 * kC8Row * kb2));
     };
-    i32x2 pring[DP];
+    auto b_read = [&](uint32_t pbk, int nb) __attribute__((always_inline)) -> bf16x8 {
+      return *(const LDS bf16x8*)((LDS char*)(uintptr_t)pbk + 2048 * nb);
+    };
+    i32x2 araw[2];
+    bf16x8 A[2], B[4];
+    // weighted-latent operands read before its first MFMA: the raw A
+    // operands of blocks 0 and 1, the B operands of position half 0
+    auto pre = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < 2) araw[i] = a_raw(std::integral_constant<int, i>{});
+      else B[i - 2] = b_read(pb, i - 2);
+    };
+    constexpr int kPre = 6;
     bf16x8 ro[2], rq[2];
     if constexpr (HAS_S) {
       i32x4 sring[DS];
@@ -321,25 +359,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
         if constexpr (p + DS < 16) {
           sring[p % DS] = pair_raw(std::integral_constant<int, p + DS>{});
         } else {
-          // the first weighted-latent operands, all DP of them spread over the
-          // last DS pairs (pair 16 - DS + i loads operands [i DP / DS, (i + 1) DP / DS))
+          // the first weighted-latent operands, spread over the last DS pairs
           constexpr int i = p + DS - 16;
-          static_for<i * DP / DS, (i + 1) * DP / DS>([&](auto xc) { pring[decltype(xc)::value] = pv_raw(xc); });
+          static_for<i * kPre / DS, (i + 1) * kPre / DS>([&](auto xc) { pre(xc); });
         }
         if constexpr (p + 1 < 16) cur = widen8((uint32_t)sring[(p + 1) % DS][0], (uint32_t)sring[(p + 1) % DS][1]);
         after_s(2 * p + 1);
         __builtin_amdgcn_sched_barrier(0);
       });
     } else {
-      static_for<0, DP>([&](auto xc) { pring[decltype(xc)::value] = pv_raw(xc); });
+      static_for<0, kPre>([&](auto ic) { pre(ic); });
       __builtin_amdgcn_sched_barrier(0);
     }
-    bf16x8 av = widen8((uint32_t)pring[0][0], (uint32_t)pring[0][1]);
+    A[0] = widen8((uint32_t)araw[0][0], (uint32_t)araw[0][1]);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t pb1 = 0;  // probability read address of position half 1
     static_for<0, 32>([&](auto jc) {
-      constexpr int jj = decltype(jc)::value;
-      O[jj & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, (jj >> 4) ? P1 : P0, O[jj & 15], 0, 0, 0);
-      if constexpr (jj + 1 < 32) av = widen8((uint32_t)pring[(jj + 1) % DP][0], (uint32_t)pring[(jj + 1) % DP][1]);
-      if constexpr (jj + DP < 32) pring[jj % DP] = pv_raw(std::integral_constant<int, jj + DP>{});
+      constexpr int jj = decltype(jc)::value, kb2 = jj >> 4, mbl = (jj >> 2) & 3, nb = jj & 3;
+      constexpr int st = 4 * kb2 + mbl;
+      O[4 * mbl + nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[st & 1], B[nb], O[4 * mbl + nb], 0, 0, 0);
+      // block st + 2's raw read replaces st's (widened before this block);
+      // block st + 1 is widened into the register block st - 1 used
+      if constexpr (nb == 0 && st + 2 < 8) araw[st & 1] = a_raw(std::integral_constant<int, st + 2>{});
+      if constexpr (nb == 1 && st + 1 < 8)
+        A[(st + 1) & 1] = widen8((uint32_t)araw[(st + 1) & 1][0], (uint32_t)araw[(st + 1) & 1][1]);
+      // B operand (nb, 1) replaces (nb, 0) after its last use
+      if constexpr (jj == 12) pb1 = xor_here<32>(pb);
+      if constexpr (jj >= 12 && jj < 16) B[nb] = b_read(pb1, nb);
       if constexpr (HAS_S) {
         // rotary operands: K-blocks 0, 1 read after weighted MFMA 0, K-blocks
         // 2, 3 after the rotary MFMAs that free their registers
@@ -350,6 +397,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
         if constexpr (jj == 0) {
           rot_read(0);
           rot_read(1);
+          // the row scales for the latent scores (read here, not earlier, so
+          // that they hold no registers while the score operands do)
+          row_scales(sst, rsc);
         }
         if constexpr (jj == 1) {
           // two weighted MFMAs have run since the last latent score MFMA: its
@@ -370,6 +420,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+  };
+
+  // rescale factors of tile tt of the chunk (written by the owners in its iteration)
+  auto alpha_of = [&](int32_t tt) __attribute__((always_inline)) -> f32x4 {
+    return *(const LDS f32x4*)(L + C::A_OFF + (tt & 1) * 512 + 16 * row);
+  };
+  // rescale the accumulator by the factors of the previous tile, if any is not 1
+  auto rescale = [&](const f32x4& al) __attribute__((always_inline)) {
+    const bool mine = al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f;
+    if (__builtin_amdgcn_ballot_w64(mine) != 0) {
+#pragma unroll
+      for (int b = 0; b < 16; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[b][r] = scale_acc(O[b][r], al[b & 3]);
+    }
   };
 
   int32_t cb = b0;
@@ -421,12 +486,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
       }
       if (TOPK) fill_index_codes(a, cb, tc0, clen, T, list, tid);
       {
-        // The weighted latent of "tile -1" reads the last stage with zero
-        // probabilities; zero its latent rows so stale LDS cannot turn 0 x NaN
-        // into NaN.
+        // The weighted latent of "tile -1" reads the last stage with the
+        // probabilities of buffer 1: zero both, so stale LDS cannot turn
+        // 0 x NaN into NaN.
         LDS char* dst = L + (NS - 1) * C::STAGE + (tid >> 3) * kC8Row + 64 * (tid & 7);
 #pragma unroll
         for (int v = 0; v < 4; ++v) *(LDS i32x4*)(dst + 16 * v) = i32x4{0, 0, 0, 0};
+        LDS char* pz = L + C::P_OFF + C::P_BYTES + 32 * tid;
+        *(LDS i32x4*)pz = i32x4{0, 0, 0, 0};
+        *(LDS i32x4*)(pz + 16) = i32x4{0, 0, 0, 0};
       }
       __syncthreads();  // the row list and the zeroed stage are complete
 
@@ -469,13 +537,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 32; ++kb) asm volatile("" ::"v"(q[kb]));
 
-      bf16x8 Pp0, Pp1;  // probabilities (times the row scales) of the previous tile
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        Pp0[r] = (__bf16)0.f;
-        Pp1[r] = (__bf16)0.f;
-      }
-
       for (int32_t j = 0; j < clen; ++j) {
         const int32_t t = tc0 + j;
         const int st = j % NS;
@@ -486,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
         else if (ahead == 1) wait_vmcnt<C::DPW>();
         else wait_vmcnt<0>();
         __syncthreads();
-        const uint32_t mask = *(const LDS uint32_t*)(L + C::MASK_OFF + 4 * st);
+        const uint32_t mask = __builtin_amdgcn_readfirstlane(*(const LDS uint32_t*)(L + C::MASK_OFF + 4 * st));
         if (mask != 0xFFFFFFFFu) {
           // zero the latent rows and the scales of masked positions (their
           // probability is 0, and the bytes may be anything)
@@ -517,26 +578,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
         // ---- softmax of tile j, in pieces, inside the weighted latent of tile j - 1 ----
         f32x16 S;
         float rsc[16];
-        float mt = -INFINITY, m_use = m_run, neg_m = 0.f, lsum = 0.f;
+        float mt = -INFINITY, m_use = m_run, neg_m = 0.f, lsum = 0.f, alpha = 1.f;
         bool need = false;
         bf16x8 Pc0, Pc1;
+        // this lane's probability row of tile j (kb2 = 0 at pw, 1 at pw ^ 32)
+        const uint32_t pw = ld.lds0 + C::P_OFF + (j & 1) * C::P_BYTES + bp + 2048 * w;
+        // rescale factors of tile j - 1 (none before the chunk's first tile),
+        // read near the end of the scores so that they hold registers briefly
+        f32x4 al_prev;
         auto after_s = [&](int k) {
+          if (k == 28) al_prev = alpha_of(j + 1);
           if (has_next && (k & 3) == 0 && (k >> 2) < C::DPW) {
             if (TOPK) ld.gather_one(gnext, k >> 2);
             else ld.dense_one(dnext, k >> 2);
           }
-          if (k == 26) row_scales(st, rsc);
         };
         auto piece = [&](int k) {
           // Each step ends with an empty asm that takes its result: code motion
           // cannot then sink the VALU work past the MFMAs that hide it.
           if (k == 0 || k == 1) {
-            // masked rows -inf; running maximum over the other 8
-            const uint32_t mlane = mask >> (4 * hi);
+            // masked rows -inf (only in tiles that have any); running maximum
+            // over the other 8
+            if (mask != 0xFFFFFFFFu) {
+              const uint32_t mlane = mask >> (4 * hi);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 8 * k + e;
-              S[r] = ((mlane >> (8 * (r >> 2) + (r & 3))) & 1u) ? S[r] : -INFINITY;
+              for (int e = 0; e < 8; ++e) {
+                const int r = 8 * k + e;
+                S[r] = ((mlane >> (8 * (r >> 2) + (r & 3))) & 1u) ? S[r] : -INFINITY;
+              }
             }
             const float m8 = max3_raw(max3_raw(S[8 * k], S[8 * k + 1], S[8 * k + 2]),
                                       max3_raw(S[8 * k + 3], S[8 * k + 4], S[8 * k + 5]), max_raw(S[8 * k + 6], S[8 * k + 7]));
@@ -582,9 +651,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
             asm volatile("" : "+v"(lsum));
             if (k == 15) asm volatile("" : "+v"(Pc0));
             if (k == 19) asm volatile("" : "+v"(Pc1));
+          } else if (k == 20) {
+            // factor that takes sums relative to m_run to m_use; every wave
+            // applies it to its columns of this head before the tile's
+            // weighted latent.  A head whose maximum is still -inf has only
+            // zeros there (all its probabilities so far were 0): factor 1, so
+            // the first tile of a chunk costs no accumulator pass.
+            alpha = (need && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
+            *(LDS float*)(L + C::A_OFF + (j & 1) * 512 + 4 * head_slot(head)) = alpha;
+            *(LDS bf16x8*)(LDS char*)(uintptr_t)pw = Pc0;
+          } else if (k == 21) {
+            *(LDS bf16x8*)(LDS char*)(uintptr_t)xor_here<32>(pw) = Pc1;
           }
         };
-        stream(std::true_type{}, st, (j + NS - 1) % NS, Pp0, Pp1, S, rsc, after_s, piece);
+        stream(std::true_type{}, st, (j + NS - 1) % NS, ld.lds0 + C::P_OFF + ((j + 1) & 1) * C::P_BYTES + bp, S, rsc,
+               after_s,
+               [&]() {
+                 if (j > 0) rescale(al_prev);
+               },
+               piece);
         if (TOPK && has_next) {
           const uint32_t bits = ld.gather_bits(gnext);
           if (lane == 0) L[C::MASK_OFF + 4 * nst + w] = (char)bits;
@@ -592,30 +677,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
           if (lane == 0) L[C::MASK_OFF + 4 * nst + w] = (char)dnext.bits;
         }
 
-        // rescale what the accumulator holds (tiles up to j - 1) to the new
-        // reference; a head whose maximum is still -inf has only zeros there
-        // (all its probabilities so far were 0), so the first tile of a
-        // segment never needs the accumulator pass
-        {
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
-          l_run *= alpha;
-          if (__builtin_amdgcn_ballot_w64(need && m_run != -INFINITY) != 0) {
-#pragma unroll
-            for (int mb = 0; mb < 16; ++mb)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) O[mb][r] = scale_acc(O[mb][r], alpha);
-          }
-        }
         m_run = m_use;
-        l_run += lsum;
-        Pp0 = Pc0;
-        Pp1 = Pc1;
+        l_run = l_run * alpha + lsum;
       }
       {
-        // weighted latent of the chunk's last tile
+        // weighted latent of the chunk's last tile, after its rescale; the
+        // barrier makes every owner's probabilities and factors visible
+        __syncthreads();
+        const f32x4 al_last = alpha_of(clen - 1);
         f32x16 S_unused;
         float rsc_unused[16];
-        stream(std::false_type{}, 0, (clen + NS - 1) % NS, Pp0, Pp1, S_unused, rsc_unused, [](int) {}, [](int) {});
+        stream(std::false_type{}, 0, (clen + NS - 1) % NS, ld.lds0 + C::P_OFF + ((clen + 1) & 1) * C::P_BYTES + bp,
+               S_unused, rsc_unused, [](int) {}, [&]() { rescale(al_last); }, [](int) {});
       }
     }
     done += seg;
@@ -628,7 +701,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
       const int64_t slot = worker + cb;
       __bf16* rows = DIRECT ? (__bf16*)a.o_lat + (int64_t)cb * kHeads * kLatent
                             : (__bf16*)a.part_o + slot * kHeads * kLatent;
-      store_rows_staged(L, rows + (int64_t)32 * w * kLatent, O, inv, w);
+      *(LDS float*)(L + C::I_OFF + 4 * head_slot(head)) = inv;
+      store_rows_split(L, C::I_OFF, rows, O, w);
       if (DIRECT) {
         if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
       } else {
