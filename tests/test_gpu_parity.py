@@ -387,6 +387,22 @@ def test_topk_index_handling_bit_exact(torch, R, cache):
         np.testing.assert_allclose(part_l[b].cpu().numpy(), math.log(128), rtol=1e-6)
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("workers", [3, 11, 40])
+def test_tiny_segments_every_head(torch, R, cache, workers):
+    """Contexts of 1 to 65 positions over many workers: segments of one or
+    two tiles, ragged last tiles, requests split across workers, workers
+    with several short segments.  Exercises the segment start (page ids,
+    staged queries, the first two tile loads and the loads past the
+    segment's end), the first-tile rescale skip and the output staging at
+    their smallest.  Every head of every request."""
+    _log(f"tiny segments {cache} workers={workers}")
+    lens = [1, 31, 32, 33, 64, 65, 2, 17, 40, 5]
+    name = "v2_batched" if cache == "bf16" else "v2_fp8_topk"
+    inp = I.make_inputs(name, seed=31, seq_lens=lens, **({} if cache == "bf16" else {"topk": 0}))
+    check_step(torch, R, inp, split=True, num_workers=workers)
+
+
 @pytest.mark.parametrize("name", ["v2_fp8_topk", "v2_fp8g_topk"])
 def test_fp8_topk_small(torch, R, name):
     _log(f"{name} small")
