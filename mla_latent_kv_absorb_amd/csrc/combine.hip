@@ -267,19 +267,61 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   if (a.lse_out != nullptr && lane == 0 && (!SPLIT || wv == 0)) a.lse_out[(int64_t)b * a.H + h] = m.lse();
 }
 
+// merge_cols for BF16 rows of 512 columns, each lane 8 of them, for a plan
+// whose request and head are the same in every lane: the row addresses are
+// scalar, the loads of a group take 4 registers each until they are summed,
+// and the sum runs in the same order as merge_cols, so the result is the same.
+__device__ __forceinline__ void merge_rows_bf16(const MergePlan& m, const char* row0, int64_t row_bytes,
+                                                f32x4& acc0, f32x4& acc1, int32_t j_lo, int32_t j_hi) {
+  acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc1 = acc0;
+  if (j_hi > m.np) j_hi = m.np;
+  const uint32_t lane_off = 16u * __lane_id();
+  for (int32_t c = j_lo >> 6; 64 * c < j_hi; ++c) {
+    const float l = m.chunk_lse(c);
+    const float wl = (l == -INFINITY) ? 0.f : expf(l - m.mref) * m.inv;  // lane's weight
+    const int32_t n = j_hi - 64 * c < 64 ? j_hi - 64 * c : 64;
+    for (int32_t j = j_lo - 64 * c > 0 ? j_lo - 64 * c : 0; j < n; j += kUnroll) {
+      bf16x8 raw[kUnroll];
+      float wg[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int32_t jj = j + u < n ? j + u : n - 1;
+        wg[u] = j + u < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), jj)) : 0.f;
+        const char* row = row0 + (m.p_first + 64 * c + jj) * row_bytes;
+        raw[u] = *(const bf16x8*)(row + lane_off);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float w = wg[u];
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = (float)raw[u][e];
+          hi[e] = (float)raw[u][4 + e];
+        }
+        acc0 += w == 0.f ? f32x4{0.f, 0.f, 0.f, 0.f} : w * lo;
+        acc1 += w == 0.f ? f32x4{0.f, 0.f, 0.f, 0.f} : w * hi;
+      }
+    }
+  }
+}
+
 // ---- merge and value up-projection in one launch (V2 dims, BF16) ----
-// Work-group (head h, 32 requests), 8 waves: each wave merges four requests'
+// Work-group (head h, 32 requests), 16 waves: each wave merges two requests'
 // partials of head h into BF16 rows in LDS (the same arithmetic as
-// combine_kernel, rounded to BF16 as o_lat would be).  With fewer than 8
-// requests in the group, the 8 / n waves of a request split its partials
+// combine_kernel, rounded to BF16 as o_lat would be).  With fewer than 16
+// requests in the group, the 16 / n waves of a request split its partials
 // into contiguous ranges and their float32 sums are added in LDS, so a lone
-// long request (hundreds of partials) is merged by all 8 waves.  Each wave
-// loads its slice of W_UV[h] (32 rows, half of K) before merging, so those
-// reads overlap the merge; then every wave multiplies its slice by the merged
-// rows on MFMA 32x32x16, the two K halves meet in LDS, and waves 0..3 store
-// out^T[m][b] = sum_k W_UV[h][m][k] o[b][k] for 32 rows m each ("DeepSeek's
-// KV Cache", Figure 6, form (2)).  The merged latent never goes to HBM.
-constexpr int kCuThreads = 512;
+// long request (hundreds of partials) is merged by all 16 waves.  Each wave
+// loads its slice of W_UV[h] (32 rows, a quarter of K) before merging, so
+// those reads overlap the merge; then every wave multiplies its slice by the
+// merged rows on MFMA 32x32x16, the four K quarters meet in LDS, and waves
+// 0..3 store out^T[m][b] = sum_k W_UV[h][m][k] o[b][k] for 32 rows m each
+// ("DeepSeek's KV Cache", Figure 6, form (2)).  The merged latent never goes
+// to HBM.  16 waves of at most 128 registers (4 per SIMD) keep twice as many
+// requests' loads in flight as 8 waves of 169.
+constexpr int kCuThreads = 1024;
 constexpr int kCuWaves = kCuThreads / 64;
 constexpr int kCuReq = 32;                // MFMA N: requests per work-group at most
 // requests per work-group: 16 up to 32 requests, so that 32 requests still
@@ -303,11 +345,11 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
   const int32_t b0 = blockIdx.y * grp;
   const int32_t nb = a.batch - b0 < grp ? a.batch - b0 : grp;
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int64_t row_stride = (int64_t)kHeads * kLatent;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row_bytes = (int64_t)kHeads * kLatent * 2;
 
   // This wave's share of the up-projection: rows 32 (wv % 4) .. +31 of
-  // W_UV[h], latent columns 256 (wv / 4) .. +255.  Loaded first, so the
+  // W_UV[h], latent columns 128 (wv / 4) .. +127.  Loaded first, so the
   // weight reads overlap the merge.
   constexpr int kKB = kLatent / 16 / (kCuWaves / 4);  // K-blocks per wave
   const int rb = wv & 3, kq = wv >> 2;
@@ -347,11 +389,10 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
     if (bl < nb) {  // wave-uniform
       const int32_t b = b0 + bl;
       MergePlan m;
-      m.init(a, b, h, below_s[kCuReq], below_s[bl]);
-      const __bf16* row0 = (const __bf16*)a.part_o + ((int64_t)b * kHeads + h) * kLatent;
+      m.init(a, b, h, uniform_i64(below_s[kCuReq]), uniform_i64(below_s[bl]));
+      const char* row0 = (const char*)a.part_o + ((int64_t)b * kHeads + h) * kLatent * 2;
       const int32_t j_lo = (int32_t)((int64_t)m.np * g / G), j_hi = (int32_t)((int64_t)m.np * (g + 1) / G);
-      float acc;
-      merge_cols<__bf16, true>(m, row0, row_stride, 8 * lane, acc0, acc1, acc, j_lo, j_hi);
+      merge_rows_bf16(m, row0, row_bytes, acc0, acc1, j_lo, j_hi);
       if (g == 0 && a.lse_out != nullptr && lane == 0) a.lse_out[(int64_t)b * kHeads + h] = m.lse();
     }
     *(f32x4*)(red + wv * kLatent + 8 * lane) = acc0;
@@ -381,11 +422,10 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
     if (bl < nb) {  // wave-uniform
       const int32_t b = b0 + bl;
       MergePlan m;
-      m.init(a, b, h, below_s[kCuReq], below_s[bl]);
-      const __bf16* row0 = (const __bf16*)a.part_o + ((int64_t)b * kHeads + h) * kLatent;
+      m.init(a, b, h, uniform_i64(below_s[kCuReq]), uniform_i64(below_s[bl]));
+      const char* row0 = (const char*)a.part_o + ((int64_t)b * kHeads + h) * kLatent * 2;
       f32x4 acc0, acc1;
-      float acc;
-      merge_cols<__bf16, true>(m, row0, row_stride, 8 * lane, acc0, acc1, acc);
+      merge_rows_bf16(m, row0, row_bytes, acc0, acc1, 0, 0x7fffffff);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         o[e] = (__bf16)acc0[e];
@@ -398,7 +438,7 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
   __syncthreads();
 
   // A: W_UV[h] rows 32 rb + (lane % 32), 8 columns per lane per K-block;
-  // B: merged row (lane % 32), the same 8 columns; this wave's K half
+  // B: merged row (lane % 32), the same 8 columns; this wave's K quarter
   const char* op = olds + (lane & 31) * kCuRow + 16 * (lane >> 5) + 32 * kKB * kq;
   f32x16 acc = f32x16{};
 #pragma unroll
@@ -406,13 +446,15 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
     const bf16x8 bv = *(const bf16x8*)(op + 32 * kb);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wreg[kb], bv, acc, 0, 0, 0);
   }
-  // the two K halves of each row block meet in LDS
+  // the four K quarters of each row block meet in LDS
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[wv * 1024 + r * 64 + lane] = acc[r];
   __syncthreads();
   if (wv >= kDv / 32) return;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] += red[(rb + 4) * 1024 + r * 64 + lane];
+  for (int q = 1; q < kCuWaves / 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += red[(rb + 4 * q) * 1024 + r * 64 + lane];
   // lane holds rows m = 32 rb + 8 g + 4 (lane / 32) + e of request lane % 32
   const int bl = lane & 31;
   if (bl < nb) {

@@ -114,7 +114,10 @@ __global__ __launch_bounds__(256) void head_gemm_bf16_kernel(HeadGemmArgs a) {
 // XOR-swizzled by the row index so the operand reads below are free of bank
 // conflicts; then every wave reads its MFMA operands from LDS.  Each weight
 // byte is read from HBM once, in whole cache lines, and x once per
-// work-group.
+// work-group.  The results go back through LDS as well, so that each
+// request's 256 output bytes leave in one 16-byte store per lane (storing
+// straight from the accumulator layout scatters 8-byte pieces over 32
+// requests per instruction, 1.4 us slower in a 7 us launch).
 constexpr int kAbK = 128;
 constexpr int kAbRow = kAbK * 2;  // bytes per row
 __device__ __forceinline__ int ab_off(int row, int chunk) { return row * kAbRow + 16 * (chunk ^ (row & 15)); }
@@ -162,20 +165,31 @@ __global__ __launch_bounds__(256) void absorb_k128_kernel(HeadGemmArgs a) {
     accA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ba, accA, 0, 0, 0);
     accB = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bb, accB, 0, 0, 0);
   }
-  // lane holds rows mb + 32 wv + 8g + 4 kg + e (e = 0..3) of its column
+  // lane holds rows mb + 32 wv + 8g + 4 kg + e (e = 0..3) of its column:
+  // staged as BF16 rows of 128 values per column in LDS (over ws, whose
+  // reads all finished at the barrier), then stored 16 bytes per lane with
+  // every column's 256 bytes contiguous
+  __syncthreads();
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const int col = n0 + c + 32 * half;
-    if (col >= a.batch) continue;
     const f32x16& acc = half ? accB : accA;
-    __bf16* yp = (__bf16*)a.y + ((int64_t)col * a.H + h) * a.M + mb + 32 * wv + 4 * kg;
+    char* row = ws + (c + 32 * half) * kAbRow;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * g + e];
-      *(bf16x4*)(yp + 8 * g) = v;
+      // values 32 wv + 8 g + 4 kg .. +3: chunk 4 wv + g, half kg of it
+      *(bf16x4*)(row + 16 * ((4 * wv + g) ^ (c & 15)) + 8 * kg) = v;
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = t + 256 * i, cl = q >> 4, ch = q & 15, col = n0 + cl;
+    if (col < a.batch)
+      *(i32x4*)((char*)a.y + (((int64_t)col * a.H + h) * a.M + mb) * 2 + 16 * ch) =
+          *(const i32x4*)(ws + cl * kAbRow + 16 * (ch ^ (cl & 15)));
   }
 }
 
