@@ -333,6 +333,7 @@ constexpr int kDv = 128;
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u) {
   __shared__ __attribute__((aligned(16))) char olds[kCuReq * kCuRow];
@@ -450,22 +451,32 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[wv * 1024 + r * 64 + lane] = acc[r];
   __syncthreads();
-  if (wv >= kDv / 32) return;
+  if (wv < kDv / 32) {
 #pragma unroll
-  for (int q = 1; q < kCuWaves / 4; ++q)
+    for (int q = 1; q < kCuWaves / 4; ++q)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] += red[(rb + 4 * q) * 1024 + r * 64 + lane];
-  // lane holds rows m = 32 rb + 8 g + 4 (lane / 32) + e of request lane % 32
-  const int bl = lane & 31;
-  if (bl < nb) {
-    __bf16* y = (__bf16*)u.out + ((int64_t)(b0 + bl) * kHeads + h) * kDv + 32 * rb + 4 * (lane >> 5);
+      for (int r = 0; r < 16; ++r) acc[r] += red[(rb + 4 * q) * 1024 + r * 64 + lane];
+    // lane holds rows m = 32 rb + 8 g + 4 (lane / 32) + e of request lane % 32:
+    // staged in LDS as one 256-byte row of outputs per request (over olds,
+    // whose reads all finished before the last barrier), 16-byte chunks
+    // XOR-swizzled by the request
+    const int bl = lane & 31;
+    char* row = olds + bl * (kDv * 2);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * g + e];
-      *(bf16x4*)(y + 8 * g) = v;
+      *(bf16x4*)(row + 16 * ((4 * rb + g) ^ (bl & 15)) + 8 * (lane >> 5)) = v;
     }
+  }
+  __syncthreads();
+  // each request's 256 output bytes leave as 16 lanes x 16 bytes
+  if (threadIdx.x < kCuReq * 16) {
+    const int r = threadIdx.x >> 4, ch = threadIdx.x & 15;
+    if (r < nb)
+      *(i32x4*)((char*)u.out + ((int64_t)(b0 + r) * kHeads + h) * kDv * 2 + 16 * ch) =
+          *(const i32x4*)(olds + r * (kDv * 2) + 16 * (ch ^ (r & 15)));
   }
 }
 
