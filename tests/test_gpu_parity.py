@@ -237,14 +237,16 @@ def test_v2_absorb_and_up_projection_alone(torch, R, v2_ragged):
     assert_close(to_np(w.out), oracle.up_project(x, inp.w_uv), what="out_up")
 
 
-@pytest.mark.parametrize("batch", [3, 20, 37])
+@pytest.mark.parametrize("batch", [3, 16, 20, 33, 37])
 def test_v2_fused_combine_up(torch, R, batch):
     """mla_combine_out_up: against the oracle, and against mla_combine then
     mla_out_up on the same partials.  The merge is the same code, so lse is
     bit-identical; out may differ in the last BF16 bit (GEMM summation order).
-    The fused kernel takes requests in blocks of 16 (up to 32 requests) or 32:
-    20 requests make a full block and a partial one of 16, 37 a full one and a
-    partial one of 32."""
+    The fused kernel takes requests in blocks of 16 (up to 32 requests) or 32,
+    and merges a block of n requests on 16 waves, each request on 16 // n
+    waves when n < 16: 3 requests (5 waves each, one wave idle), 16 (one wave
+    each), 20 (a full block and one of 4), 33 (a full block of 32, two
+    requests per wave, and one lone request on all 16 waves), 37 (32 and 5)."""
     _log(f"fused merge + up-projection, batch {batch}")
     inp = I.make_inputs("v2_batched", seed=31, batch=batch, ctx=(40, 900))
     for nw in (None, 7):
