@@ -93,18 +93,31 @@ struct MergePlan {
   }
   // the same, given W and the units below request b
   __device__ __forceinline__ void init(const CombineArgs& a, int32_t b, int h, int64_t W_, int64_t below) {
-    W = W_;
-    const int64_t start = below + lead_of(a.topk);  // first tile of request b
     const int32_t nt_b = a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[b]);
+    int64_t pf, pl;
+    slot_range(a, W_, below, nt_b, &pf, &pl);
+    init_range(a, b, h, W_, pf, (int32_t)(pl - pf + 1));
+  }
+  // Workers [*pf, *pl] hold the partials of a request with nt_b tiles and
+  // `below` units below it (an empty range, *pl = *pf - 1, for no tiles).
+  __device__ __forceinline__ static void slot_range(const CombineArgs& a, int64_t W_, int64_t below, int32_t nt_b,
+                                                    int64_t* pf, int64_t* pl) {
+    const int64_t start = below + lead_of(a.topk);  // first tile of the request
+    *pf = 0;
+    *pl = -1;
+    if (nt_b > 0) {
+      *pf = worker_of(start, W_, a.num_workers, a.topk);
+      *pl = worker_of(start + nt_b - 1, W_, a.num_workers, a.topk);
+    }
+  }
+  // the same, given the first candidate worker and the candidate count
+  __device__ __forceinline__ void init_range(const CombineArgs& a, int32_t b, int h, int64_t W_, int64_t pf,
+                                             int32_t n) {
+    W = W_;
     P = a.num_workers;
     H = a.H;
-    p_first = 0;
-    int64_t p_last = -1;
-    if (nt_b > 0) {
-      p_first = worker_of(start, W, P);
-      p_last = worker_of(start + nt_b - 1, W, P);
-    }
-    np = (int32_t)(p_last - p_first + 1);  // candidate partials (some workers may be empty)
+    p_first = pf;
+    np = n;  // candidate partials (some workers may be empty)
     nchunks = (np + 63) / 64;
     lse_col = a.part_lse + (int64_t)b * a.H + h;
     // Workers are empty only when there are fewer units than workers; then
@@ -340,6 +353,9 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
   // per-wave float32 sums: the merge of small groups, then the up-projection's K quarters
   __shared__ __attribute__((aligned(16))) float red[kCuWaves * 1024];
   __shared__ int64_t below_s[kCuReq + 1];  // units below each request of the group; [kCuReq] = total
+  // first candidate worker and candidate count of each request of the group
+  __shared__ int32_t pfirst_s[kCuReq], np_s[kCuReq];
+  __shared__ int32_t tiles_s[kCuReq];  // tiles of each request of the group
   const CombineArgs& a = u.c;
   const int h = blockIdx.x;
   const int grp = cu_group(a.batch);
@@ -367,8 +383,9 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
     int64_t off = 0;
     for (int32_t base = 0; base < a.batch; base += 64) {
       const int32_t r = base + lane;
-      const int64_t sp =
-          r < a.batch ? span_of(a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[r]), a.topk) : 0;
+      const int32_t nt = r < a.batch ? (a.topk > 0 ? tiles_of(a.topk) : tiles_dense(a.seq_lens[r])) : 0;
+      const int64_t sp = span_of(nt, a.topk);
+      if (r >= b0 && r < b0 + kCuReq) tiles_s[r - b0] = nt;
       int64_t incl = sp;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -379,6 +396,13 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
       off += __shfl(incl, 63);
     }
     if (lane == 0) below_s[kCuReq] = off;
+    // each request's slot range, one request per lane, once for all waves
+    if (lane < kCuReq && b0 + lane < a.batch) {
+      int64_t pf, pl;
+      MergePlan::slot_range(a, off, below_s[lane], tiles_s[lane], &pf, &pl);
+      pfirst_s[lane] = (int32_t)pf;
+      np_s[lane] = (int32_t)(pl - pf + 1);
+    }
   }
   __syncthreads();
 
@@ -390,7 +414,8 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
     if (bl < nb) {  // wave-uniform
       const int32_t b = b0 + bl;
       MergePlan m;
-      m.init(a, b, h, uniform_i64(below_s[kCuReq]), uniform_i64(below_s[bl]));
+      m.init_range(a, b, h, uniform_i64(below_s[kCuReq]), __builtin_amdgcn_readfirstlane(pfirst_s[bl]),
+                   __builtin_amdgcn_readfirstlane(np_s[bl]));
       const char* row0 = (const char*)a.part_o + ((int64_t)b * kHeads + h) * kLatent * 2;
       const int32_t j_lo = (int32_t)((int64_t)m.np * g / G), j_hi = (int32_t)((int64_t)m.np * (g + 1) / G);
       merge_rows_bf16(m, row0, row_bytes, acc0, acc1, j_lo, j_hi);
@@ -423,7 +448,8 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(CombineUpArgs u)
     if (bl < nb) {  // wave-uniform
       const int32_t b = b0 + bl;
       MergePlan m;
-      m.init(a, b, h, uniform_i64(below_s[kCuReq]), uniform_i64(below_s[bl]));
+      m.init_range(a, b, h, uniform_i64(below_s[kCuReq]), __builtin_amdgcn_readfirstlane(pfirst_s[bl]),
+                   __builtin_amdgcn_readfirstlane(np_s[bl]));
       const char* row0 = (const char*)a.part_o + ((int64_t)b * kHeads + h) * kLatent * 2;
       f32x4 acc0, acc1;
       merge_rows_bf16(m, row0, row_bytes, acc0, acc1, 0, 0x7fffffff);

@@ -48,8 +48,8 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
     // request's lead, then its tiles)
     int64_t W = 0;
     for (int32_t b = 0; b < a.batch; ++b) W += span_of(ntiles(b), TOPK ? a.topk : 0);
-    const int64_t g0 = worker_lo(worker, W, a.num_workers);
-    const int64_t g1 = worker_lo(worker + 1, W, a.num_workers);
+    const int64_t g0 = worker_lo(worker, W, a.num_workers, TOPK ? a.topk : 0);
+    const int64_t g1 = worker_lo(worker + 1, W, a.num_workers, TOPK ? a.topk : 0);
     n = g1 - g0;
     if (n <= 0) return;
     int64_t acc = 0;

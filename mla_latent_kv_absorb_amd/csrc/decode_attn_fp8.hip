@@ -239,8 +239,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
     n = ntiles(b0);
   } else {
     const int64_t W = spans_below(a.seq_lens, a.batch, topk);
-    const int64_t g0 = worker_lo(worker, W, a.num_workers);
-    const int64_t g1 = worker_lo(worker + 1, W, a.num_workers);
+    const int64_t g0 = worker_lo(worker, W, a.num_workers, topk);
+    const int64_t g1 = worker_lo(worker + 1, W, a.num_workers, topk);
     n = g1 - g0;
     if (n <= 0) return;
     locate_span(a.seq_lens, a.batch, topk, g0, &b0, &v0);

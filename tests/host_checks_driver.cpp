@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "host_checks.h"
+#include "mla_args.h"
 
 using namespace mla_host;
 
@@ -276,6 +277,72 @@ static void test_side_calls() {
                            1 << 20) == MLA_ERR_INVALID_ARG);
 }
 
+// The split partition shared by the attention and merge kernels
+// (mla_args.h): bounds start at 0, end at W and never decrease; worker_of
+// inverts worker_lo; dense batches with at least 64 units per worker give
+// workers on even XCDs (p / (P / 8) even) the larger shares, by 65 : 63.
+static void test_partition() {
+  using namespace mla;
+  const int64_t Ps[] = {1, 7, 8, 16, 96, 100, 256, 1024};
+  const int64_t Ws[] = {1, 5, 255, 256, 1023, 16383, 16384, 16385, 49152 + 64 * 12, 1532221 / 32 + 64 * 12, 4108,
+                        (int64_t)1 << 32};
+  for (int32_t topk : {0, 2048}) {
+    for (int64_t P : Ps) {
+      for (int64_t W : Ws) {
+        const bool weighted = xcd_weighted(W, P, topk);
+        EXPECT(weighted == (topk == 0 && P >= 16 && (P & (P - 1)) == 0 && W >= 64 * P));
+        EXPECT(worker_lo(0, W, P, topk) == 0 && worker_lo(P, W, P, topk) == W);
+        int64_t even = 0, odd = 0;
+        bool monotone = true, inverse = true, no_empty = true;
+        for (int64_t q = 0; q < P; ++q) {
+          const int64_t a = worker_lo(q, W, P, topk), b = worker_lo(q + 1, W, P, topk);
+          monotone = monotone && b >= a;
+          if (W >= P) no_empty = no_empty && b > a;
+          if (b > a) {
+            // the first and last unit of a non-empty share belong to it
+            inverse = inverse && worker_of(a, W, P, topk) == q && worker_of(b - 1, W, P, topk) == q;
+          }
+          if (P % 8 == 0 && (q / (P / 8)) % 2 == 0) even += b - a;
+          else odd += b - a;
+        }
+        EXPECT(monotone);
+        EXPECT(inverse);
+        if (!weighted) EXPECT(no_empty);
+        if (weighted) {
+          EXPECT(no_empty);
+          // even-XCD workers carry 65/128 of the units, to within one unit each
+          const double want = (double)W * 65.0 / 128.0;
+          EXPECT(fabs((double)even - want) <= (double)P);
+          EXPECT(even > odd);
+        }
+      }
+    }
+  }
+  // every unit of a small space maps to the worker whose range holds it
+  for (int64_t P : {16, 24, 256}) {
+    const int64_t W = 64 * P + 37;
+    for (int64_t x = 0; x < W; ++x) {
+      const int64_t q = worker_of(x, W, P, 0);
+      if (!(q >= 0 && q < P && worker_lo(q, W, P, 0) <= x && x < worker_lo(q + 1, W, P, 0))) {
+        EXPECT(false);
+        break;
+      }
+    }
+  }
+  // equal shares, empty workers included: the last worker whose range starts
+  // at or before x, (x + 1) P - 1 over W
+  for (int64_t P : {7, 16, 100, 256}) {
+    for (int64_t W : {1, 3, 15, 16, 17, 99, 255, 1000}) {
+      for (int64_t x = 0; x < W; ++x) {
+        if (worker_of(x, W, P, 2048) != ((x + 1) * P - 1) / W || worker_of(x, W, P, 0) != ((x + 1) * P - 1) / W) {
+          EXPECT(false);
+          break;
+        }
+      }
+    }
+  }
+}
+
 int main() {
   test_status_and_version();
   test_config_and_layout();
@@ -285,6 +352,7 @@ int main() {
   test_prepare_merges_and_gemms();
   test_packed_partials();
   test_side_calls();
+  test_partition();
   printf("host checks: %d expectations met\n", g_checks);
   return 0;
 }
