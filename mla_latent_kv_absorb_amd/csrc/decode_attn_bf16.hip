@@ -154,12 +154,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
     v0 = kLeadTiles;  // no lead: straight to tile 0
     n = ntiles(b0);
   } else {
-    const int64_t W = spans_below(a.seq_lens, a.batch, 0);
-    const int64_t g0 = worker_lo(worker, W, a.num_workers, 0);
-    const int64_t g1 = worker_lo(worker + 1, W, a.num_workers, 0);
-    n = g1 - g0;
+    const WorkerSpan ws = locate_worker(a.seq_lens, a.batch, 0, worker, a.num_workers);
+    n = ws.g1 - ws.g0;
     if (n <= 0) return;
-    locate_span(a.seq_lens, a.batch, 0, g0, &b0, &v0);
+    b0 = ws.b;
+    v0 = ws.t;
   }
 
   if (n == 0) {  // direct mode, a request with no position

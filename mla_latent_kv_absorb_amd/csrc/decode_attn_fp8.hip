@@ -238,12 +238,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
     v0 = lead;
     n = ntiles(b0);
   } else {
-    const int64_t W = spans_below(a.seq_lens, a.batch, topk);
-    const int64_t g0 = worker_lo(worker, W, a.num_workers, topk);
-    const int64_t g1 = worker_lo(worker + 1, W, a.num_workers, topk);
-    n = g1 - g0;
+    const WorkerSpan ws = locate_worker(a.seq_lens, a.batch, topk, worker, a.num_workers);
+    n = ws.g1 - ws.g0;
     if (n <= 0) return;
-    locate_span(a.seq_lens, a.batch, topk, g0, &b0, &v0);
+    b0 = ws.b;
+    v0 = ws.t;
   }
   if (n == 0) {  // direct mode, a request with no position
     if (DIRECT) {

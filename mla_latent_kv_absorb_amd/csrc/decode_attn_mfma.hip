@@ -234,12 +234,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     v0 = lead;  // straight to tile 0
     n = ld.ntiles(b0);
   } else {
-    const int64_t W = spans_below(a.seq_lens, a.batch, TOPK ? a.topk : 0);
-    const int64_t g0 = worker_lo(worker, W, a.num_workers, TOPK ? a.topk : 0);
-    const int64_t g1 = worker_lo(worker + 1, W, a.num_workers, TOPK ? a.topk : 0);
-    n = g1 - g0;
+    const WorkerSpan ws = locate_worker(a.seq_lens, a.batch, TOPK ? a.topk : 0, worker, a.num_workers);
+    n = ws.g1 - ws.g0;
     if (n <= 0) return;
-    locate_span(a.seq_lens, a.batch, TOPK ? a.topk : 0, g0, &b0, &v0);
+    b0 = ws.b;
+    v0 = ws.t;
   }
 
   // ---- per-lane LDS offsets (relative to a tile) ----

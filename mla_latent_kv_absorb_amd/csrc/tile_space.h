@@ -85,4 +85,62 @@ __device__ inline void locate_span(const int32_t* seq_lens, int32_t batch, int32
   *t = 0;
 }
 
+// A worker's place in the split space: W (the space's units), its range
+// [g0, g1), and the request b and offset t of unit g0 (as locate_span; b is
+// the batch size when the range is empty at the end).  For a batch that fits
+// the wave's lanes, one load of the context lengths and one scan give both W
+// and the place (spans_below then locate_span would read them twice, one
+// dependent round trip after the other); index lists need no load at all.
+struct WorkerSpan {
+  int64_t W, g0, g1;
+  int32_t b, t;
+};
+__device__ inline WorkerSpan locate_worker(const int32_t* seq_lens, int32_t batch, int32_t topk, int64_t p,
+                                           int64_t P) {
+  WorkerSpan s;
+  if (topk > 0) {
+    const int64_t sp = span_of(tiles_of(topk), topk);
+    s.W = (int64_t)batch * sp;
+    s.g0 = worker_lo(p, s.W, P, topk);
+    s.g1 = worker_lo(p + 1, s.W, P, topk);
+    // g0 / sp without a 64-bit division
+    int64_t q = (int64_t)((double)s.g0 / (double)sp);
+    while (q > 0 && q * sp > s.g0) --q;
+    while ((q + 1) * sp <= s.g0) ++q;
+    s.b = (int32_t)q;
+    s.t = (int32_t)(s.g0 - q * sp);
+    return s;
+  }
+  if (batch > 64) {
+    s.W = spans_below(seq_lens, batch, 0);
+    s.g0 = worker_lo(p, s.W, P, 0);
+    s.g1 = worker_lo(p + 1, s.W, P, 0);
+    s.b = batch;
+    s.t = 0;
+    if (s.g1 > s.g0) locate_span(seq_lens, batch, 0, s.g0, &s.b, &s.t);
+    return s;
+  }
+  const int lane = __lane_id();
+  const int64_t sp = lane < batch ? span_of(tiles_dense(seq_lens[lane]), 0) : 0;
+  int64_t incl = sp;  // inclusive scan over the lanes
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t up = __shfl_up(incl, d);
+    if (lane >= d) incl += up;
+  }
+  s.W = uniform_i64(__shfl(incl, 63));
+  s.g0 = worker_lo(p, s.W, P, 0);
+  s.g1 = worker_lo(p + 1, s.W, P, 0);
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > s.g0);
+  s.b = batch;
+  s.t = 0;
+  if (hit != 0) {
+    const int l = __builtin_ctzll(hit);
+    const int64_t end = __shfl(incl, l), len = __shfl(sp, l);
+    s.b = l;
+    s.t = __builtin_amdgcn_readfirstlane((int32_t)(s.g0 - (end - len)));
+  }
+  return s;
+}
+
 }  // namespace mla
