@@ -632,6 +632,18 @@ def test_v2_batched_full_size(torch, R):
                checks=[([0, 1, 17, 31, 32, 47, 62, 63], None), (range(inp.B), [0, 40, 77, 127])])
 
 
+@pytest.mark.parametrize("workers", [16, 32])
+def test_v2_xcd_weighted_split(torch, R, workers):
+    """The split weighted by XCD (dense batches, a power-of-two worker count,
+    at least 64 units per worker: workers on even XCDs take 65/64 of an
+    equal share, odd ones 63/64) against the oracle: 5 requests of 6K-12K
+    positions (about 1,400 units), 16 workers (weighted) and 32 (equal
+    shares), every request and head."""
+    _log(f"xcd-weighted split, {workers} workers")
+    inp = I.make_inputs("v2_batched", seed=41, batch=5, ctx=(6000, 12000))
+    check_step(torch, R, inp, split=True, num_workers=workers)
+
+
 @pytest.mark.parametrize("layer", [0, 29, 59])
 def test_v2_long_layer_full(torch, R, layer):
     """Long context (1 request x 131,072 positions): the first, middle and
