@@ -249,6 +249,15 @@ __device__ __forceinline__ void mfma_sv(f32x16& d, const bf16x8& a, const bf16x8
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 
+// A copy of v that the compiler cannot see through: what is derived from it
+// is computed anew where it is used, not kept (or spilled and reloaded) from
+// an earlier computation.
+__device__ __forceinline__ int opaque(int v) {
+  int r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
 // Uniform metadata reads go through the constant address space so they become
 // scalar loads (lgkmcnt), never vector loads that would queue behind the
 // in-flight LDS-bound loads on vmcnt.

@@ -176,14 +176,15 @@ struct Fp8Loader {
     int32_t code_c[4], code_r, code_s;
     uint32_t sb;
   };
-  __device__ __forceinline__ Gather gather(int st, const LDS int32_t* lc) const {
+  // ln: the lane id (passed in, so a caller can hand over a fresh copy)
+  __device__ __forceinline__ Gather gather(int st, const LDS int32_t* lc, int ln) const {
     // lc: the 32 codes of the tile; this wave loads rows 8 w .. 8 w + 7
-    const int hi = lane >> 5;
+    const int hi = ln >> 5;
     Gather g;
 #pragma unroll
     for (int q = 0; q < 4; ++q) g.code_c[q] = lc[8 * w + 2 * q + hi];
-    g.code_r = lc[8 * w + (lane >> 3)];
-    g.code_s = lc[8 * w + (lane & 7)];
+    g.code_r = lc[8 * w + (ln >> 3)];
+    g.code_s = lc[8 * w + (ln & 7)];
     g.sb = lds0 + st * C::STAGE;
     return g;
   }
@@ -497,22 +498,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
       }
       __syncthreads();  // the row list and the zeroed stage are complete
 
-      if (tc0 == ct) {
-        // the latent queries: issued with the first tiles, so that their
-        // latency overlaps that of the tiles
-        const __bf16* ql = (const __bf16*)a.q_lat + ((int64_t)cb * kHeads + head) * kLatent + 16 * hi;
-#pragma unroll
-        for (int p = 0; p < 16; ++p) {
-          q[2 * p] = *(const bf16x8*)(ql + 32 * p);
-          q[2 * p + 1] = *(const bf16x8*)(ql + 32 * p + 8);
-        }
-      }
-      // pipeline fill: tiles tc0 .. tc0 + NS - 3
+      // pipeline fill: tiles tc0 .. tc0 + NS - 3.  The gathers take their
+      // row-code addresses from a fresh copy of the lane id: a kept copy was
+      // spilled and reloaded, and the compiler's wait for the reload, inside
+      // this loop, waited (loads return in order) for the tiles issued in the
+      // iterations before as well.
       const int32_t pro = clen < NS - 2 ? clen : NS - 2;
       int32_t pg_next_p = 0, pg_next_raw = 0;
       if (TOPK) {
         for (int32_t k = 0; k < pro; ++k) {
-          const auto g = ld.gather(k, list + k * kTile);
+          const auto g = ld.gather(k, list + k * kTile, opaque(lane));
 #pragma unroll
           for (int x = 0; x < C::DPW; ++x) ld.gather_one(g, x);
           const uint32_t bits = ld.gather_bits(g);
@@ -529,6 +524,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
         }
         pg_next_p = (tc0 + NS - 2) >> 1;
         pg_next_raw = ld.raw(NS - 2 < clen ? pg_next_p : 0);
+      }
+      if (tc0 == ct) {
+        // the latent queries, behind the first tiles: the tiles do not wait
+        // for them, and their latency overlaps that of the tiles
+        const __bf16* ql = (const __bf16*)a.q_lat + ((int64_t)cb * kHeads + head) * kLatent + 16 * hi;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+          q[2 * p] = *(const bf16x8*)(ql + 32 * p);
+          q[2 * p + 1] = *(const bf16x8*)(ql + 32 * p + 8);
+        }
       }
       // The queries and the first tiles: waited for here, every chunk, and
       // taken, so that no wait for them is left inside the tile loop.
@@ -566,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
         typename Fp8Loader<TOPK>::Gather gnext;
         typename Fp8Loader<TOPK>::Dense dnext;
         if (TOPK) {
-          gnext = ld.gather(nst, list + (has_next ? j + NS - 2 : 0) * kTile);
+          gnext = ld.gather(nst, list + (has_next ? j + NS - 2 : 0) * kTile, lane);
         } else {
           const int32_t pg = ld.checked(pg_next_p, pg_next_raw);
           dnext = ld.dense(nst, t + NS - 2, pg, T);

@@ -503,6 +503,46 @@ def test_topk_list_over_several_chunks(torch, R, cache):
             check_step(torch, R, inp, split=True, num_workers=None if mode == "auto" else mode)
 
 
+@pytest.mark.parametrize("cache", [I.DTYPE_BF16, I.DTYPE_FP8, I.DTYPE_FP8_G128])
+@pytest.mark.parametrize("T, extra_cols", [(1_000_000, 5), (2_500_000, 0), (1_000_000, -15_000)])
+def test_topk_long_block_table_rows(torch, R, cache, T, extra_cols):
+    """Index lists into contexts of 1,000,000 and 2,500,000 positions, with
+    block-table rows of 15,630 and 39,063 entries: picks anywhere in a long
+    row resolve to the right page.  The last case's row has 625 entries
+    (fewer than the context's pages), so picks past its pages are skipped.
+    The logical pages map onto a 48-page pool (logical page j on the physical
+    page of page j % 48 of a 3,072-position request), so the oracle reads
+    position p at (p / 64 % 48) * 64 + p % 64 of that request."""
+    import dataclasses
+    name = {I.DTYPE_BF16: "v2_batched", I.DTYPE_FP8: "v2_fp8_topk", I.DTYPE_FP8_G128: "v2_fp8g_topk"}[cache]
+    _log(f"topk over a {T}-position context, {cache}, table columns {extra_cols:+d}")
+    small = I.make_inputs(name, seed=43, batch=1, ctx=(48 * 64, 48 * 64), topk=0)
+    pool, table = I.build_paged_pool(small)
+    pages = -(-T // 64)
+    cols = pages + extra_cols
+    long_table = np.ascontiguousarray(table[0][np.arange(cols) % 48][None, :], dtype=np.int32)
+    rng = np.random.default_rng(43)
+    k = 600
+    idx = np.sort(rng.choice(T, k, replace=False)).astype(np.int32)[None, :]
+    inp = dataclasses.replace(small, seq_lens=np.array([T], np.int32), offsets=np.array([0, T], np.int64),
+                              topk_idx=idx)
+    seen = idx[0][(idx[0] >> 6) < cols]
+    src = (seen >> 6) % 48 * 64 + (seen & 63)
+    if cache in I.FP8_DTYPES:
+        c = oracle.dequant_fp8_latent(small.c_codes[src], small.c_scales[src])
+    else:
+        c = small.c_kv[src]
+    r_out, r_lse, r_olat = oracle.decode_unabsorbed(c, small.k_rope[src], small.q_nope[0], small.q_rope[0],
+                                                    small.w_uk, small.w_uv, small.scale)
+    for split in (False, True):
+        w = R.DeviceWorkload(inp, split=split, pool=pool, table=long_table)
+        w.step()
+        torch.cuda.synchronize()
+        assert_close(to_np(w.out)[0], r_out, what=f"out split={split}")
+        assert_close(to_np(w.o_lat)[0], r_olat, what=f"o_lat split={split}")
+        assert_close(to_np(w.lse)[0], r_lse, abs_tol=LSE_ABS_TOL, what=f"lse split={split}")
+
+
 @pytest.mark.parametrize("name", ["v2_fp8_topk", "v2_fp8g_topk"])
 def test_fp8_dense_over_one_page_chunk(torch, R, name):
     """One dense FP8 request of 130,000 positions (4,063 tiles: one full chunk
