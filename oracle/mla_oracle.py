@@ -41,6 +41,7 @@ __all__ = [
     "e4m3_to_f64",
     "dequant_fp8_latent",
     "visible_positions",
+    "expand_keys_values",
     "decode_unabsorbed",
     "prefill_unabsorbed",
     "absorb_query",
@@ -116,6 +117,17 @@ def visible_positions(T: int, picked=None) -> np.ndarray:
     return np.unique(idx)  # a mask has set semantics
 
 
+def expand_keys_values(c_kv, w_uk, w_uv, h):
+    """Head h's content keys and values for every cached latent row, float64:
+    k_content_j = c_j W^UK_h (Figure 5 (1): the key built from the latent) and
+    v_j = W^UV_h c_j (Figure 6 (1): the value built from the same latent).
+    Returns (k_content [T, D_N], values [T, D_V])."""
+    c = np.asarray(c_kv, dtype=np.float64)
+    k_content = c @ np.asarray(w_uk[h], dtype=np.float64)
+    values = c @ np.asarray(w_uv[h], dtype=np.float64).T
+    return k_content, values
+
+
 def decode_unabsorbed(c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, scale, picked=None, heads=None):
     """One decode query of one request, unabsorbed, float64.
 
@@ -142,10 +154,11 @@ def decode_unabsorbed(c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, scale, picked=No
     lse = np.empty(len(hs))
     o_lat = np.empty((len(hs), c_kv.shape[1]))
     for i, h in enumerate(hs):
-        # Figure 5 (1): build the per-head content key from the latent, then
-        # concatenate the shared rotary key (Figure 4: the two scores add up to
-        # the dot product of the concatenated query and key).
-        k_content = c @ w_uk[h]                       # [n, D_N]
+        # Figure 5 (1) and Figure 6 (1): build the per-head content key and
+        # value from the latent; concatenate the shared rotary key to the key
+        # (Figure 4: the two scores add up to the dot product of the
+        # concatenated query and key).
+        k_content, values = expand_keys_values(c, w_uk, w_uv, h)  # [n, D_N], [n, D_V]
         keys = np.concatenate([k_content, kr], axis=1)  # [n, D_N + D_R]
         query = np.concatenate([q_nope[h], q_rope[h]])
         s = scale * (keys @ query)                    # [n]
@@ -153,8 +166,7 @@ def decode_unabsorbed(c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, scale, picked=No
         e = np.exp(s - m)
         z = e.sum()
         p = e / z
-        # Figure 6 (1): expand the values, then weight them.
-        values = c @ w_uv[h].T                        # [n, D_V]
+        # Figure 6 (1): weight the expanded values.
         out[i] = p @ values
         o_lat[i] = p @ c
         lse[i] = m + np.log(z)

@@ -61,8 +61,7 @@ def test_prefill_expand(torch, R):
     kn, v, kr = _np(w.k_nope), _np(w.v), _np(w.k_rope)
     np.testing.assert_array_equal(kr, inp.k_rope)
     for h in (0, 31, 64, 127):
-        ref_k = inp.c_kv.astype(np.float64) @ inp.w_uk[h].astype(np.float64)
-        ref_v = inp.c_kv.astype(np.float64) @ inp.w_uv[h].astype(np.float64).T
+        ref_k, ref_v = oracle.expand_keys_values(inp.c_kv, inp.w_uk, inp.w_uv, h)
         assert np.max(np.abs(kn[:, h] - ref_k)) <= 1e-2 * np.max(np.abs(ref_k)), f"k head {h}"
         assert np.max(np.abs(v[:, h] - ref_v)) <= 1e-2 * np.max(np.abs(ref_v)), f"v head {h}"
 

@@ -110,6 +110,22 @@ def _random_case(rng, H=3, D_C=12, D_R=4, D_N=5, D_V=6, T=9):
         scale=1.0 / math.sqrt(D_N + D_R))
 
 
+def test_expansion_by_hand():
+    """Figure 5 (1) and Figure 6 (1) of "DeepSeek's KV Cache": the content key
+    is the latent times W^UK ([input, output] form) and the value is W^UV
+    times the latent.  Two latent rows of width 3, one head, worked by hand:
+    rows (1, 2, 0) and (0, 1, -1); W^UK columns (1, 0, 2) and (0, 3, 1) give
+    keys (1, 6) and (-2, 2); W^UV rows (2, 0, 1), (0, -1, 4), (1, 1, 1) give
+    values (2, -2, 3) and (-1, -5, 0).  A transposed weight or a dropped
+    row would change them."""
+    c = np.array([[1.0, 2.0, 0.0], [0.0, 1.0, -1.0]])
+    w_uk = np.array([[[1.0, 0.0], [0.0, 3.0], [2.0, 1.0]]])   # [H=1, D_C=3, D_N=2]
+    w_uv = np.array([[[2.0, 0.0, 1.0], [0.0, -1.0, 4.0], [1.0, 1.0, 1.0]]])  # [H=1, D_V=3, D_C=3]
+    k, v = oracle.expand_keys_values(c, w_uk, w_uv, 0)
+    np.testing.assert_array_equal(k, [[1.0, 6.0], [-2.0, 2.0]])
+    np.testing.assert_array_equal(v, [[2.0, -2.0, 3.0], [-1.0, -5.0, 0.0]])
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_absorbed_equals_expanded(seed):
     """Figures 5 and 6 of "DeepSeek's KV Cache": moving W^UK to the query side
