@@ -429,12 +429,15 @@ def fp8_topk_step(torch, I, runner, DI, num_cus, group128, lists=16, reps=6):
     return res, w
 
 
-def prefill_leg(torch, I, runner, T=4096, reps=10):
+def prefill_leg(torch, I, runner, T=4096, reps=10, name="v2_single"):
     """Prefill of a T-token prompt of one request at V2 dims on the expanded
     path: expansion of the cached latent per head (two GEMMs over the 512
     latent channels) and causal attention of the T queries.  Reports the time
-    of each and their matrix-core rates (dense BF16 peak)."""
-    inp = I.make_inputs("v2_single", ctx=(T, T))
+    of each and their matrix-core rates (dense BF16 peak).  ``name`` picks the
+    cache: BF16 (v2_single) or FP8 with one scale per position (v2_fp8_topk)
+    or per 128 channels (v2_fp8g_topk)."""
+    inp = I.make_inputs(name, batch=1, ctx=(T, T), topk=0) if name != "v2_single" else \
+        I.make_inputs(name, ctx=(T, T))
     qn, qr = I.make_prefill_queries(inp, T, seed=56)
     w = runner.PrefillWorkload(inp, qn, qr)
     w.step()
@@ -459,7 +462,7 @@ def prefill_leg(torch, I, runner, T=4096, reps=10):
             "expand_TFLOPs": round(exp_flop / (exp_us * 1e-6) / 1e12, 1),
             "attn_TFLOPs": round(att_flop / (att_us * 1e-6) / 1e12, 1),
             "attn_mfma_util": round(att_flop / (att_us * 1e-6) / BF16_PEAK_FLOPS, 4),
-            "prefill_tokens_per_s": round(T / ((exp_us + att_us) * 1e-6), 1)}
+            "prefill_tokens_per_s": round(T / ((exp_us + att_us) * 1e-6), 1), "cache": inp.cache_dtype}
 
 
 def cache_append_part(torch, I, w, reps=200):
@@ -818,6 +821,8 @@ def main():
         torch.cuda.empty_cache()
         if args.prefill:
             result["prefill_4096"] = prefill_leg(torch, I, runner)
+            result["prefill_4096_fp8"] = prefill_leg(torch, I, runner, name="v2_fp8_topk")
+            result["prefill_4096_fp8g"] = prefill_leg(torch, I, runner, name="v2_fp8g_topk")
         result["configs"] = configs
 
     if not args.no_cpu_baseline:

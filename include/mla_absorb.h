@@ -153,8 +153,9 @@ mla_status mla_cache_append(const mla_config* cfg, const void* c_new, const void
 /* ---- Prefill (many queries of one request) on the expanded path ----
  * With many queries a key expanded once is shared by all of them ("DeepSeek's
  * KV Cache", the paragraph after Figure 5 on when absorption wins; Figure 5
- * (1) and Figure 6 (1) for the expanded forms).  V2 dims, BF16 cache and
- * activations, d_nope = d_v = 128 (MLA_ERR_UNSUPPORTED otherwise).
+ * (1) and Figure 6 (1) for the expanded forms).  V2 dims, a BF16 or FP8
+ * cache, BF16 activations, d_nope = d_v = 128 (MLA_ERR_UNSUPPORTED
+ * otherwise).
  *
  * mla_prepare_w_uk_t: the weight layout the expansion reads, once per set of
  * weights: w_uk_t[h][n][c] = w_uk[h][c][n] ([H][D_N][D_C], BF16). */
@@ -165,9 +166,15 @@ mla_status mla_prepare_w_uk_t(const mla_config* cfg, const void* w_uk, void* w_u
  *   k_nope[s][h][n] = sum_c c_s[c] w_uk[h][c][n]   [T][H][D_N] BF16
  *   v[s][h][n]      = sum_c w_uv[h][n][c] c_s[c]    [T][H][D_V] BF16
  *   k_rope[s][r]    = the cached rotary key         [T][D_R]    BF16
- * (float32 accumulation, one BF16 rounding).  Positions on a page id out of
- * range get unspecified values (never a fault).  Errors: null or misaligned
- * pointers, T < 1 -> MLA_ERR_INVALID_ARG. */
+ * (float32 accumulation, one BF16 rounding).  The cache is BF16 or FP8
+ * ("DeepSeek's KV Cache", section "Calculating V3.2's KV cache": c_s is the
+ * E4M3 value times its scale): with one scale per position the sums run on
+ * the exact code values and are multiplied by the position's scale in
+ * float32; with one scale per 128 channels each value times its group's
+ * scale is rounded once to BF16 first.  Positions on a page id out of range
+ * get unspecified values (never a fault).  Errors: null or misaligned
+ * pointers, T < 1 -> MLA_ERR_INVALID_ARG; a float32 cache ->
+ * MLA_ERR_UNSUPPORTED. */
 mla_status mla_prefill_expand(const mla_config* cfg, const void* kv_pool, int64_t num_pages,
                               const int32_t* block_table, int32_t T, const void* w_uk_t, const void* w_uv,
                               void* k_nope, void* v, void* k_rope, void* stream);

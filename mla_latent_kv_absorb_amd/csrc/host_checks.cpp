@@ -238,7 +238,7 @@ mla_status check_prefill_config(const mla_config* cfg) {
   Path path;
   mla_status st = check_config(cfg, &path);
   if (st != MLA_OK) return st;
-  if (path != Path::kMfmaBf16 || cfg->d_nope != 128 || cfg->d_v != 128) return MLA_ERR_UNSUPPORTED;
+  if (path == Path::kF32 || cfg->d_nope != 128 || cfg->d_v != 128) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 }  // namespace

@@ -63,6 +63,10 @@ mla_status mla_prefill_expand(const mla_config* cfg, const void* kv_pool, int64_
   a.pool = (const uint8_t*)kv_pool;
   a.page_bytes = (int64_t)page;
   a.rope_off = (int64_t)rope_off;
+  a.scale_off = (int64_t)scale_off;
+  a.fmt = cfg->cache_dtype == MLA_FP8_E4M3        ? mla::kExpandFp8Token
+          : cfg->cache_dtype == MLA_FP8_E4M3_G128 ? mla::kExpandFp8Group
+                                                  : mla::kExpandBf16;
   a.num_pages = num_pages;
   a.block_table = block_table;
   a.T = T;

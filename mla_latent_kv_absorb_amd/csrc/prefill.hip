@@ -12,7 +12,13 @@
 // two weights viewed as [H * 128][512] (W_UV as stored; W_UK transposed once
 // by transpose_w_uk_kernel).  Tiles of 128 positions x 128 features, K in
 // chunks of 64 moved HBM -> LDS without registers (double buffered), four
-// waves of 64 x 64 on MFMA 32x32x16.
+// waves of 64 x 64 on MFMA 32x32x16.  FP8 caches ("DeepSeek's KV Cache",
+// section "Calculating V3.2's KV cache": the latent is the E4M3 value times
+// its scale): each chunk's codes come through registers and go to LDS as
+// BF16.  With one scale per position the codes go as their exact BF16 values
+// and each output row is multiplied by its position's scale in float32; with
+// one scale per 128 channels each value times its group's scale is rounded
+// once to BF16 (a 64-channel chunk lies in one group).
 //
 // prefill_attn_kernel: per work-group one head and 4 x 32 x QB queries (32 x QB
 // per wave, one query per lane column of each column block).  Tiles of 32 positions (content key, rotary key,
@@ -34,8 +40,13 @@ constexpr int kGChunks = kLatent / kGK; // 8
 
 __device__ __forceinline__ int gswz(int r) { return r & 7; }
 
+// FMT: kExpandBf16, kExpandFp8Token (one scale per position), kExpandFp8Group
+// (one scale per 128 latent channels)
+template <int FMT>
 __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
+  constexpr bool FP8 = FMT != kExpandBf16;
   __shared__ __attribute__((aligned(16))) char lds[2 * 2 * kGTile];
+  __shared__ float srow[kGM];  // one scale per position: the tile rows' scales
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t m0 = (int64_t)blockIdx.y * kGM;
@@ -61,8 +72,63 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t dst = base + buf * 2 * kGTile + 8 * (4 * w + i) * kGRow;
-      dma16(asrc[i] + kc * kGRow, dst);
+      if (!FP8) dma16(asrc[i] + kc * kGRow, dst);
       dma16(bsrc[i] + kc * kGK, dst + kGTile);
+    }
+  };
+
+  // FP8: thread t takes 32 codes (channels 32 (t % 2) .. + 31 of a chunk) of
+  // tile row t / 2
+  const int r8 = threadIdx.x >> 1, h8 = threadIdx.x & 1;
+  const uint8_t* csrc = nullptr;
+  const float* ssrc = nullptr;
+  float row_scale = 1.0f;
+  if (FP8) {
+    int64_t s = m0 + r8;
+    if (s >= a.T) s = a.T - 1;
+    int32_t page = a.block_table[s >> 6];
+    if (page < 0 || page >= a.num_pages) page = 0;
+    const uint8_t* pg = a.pool + (int64_t)page * a.page_bytes;
+    csrc = pg + (s & 63) * kC8Row + 32 * h8;
+    ssrc = (const float*)(pg + a.scale_off) + (s & 63) * (FMT == kExpandFp8Group ? kLatent / 128 : 1);
+    if (FMT == kExpandFp8Token) row_scale = *ssrc;  // to LDS with the first chunk's codes
+  }
+  struct Codes {
+    i32x4 c0, c1;
+    float sc;  // the chunk's group scale (one scale per 128 channels)
+  };
+  auto load_codes = [&](int kc) -> Codes {
+    Codes c;
+    c.c0 = *(const i32x4*)(csrc + kc * kGK);
+    c.c1 = *(const i32x4*)(csrc + kc * kGK + 16);
+    c.sc = FMT == kExpandFp8Group ? ssrc[kc >> 1] : 1.0f;
+    return c;
+  };
+  // the chunk's codes as BF16 into the A tile of buffer buf (chunk 4 h8 + i
+  // of row r8 holds channels 8 (4 h8 + i) .. + 7)
+  auto put_codes = [&](int buf, const Codes& c) {
+    LDS char* A = (LDS char*)lds + buf * 2 * kGTile + r8 * kGRow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const i32x4& q = i < 2 ? c.c0 : c.c1;
+      const int w0 = q[2 * (i & 1)], w1 = q[2 * (i & 1) + 1];
+      bf16x8 v;
+      if (FMT == kExpandFp8Token) {
+        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+        v = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      } else {
+        const f32x2 f[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(w0, false), __builtin_amdgcn_cvt_pk_f32_fp8(w0, true),
+                            __builtin_amdgcn_cvt_pk_f32_fp8(w1, false), __builtin_amdgcn_cvt_pk_f32_fp8(w1, true)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = (__bf16)(f[e][0] * c.sc);
+          v[2 * e + 1] = (__bf16)(f[e][1] * c.sc);
+        }
+      }
+      *(LDS bf16x8*)(A + 16 * ((4 * h8 + i) ^ gswz(r8))) = v;
     }
   };
 
@@ -74,9 +140,21 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   issue(0, 0);
+  Codes cur;
+  if (FP8) cur = load_codes(0);
   for (int kc = 0; kc < kGChunks; ++kc) {
     const int buf = kc & 1;
-    if (kc + 1 < kGChunks) {
+    if (FP8) {
+      // the weight rows and the codes of chunk kc have landed (issued last,
+      // nothing after them); the codes go to LDS, then chunk kc + 1 goes out
+      wait_vmcnt<0>();
+      put_codes(buf, cur);
+      if (FMT == kExpandFp8Token && kc == 0 && h8 == 0) srow[r8] = row_scale;
+      if (kc + 1 < kGChunks) {
+        issue(buf ^ 1, kc + 1);
+        cur = load_codes(kc + 1);
+      }
+    } else if (kc + 1 < kGChunks) {
       issue(buf ^ 1, kc + 1);
       wait_vmcnt<8>();  // chunk kc landed (chunk kc + 1 may be in flight)
     } else {
@@ -114,7 +192,8 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int sr = 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
-        *(LDS __bf16*)(ob + sr * kOPitch + 2 * (32 * j + row)) = (__bf16)acc[i][j][r];
+        const float sc = FMT == kExpandFp8Token ? srow[64 * wm + sr] : 1.0f;
+        *(LDS __bf16*)(ob + sr * kOPitch + 2 * (32 * j + row)) = (__bf16)(acc[i][j][r] * sc);
       }
   // each wave reads back only its own block: no barrier needed
 #pragma unroll
@@ -362,7 +441,9 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void prefill_attn_kernel(Pref
 
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.N / kGN), (unsigned)((a.T + kGM - 1) / kGM));
-  hipLaunchKernelGGL(expand_kernel, grid, dim3(256), 0, s, a);
+  if (a.fmt == kExpandFp8Token) hipLaunchKernelGGL(expand_kernel<kExpandFp8Token>, grid, dim3(256), 0, s, a);
+  else if (a.fmt == kExpandFp8Group) hipLaunchKernelGGL(expand_kernel<kExpandFp8Group>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(expand_kernel<kExpandBf16>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

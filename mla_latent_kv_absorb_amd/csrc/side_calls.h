@@ -10,9 +10,13 @@
 namespace mla {
 
 // prefill: per-head expansion of one request's latent (NT GEMM over D_C)
+// cache formats of the expansion
+constexpr int kExpandBf16 = 0, kExpandFp8Token = 1, kExpandFp8Group = 2;
+
 struct ExpandArgs {
   const uint8_t* pool;
-  int64_t page_bytes, rope_off, num_pages;
+  int64_t page_bytes, rope_off, scale_off, num_pages;
+  int32_t fmt;                 // kExpandBf16, kExpandFp8Token or kExpandFp8Group
   const int32_t* block_table;  // the request's pages
   int64_t T;
   const __bf16* w;             // [N][512]

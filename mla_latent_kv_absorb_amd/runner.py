@@ -189,7 +189,8 @@ class PrefillWorkload:
         import torch
         assert inp.B == 1
         self.inp = inp
-        self.cfg = B.make_config(inp.H, inp.D_C, inp.D_R, inp.D_N, inp.D_V, inp.scale, B.MLA_BF16, B.MLA_BF16)
+        self.cfg = B.make_config(inp.H, inp.D_C, inp.D_R, inp.D_N, inp.D_V, inp.scale,
+                                 _dtype_code(inp.cache_dtype), B.MLA_BF16)
         pool, table = I.build_paged_pool(inp)
         self.pool = torch.from_numpy(pool).to(device)
         self.block_row = torch.from_numpy(np.ascontiguousarray(table[0], dtype=np.int32)).to(device)

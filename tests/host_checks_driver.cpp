@@ -247,7 +247,12 @@ static void test_side_calls() {
                             (const int32_t*)dev(5), 4, 8, &path) == MLA_ERR_UNSUPPORTED);
   EXPECT(check_prepare_w_uk_t(&c, dev(0), dev(1)) == MLA_OK);
   mla_config fp8 = v2(MLA_FP8_E4M3);
-  EXPECT(check_prepare_w_uk_t(&fp8, dev(0), dev(1)) == MLA_ERR_UNSUPPORTED);
+  EXPECT(check_prepare_w_uk_t(&fp8, dev(0), dev(1)) == MLA_OK);
+  EXPECT(check_prefill_expand(&fp8, dev(0), 10, (const int32_t*)dev(1), 4096, dev(2), dev(3), dev(4), dev(5),
+                              dev(6)) == MLA_OK);
+  mla_config big32 = v2(MLA_F32);
+  big32.act_dtype = MLA_F32;
+  EXPECT(check_prepare_w_uk_t(&big32, dev(0), dev(1)) == MLA_ERR_UNSUPPORTED);
   EXPECT(check_prefill_expand(&c, dev(0), 10, (const int32_t*)dev(1), 4096, dev(2), dev(3), dev(4), dev(5),
                               dev(6)) == MLA_OK);
   EXPECT(check_prefill_expand(&c, dev(0), 10, (const int32_t*)dev(1), 0, dev(2), dev(3), dev(4), dev(5),

@@ -203,9 +203,13 @@ def test_append_and_prefill_validation(B):
     assert lib.mla_cache_append(c, null, p, null, null, 0, p, p, 1, p, 1, 1, null) == B.MLA_ERR_INVALID_ARG
     odd = B.make_config(4, 16, 7, 8, 8, 0.25, B.MLA_F32, B.MLA_F32)
     assert lib.mla_cache_append(ctypes.byref(odd), p, p, null, null, 0, p, p, 1, p, 1, 1, null) == B.MLA_ERR_UNSUPPORTED
-    # prefill: BF16 V2 dims only; counts and ranges checked
-    fp8 = v2(B, B.MLA_FP8_E4M3)
-    assert lib.mla_prepare_w_uk_t(ctypes.byref(fp8), p, p, null) == B.MLA_ERR_UNSUPPORTED
+    # prefill: V2 dims with a BF16 or FP8 cache (float32 refused); counts and ranges checked
+    f32 = B.make_config(128, 512, 64, 128, 128, 0.1, B.MLA_F32, B.MLA_F32)
+    assert lib.mla_prepare_w_uk_t(ctypes.byref(f32), p, p, null) == B.MLA_ERR_UNSUPPORTED
+    assert lib.mla_prefill_expand(ctypes.byref(f32), p, 1, p, 64, p, p, p, p, p, null) == B.MLA_ERR_UNSUPPORTED
+    for dt in (B.MLA_FP8_E4M3, B.MLA_FP8_E4M3_G128):
+        fp8 = v2(B, dt)
+        assert lib.mla_prefill_expand(ctypes.byref(fp8), p, 1, p, 0, p, p, p, p, p, null) == B.MLA_ERR_INVALID_ARG
     assert lib.mla_prepare_w_uk_t(c, null, p, null) == B.MLA_ERR_INVALID_ARG
     assert lib.mla_prefill_expand(c, p, 1, p, 0, p, p, p, p, p, null) == B.MLA_ERR_INVALID_ARG
     assert lib.mla_prefill_expand(c, p, 1, p, 64, p, p, null, p, p, null) == B.MLA_ERR_INVALID_ARG

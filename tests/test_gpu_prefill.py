@@ -1,6 +1,6 @@
 """GPU parity of prefill on the expanded path (mla_prepare_w_uk_t,
 mla_prefill_expand, mla_prefill_attn) through the C ABI against the float64
-oracle.
+oracle, from BF16 and FP8 caches.
 
 Bars: the rotary keys are copies (bit-exact); the expanded keys and values
 are one GEMM each with float32 accumulation and one BF16 rounding (max |err|
@@ -39,12 +39,21 @@ def _np(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
+def latent_of(inp):
+    """The cached latent as the oracle reads it: the BF16 values, or the E4M3
+    codes times their scales in float64."""
+    if inp.cache_dtype in I.FP8_DTYPES:
+        return oracle.dequant_fp8_latent(inp.c_codes, inp.c_scales)
+    return inp.c_kv
+
+
 def check_queries(w, inp, qn, qr, queries, heads):
     out, lse = _np(w.out), w.lse.cpu().numpy()
     T, N = w.T, w.N
+    c = latent_of(inp)
     for i in queries:
         pos = T - N + i
-        ref_o, ref_l, _ = oracle.decode_unabsorbed(inp.c_kv[:pos + 1], inp.k_rope[:pos + 1], qn[i], qr[i],
+        ref_o, ref_l, _ = oracle.decode_unabsorbed(c[:pos + 1], inp.k_rope[:pos + 1], qn[i], qr[i],
                                                    inp.w_uk, inp.w_uv, inp.scale, heads=heads)
         err = np.max(np.abs(out[i][heads] - ref_o))
         assert err <= 2e-2 * np.max(np.abs(ref_o)), f"query {i}: {err}"
@@ -64,6 +73,41 @@ def test_prefill_expand(torch, R):
         ref_k, ref_v = oracle.expand_keys_values(inp.c_kv, inp.w_uk, inp.w_uv, h)
         assert np.max(np.abs(kn[:, h] - ref_k)) <= 1e-2 * np.max(np.abs(ref_k)), f"k head {h}"
         assert np.max(np.abs(v[:, h] - ref_v)) <= 1e-2 * np.max(np.abs(ref_v)), f"v head {h}"
+
+
+@pytest.mark.parametrize("name", ["v2_fp8_topk", "v2_fp8g_topk"])
+def test_prefill_expand_fp8(torch, R, name):
+    """FP8 caches, one scale per position and one per 128 channels, with the
+    scales spread over 2^-3 .. 2^3 across positions (and groups): the
+    expansion reads code x scale.  Bound 1e-2 x max|ref| per head as for
+    BF16: with per-position scales the sums run on the exact codes and take
+    the scale in float32; group-scaled values are rounded once to BF16."""
+    _log(f"prefill expand {name}")
+    inp = I.make_inputs(name, seed=56, batch=1, ctx=(333, 333), topk=0)
+    rng = np.random.default_rng(56)
+    inp.c_scales[:] = inp.c_scales * np.exp2(rng.integers(-3, 4, size=inp.c_scales.shape)).astype(np.float32)
+    qn, qr = I.make_prefill_queries(inp, 8, seed=57)
+    w = R.PrefillWorkload(inp, qn, qr)
+    w.expand()
+    torch.cuda.synchronize()
+    kn, v, kr = _np(w.k_nope), _np(w.v), _np(w.k_rope)
+    np.testing.assert_array_equal(kr, inp.k_rope)
+    c = latent_of(inp)
+    for h in (0, 33, 64, 127):
+        ref_k, ref_v = oracle.expand_keys_values(c, inp.w_uk, inp.w_uv, h)
+        assert np.max(np.abs(kn[:, h] - ref_k)) <= 1e-2 * np.max(np.abs(ref_k)), f"k head {h}"
+        assert np.max(np.abs(v[:, h] - ref_v)) <= 1e-2 * np.max(np.abs(ref_v)), f"v head {h}"
+
+
+@pytest.mark.parametrize("name", ["v2_fp8_topk", "v2_fp8g_topk"])
+def test_prefill_attn_fp8(torch, R, name):
+    _log(f"prefill {name} T=700 N=130")
+    inp = I.make_inputs(name, seed=58, batch=1, ctx=(700, 700), topk=0)
+    qn, qr = I.make_prefill_queries(inp, 130, seed=59)
+    w = R.PrefillWorkload(inp, qn, qr)
+    w.step()
+    torch.cuda.synchronize()
+    check_queries(w, inp, qn, qr, [0, 31, 64, 129], [0, 40, 127])
 
 
 @pytest.mark.parametrize("T,N", [(300, 300), (300, 77), (97, 1), (1000, 260)])
