@@ -175,8 +175,12 @@ constexpr int kSplitStage = kHeads * kSplitPitch;       // bytes of the output s
 // owners through the float array at inv_off ([128], head_slot order),
 // written before the call; the rows are assembled in the first kSplitStage
 // bytes of the work-group's LDS.
+// before_flush() runs after the rows are staged and before their global
+// stores are issued: a store it makes (the log-sum-exps) goes out without
+// waiting behind the row stores, as a wait for any value it reloads would.
+template <typename F>
 __device__ __forceinline__ void store_rows_split(LDS char* L, int inv_off, __bf16* dst, const f32x16 (&O)[16],
-                                                 int w) {
+                                                 int w, F&& before_flush) {
   wait_vmcnt<0>();
   __syncthreads();
   const int lane = __lane_id();
@@ -212,6 +216,7 @@ __device__ __forceinline__ void store_rows_split(LDS char* L, int inv_off, __bf1
       }
     }
   __syncthreads();
+  before_flush();
 #pragma unroll
   for (int r = 0; r < 32; ++r)
     *(i32x4*)(dst + (32 * w + r) * kLatent + 8 * lane) = *(const LDS i32x4*)(L + (32 * w + r) * kSplitPitch + 16 * lane);

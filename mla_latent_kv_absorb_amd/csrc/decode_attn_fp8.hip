@@ -706,12 +706,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
       __bf16* rows = DIRECT ? (__bf16*)a.o_lat + (int64_t)cb * kHeads * kLatent
                             : (__bf16*)a.part_o + slot * kHeads * kLatent;
       *(LDS float*)(L + C::I_OFF + 4 * head_slot(head)) = inv;
-      store_rows_split(L, C::I_OFF, rows, O, w);
-      if (DIRECT) {
-        if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
-      } else {
-        if (hi == 0) a.part_lse[slot * kHeads + head] = lse;
-      }
+      store_rows_split(L, C::I_OFF, rows, O, w, [&]() {
+        if (DIRECT) {
+          if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
+        } else {
+          if (hi == 0) a.part_lse[slot * kHeads + head] = lse;
+        }
+      });
     }
     // next request with tiles
     ++cb;
