@@ -100,6 +100,15 @@ __device__ __forceinline__ float max3_raw(float a, float b, float c) {
   return r;
 }
 
+// A copy of v that the compiler cannot see through: what is derived from it
+// is computed anew where it is used, not kept (or spilled and reloaded) from
+// an earlier computation.
+__device__ __forceinline__ int opaque(int v) {
+  int r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
 __device__ __forceinline__ float wave_partner(float v) {
   // value held by lane (l ^ 32)
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -113,7 +122,11 @@ __device__ __forceinline__ float wave_partner(float v) {
 // LDS (the tile ring): every tile load must have landed and every wave must
 // be done reading the ring, which the barrier here provides; the caller's
 // next use of the ring synchronises again.
-__device__ __forceinline__ void store_rows_staged(LDS char* L, __bf16* dst, const f32x16 (&O)[16], float inv, int w) {
+// before_flush(): as in store_rows_split, between the staging and the global
+// stores.
+template <typename F>
+__device__ __forceinline__ void store_rows_staged(LDS char* L, __bf16* dst, const f32x16 (&O)[16], float inv, int w,
+                                                  F&& before_flush) {
   wait_vmcnt<0>();
   __syncthreads();
   const int lane = __lane_id();
@@ -145,6 +158,7 @@ __device__ __forceinline__ void store_rows_staged(LDS char* L, __bf16* dst, cons
       *(LDS i32x4*)(rowL + 2 * (32 * mb + 8 * (hi ? g1 : g0))) = v;
     }
   // each wave reads back only its own rows: no barrier needed
+  before_flush();
 #pragma unroll
   for (int r = 0; r < 32; ++r)
     *(i32x4*)(dst + r * kLatent + 8 * lane) = *(const LDS i32x4*)(mine + r * kPitch + 16 * lane);
@@ -252,15 +266,6 @@ __device__ __forceinline__ f32x16 mfma_sv0(const bf16x8& a, const bf16x8& b) {
 }
 __device__ __forceinline__ void mfma_sv(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-
-// A copy of v that the compiler cannot see through: what is derived from it
-// is computed anew where it is used, not kept (or spilled and reloaded) from
-// an earlier computation.
-__device__ __forceinline__ int opaque(int v) {
-  int r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
-  return r;
 }
 
 // Uniform metadata reads go through the constant address space so they become

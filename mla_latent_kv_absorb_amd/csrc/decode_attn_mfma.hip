@@ -503,12 +503,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       const int64_t slot = worker + cb;
       __bf16* rows = DIRECT ? (__bf16*)a.o_lat + (int64_t)cb * kHeads * kLatent
                             : (__bf16*)a.part_o + slot * kHeads * kLatent;
-      store_rows_staged(L, rows + (int64_t)32 * w * kLatent, O, inv, w);
-      if (DIRECT) {
-        if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
-      } else {
-        if (hi == 0) a.part_lse[slot * kHeads + head] = lse;
-      }
+      store_rows_staged(L, rows + (int64_t)32 * w * kLatent, O, inv, w, [&]() {
+        if (DIRECT) {
+          if (a.lse_out != nullptr && hi == 0) a.lse_out[(int64_t)cb * kHeads + head] = lse;
+        } else {
+          if (hi == 0) a.part_lse[slot * kHeads + head] = lse;
+        }
+      });
     }
     // next request with tiles
     ++cb;
