@@ -63,6 +63,16 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
 __device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
+// Cache-stream forms: every line of the paged cache is read once per launch,
+// so these loads are marked non-temporal (nt) and leave the lines that are
+// reused (queries, block tables, index lists) in L2.
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+__device__ __forceinline__ void dma16s_nt(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
 __device__ __forceinline__ void dma4s(uint32_t voff, const void* sbase, uint32_t lds_addr) {
   asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }

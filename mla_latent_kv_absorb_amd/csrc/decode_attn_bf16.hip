@@ -113,9 +113,9 @@ struct TileLoader {
       const uint32_t x = 16 * swz(8 * w + k) + k * kCRow;
       uint32_t voff;
       asm volatile("v_xor_b32 %0, %1, %2" : "=v"(voff) : "s"(x), "v"(lane16));
-      dma16s(voff, tl.c_base, tl.lsb + (8 * w + k) * kCRow);
+      dma16s_nt(voff, tl.c_base, tl.lsb + (8 * w + k) * kCRow);
     } else {
-      dma16s(voff_r, tl.r_base, tl.rsb + 8 * w * kRRow);
+      dma16s_nt(voff_r, tl.r_base, tl.rsb + 8 * w * kRRow);
     }
   }
   __device__ __forceinline__ void issue(const Tile& tl) const {

@@ -166,8 +166,8 @@ struct Fp8Loader {
                  lds0 + st * C::STAGE, bits};
   }
   __device__ __forceinline__ void dense_one(const Dense& d, int k) const {
-    if (k < 4) dma16s(voff_c(k), d.c, d.sb + (8 * w + 2 * k) * kC8Row);
-    else if (k == 4) dma16s(voff_r(), d.r, d.sb + C::C_STAGE + 8 * w * kRRow);
+    if (k < 4) dma16s_nt(voff_c(k), d.c, d.sb + (8 * w + 2 * k) * kC8Row);
+    else if (k == 4) dma16s_nt(voff_r(), d.r, d.sb + C::C_STAGE + 8 * w * kRRow);
     else if (lane < 8) dma4s(voff_s(), d.s, d.sb + C::C_STAGE + C::R_STAGE + 32 * w);
   }
 
@@ -195,9 +195,9 @@ struct Fp8Loader {
   __device__ __forceinline__ int slot_of(int32_t code) const { return code >= 0 ? (code & 63) : 0; }
   __device__ __forceinline__ void gather_one(const Gather& g, int k) const {
     if (k < 4) {
-      dma16(row_base(g.code_c[k]) + slot_of(g.code_c[k]) * kC8Row + (chk_c ^ kChunkX[k]), g.sb + (8 * w + 2 * k) * kC8Row);
+      dma16_nt(row_base(g.code_c[k]) + slot_of(g.code_c[k]) * kC8Row + (chk_c ^ kChunkX[k]), g.sb + (8 * w + 2 * k) * kC8Row);
     } else if (k == 4) {
-      dma16(row_base(g.code_r) + rope_off + slot_of(g.code_r) * kRRow + chk_r, g.sb + C::C_STAGE + 8 * w * kRRow);
+      dma16_nt(row_base(g.code_r) + rope_off + slot_of(g.code_r) * kRRow + chk_r, g.sb + C::C_STAGE + 8 * w * kRRow);
     } else if (lane < 8) {
       dma4(row_base(g.code_s) + scale_off + slot_of(g.code_s) * 4, g.sb + C::C_STAGE + C::R_STAGE + 32 * w);
     }

@@ -131,19 +131,19 @@ struct Loader {
       if (FP8) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          dma16(pg + (int64_t)(slot0 + 2 * q) * kC8Row + 16 * lane, sb + (8 * w + 2 * q) * kC8Row);
+          dma16_nt(pg + (int64_t)(slot0 + 2 * q) * kC8Row + 16 * lane, sb + (8 * w + 2 * q) * kC8Row);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          dma16(pg + (int64_t)(slot0 + k) * kCRow + 16 * (lane ^ swz(8 * w + k)), sb + (8 * w + k) * kCRow);
+          dma16_nt(pg + (int64_t)(slot0 + k) * kCRow + 16 * (lane ^ swz(8 * w + k)), sb + (8 * w + k) * kCRow);
       }
       const int rr = lane >> 3, rc = lane & 7;
-      dma16(pg + a.rope_off + (int64_t)(slot0 + rr) * kRRow + 16 * (rc ^ swz_r(8 * w + rr)),
+      dma16_nt(pg + a.rope_off + (int64_t)(slot0 + rr) * kRRow + 16 * (rc ^ swz_r(8 * w + rr)),
             sb + C::C_STAGE + 8 * w * kRRow);
       if (FP8) {
         // this wave's 8 positions' scales: 32 B, or 128 B with group scales
         if (GS) {
-          if (lane < 8) dma16(pg + a.scale_off + (int64_t)(slot0 + lane) * 16, sb + C::C_STAGE + C::R_STAGE + 128 * w);
+          if (lane < 8) dma16_nt(pg + a.scale_off + (int64_t)(slot0 + lane) * 16, sb + C::C_STAGE + C::R_STAGE + 128 * w);
         } else {
           if (lane < 8) dma4(pg + a.scale_off + (int64_t)(slot0 + lane) * 4, sb + C::C_STAGE + C::R_STAGE + 32 * w);
         }
@@ -173,12 +173,12 @@ struct Loader {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint8_t* src = (lane < 32) ? pgk[2 * q] + slk[2 * q] * CR : pgk[2 * q + 1] + slk[2 * q + 1] * CR;
-          dma16(src + 16 * (lane & 31), sb + (8 * w + 2 * q) * kC8Row);
+          dma16_nt(src + 16 * (lane & 31), sb + (8 * w + 2 * q) * kC8Row);
         }
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          dma16(pgk[k] + slk[k] * CR + 16 * (lane ^ swz(8 * w + k)), sb + (8 * w + k) * kCRow);
+          dma16_nt(pgk[k] + slk[k] * CR + 16 * (lane ^ swz(8 * w + k)), sb + (8 * w + k) * kCRow);
       }
       const int rr = lane >> 3, rc = lane & 7;
       const uint8_t* rp = pgk[0];
@@ -188,7 +188,7 @@ struct Loader {
         rp = (rr == k) ? pgk[k] : rp;
         rs = (rr == k) ? slk[k] : rs;
       }
-      dma16(rp + a.rope_off + rs * kRRow + 16 * (rc ^ swz_r(8 * w + rr)), sb + C::C_STAGE + 8 * w * kRRow);
+      dma16_nt(rp + a.rope_off + rs * kRRow + 16 * (rc ^ swz_r(8 * w + rr)), sb + C::C_STAGE + 8 * w * kRRow);
       if (FP8) {
         if (lane < 8) {
           const uint8_t* sp = pgk[0];
@@ -198,7 +198,7 @@ struct Loader {
             sp = (lane == k) ? pgk[k] : sp;
             ss = (lane == k) ? slk[k] : ss;
           }
-          if (GS) dma16(sp + a.scale_off + ss * 16, sb + C::C_STAGE + C::R_STAGE + 128 * w);
+          if (GS) dma16_nt(sp + a.scale_off + ss * 16, sb + C::C_STAGE + C::R_STAGE + 128 * w);
           else dma4(sp + a.scale_off + ss * 4, sb + C::C_STAGE + C::R_STAGE + 32 * w);
         }
       }

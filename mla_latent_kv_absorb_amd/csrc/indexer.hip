@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void indexer_score_kernel(IndexerArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 8 * i + (lane >> 3);
-      dma16(keys + row * kIdxKeyRow + 16 * ((lane & 7) ^ idx_swz(row)), ring_addr + st * kIdxStage + 1024 * i);
+      dma16_nt(keys + row * kIdxKeyRow + 16 * ((lane & 7) ^ idx_swz(row)), ring_addr + st * kIdxStage + 1024 * i);
     }
     dma4(pg + a.scale_off + 4 * ((32 * (hp & 1) + lane) & 63), ring_addr + st * kIdxStage + 4096);
   };
